@@ -1,0 +1,254 @@
+"""Benchmark of the MI355X sparse MoE layer: one training step of the whole hot
+path (router, routing, dispatch, expert grouped GEMMs, combine, loss, the full
+backward and SGD) on one GPU, with synthetic seeded inputs resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line.  `value` is tokens per second of the whole training
+step.  Per-stage times come from HIP events recorded by the library between
+its launches on the bench stream (moe_train_step_profiled) inside the timed
+region; `roofline` is the dominant stage's algorithmic work over its average
+duration.  `cpu_baseline` times the float64 oracle on the host on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd tokens/sec; expert GEMM % of bf16 MFMA peak, dispatch GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def stage_work(w):
+    """Algorithmic work of each stage: ("flop", n) or ("byte", n)."""
+    s = 2 if w.dtype == "bf16" else 4
+    T, d, E, k, ffn = w.T, w.d, w.E, w.k, w.ffn
+    R = T * k
+    hid = 2 * ffn if w.expert == "swiglu" else ffn     # up-projection output columns
+    nparam = E * d + E * ffn * d * (3 if w.expert == "swiglu" else 2)
+    if w.expert != "swiglu":
+        nparam += E * ffn + E * d
+    return {
+        "router_logits": ("flop", 2.0 * T * d * E),
+        "route": ("byte", T * E * 4 + T * k * 8 + R * 12),
+        # read X once, write k rows, read the slot indices
+        "gather": ("byte", (T * d + R * d) * s + R * 4),
+        "up_fwd": ("flop", 2.0 * R * d * hid),
+        "down_fwd": ("flop", 2.0 * R * ffn * d),
+        # read k rows, gates, slots; write Y; read Y_target; write dY
+        "combine_loss": ("byte", (R * d + 3 * T * d) * s + R * 8),
+        # read dY and k rows of EO, write k rows of dEO; slots, gates, dgate
+        "combine_bwd": ("byte", (T * d + 2 * R * d) * s + R * 12),
+        "down_dgrad": ("flop", 2.0 * R * d * ffn),
+        "down_wgrad": ("flop", 2.0 * R * d * ffn),
+        "up_dgrad": ("flop", 2.0 * R * hid * d),
+        "up_wgrad": ("flop", 2.0 * R * hid * d),
+        "bias_grads": ("byte", (R * d + R * ffn) * s if w.expert != "swiglu" else 0),
+        "router_bwd": ("byte", T * E * (4 + s) + T * k * 16),
+        "router_dwg": ("flop", 2.0 * T * E * d),
+        "router_dx": ("flop", 2.0 * T * E * d),
+        # read k rows of dXp and the fp32 router part, write dX, read slots
+        "scatter": ("byte", R * d * s + T * d * (4 + s) + R * 4),
+        # master read + write, gradient read, working copy write
+        "sgd": ("byte", nparam * (4 + 4 + 4 + s)),
+    }
+
+
+GEMM_STAGES = ("up_fwd", "down_fwd", "down_dgrad", "down_wgrad", "up_dgrad", "up_wgrad")
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the workload (host cores).
+
+    Sample: routing of every token (logits, group-limited top-k, gates, dispatch
+    tables, aux), then the expert forward and backward of whole expert segments
+    (experts 0, 1, 2, ...) until the time budget is used; the expert part is
+    scaled to all T*k rows by row count.
+    """
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+
+    X64 = inp["X"].double().cpu().numpy()
+    Wg64 = inp["Wg_w"].double().cpu().numpy()
+    shp = O.Shape(E=w.E, k=w.k, n_groups=w.n_groups, topk_groups=w.topk_groups, score=w.score,
+                  expert=w.expert)
+    t0 = time.perf_counter()
+    fw = O.route(X64, Wg64, shp)
+    aux, _, _ = O.aux_loss(fw["routing"].counts, fw["q"], w.k)
+    t_route = time.perf_counter() - t0
+    r = fw["routing"]
+    rng = np.random.default_rng(0)
+    t_exp = 0.0
+    rows = 0
+    n_exp = 0
+    for e in range(w.E):
+        lo, hi = int(r.offsets[e]), int(r.offsets[e + 1])
+        if hi == lo:
+            continue
+        W1 = inp["W1_w"][e].double().cpu().numpy()
+        W2 = inp["W2_w"][e].double().cpu().numpy()
+        W3 = inp["W3_w"][e].double().cpu().numpy() if inp.get("W3_w") is not None else None
+        b1 = inp["b1_w"][e].double().cpu().numpy() if inp.get("b1_w") is not None else None
+        b2 = inp["b2_w"][e].double().cpu().numpy() if inp.get("b2_w") is not None else None
+        dEO = rng.standard_normal((hi - lo, w.d))
+        t1 = time.perf_counter()
+        Xp = O.gather_rows(X64, r.token_of[lo:hi])
+        s = O.expert_forward(w.expert, Xp, W1, b1, W2, b2, W3)
+        O.expert_backward(w.expert, Xp, W1, W2, W3, s, dEO)
+        t_exp += time.perf_counter() - t1
+        rows += hi - lo
+        n_exp += 1
+        if t_route + t_exp >= budget_s:
+            break
+    full = t_route + t_exp * (w.T * w.k / max(rows, 1))
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": w.T / full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"float64 oracle: routing of all {w.T} tokens ({t_route:.1f} s) + expert "
+                       f"forward/backward of {n_exp} whole expert segments ({rows} of {w.T * w.k} "
+                       f"rows, {t_exp:.1f} s), expert part scaled by rows; "
+                       f"estimated {full:.0f} s per step"),
+            "seconds_measured": round(t_route + t_exp, 2)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="grouped_sigmoid_t32768_d7168_e256")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print("bench.py runs on one GPU only: this layer is built and measured on a single "
+              "MI355X (no sharding, no collectives); use --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from sparse_mixture_experts_gate_amd import _lib as L
+    from sparse_mixture_experts_gate_amd import workloads as W
+
+    w = W.BY_NAME[a.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    inp = W.make_inputs(w, device=dev, masters=True)
+    cfg = L.config(w)
+    ws = L.alloc_workspace(cfg, dev)
+    r = L.alloc_routing(w, dev)
+    g = L.alloc_grads(w, dev)
+    Y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
+    loss = torch.empty(3, dtype=torch.float32, device=dev)
+    params = {}
+    for n in ("Wg", "W1", "b1", "W2", "b2", "W3"):
+        if inp.get(n) is not None:
+            params[n] = inp[n]
+            params[n + "_w"] = inp[n + "_w"]
+    X, Yt = inp["X"], inp["Yt"]
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: inputs ready, workspace {ws.numel() / 2**30:.1f} GiB", file=sys.stderr,
+          flush=True)
+
+    with torch.cuda.stream(stream):
+        for i in range(a.warmup):
+            L.moe_train_step(cfg, X, Yt, params, w.lr, w.aux_coef, Y, r, g, loss, ws, stream=stream)
+        stream.synchronize()
+        print(f"[bench] warmup done, loss {loss.tolist()}", file=sys.stderr, flush=True)
+        events = [L.StageEvents() for _ in range(a.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(a.steps):
+            L.moe_train_step_profiled(cfg, X, Yt, params, w.lr, w.aux_coef, Y, r, g, loss, ws,
+                                      events[i], stream=stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    elapsed = t1 - t0
+    stage_ms = {s: [] for s in L.STAGES}
+    for ev in events:
+        ev.collect()
+        for s in L.STAGES:
+            stage_ms[s].extend(ev.ms[s])
+    avg = {s: sum(v) / len(v) for s, v in stage_ms.items()}
+    work = stage_work(w)
+    stages = {}
+    for s in L.STAGES:
+        kind, n = work[s]
+        ms = avg[s]
+        ent = {"ms": round(ms, 4)}
+        if ms > 0 and n > 0:
+            if kind == "flop":
+                tf = n / (ms * 1e-3) / 1e12
+                ent.update(tflops=round(tf, 2), frac=round(tf / PEAK_BF16_TFLOPS, 4))
+            else:
+                gbs = n / (ms * 1e-3) / 1e9
+                ent.update(gbs=round(gbs, 1), frac=round(gbs / PEAK_HBM_GBS, 4))
+        stages[s] = ent
+    dom = max(L.STAGES, key=lambda s: avg[s])
+    kind, n = work[dom]
+    if kind == "flop":
+        ach = n / (avg[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": dom, "work_per_launch": n}
+    else:
+        ach = n / (avg[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                "work_per_launch": n}
+    gemm_ms = sum(avg[s] for s in GEMM_STAGES)
+    gemm_flop = sum(work[s][1] for s in GEMM_STAGES)
+    fwd_bwd_ms = sum(avg[s] for s in L.STAGES if s != "sgd")
+    ms_per_step = elapsed / a.steps * 1e3
+    out = {
+        "metric": METRIC,
+        "value": round(w.T * a.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "ffn": w.ffn, "k": w.k,
+                   "n_groups": w.n_groups, "topk_groups": w.topk_groups, "score": w.score,
+                   "expert": w.expert, "step": "forward+loss+backward+sgd"},
+        "roofline": roof,
+        "fwd_bwd_tokens_per_s": round(w.T / (fwd_bwd_ms * 1e-3), 1),
+        "expert_gemm_tflops": round(gemm_flop / (gemm_ms * 1e-3) / 1e12, 2),
+        "expert_gemm_frac_peak": round(gemm_flop / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "dispatch_gbps": stages["gather"].get("gbs"),
+        "combine_gbps": stages["combine_loss"].get("gbs"),
+        "stages": stages,
+        "loss": [round(x, 6) for x in loss.tolist()],
+        "counts_min_max": [int(r["counts"].min()), int(r["counts"].max())],
+        "empty_experts": int((r["counts"] == 0).sum()),
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,261 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) trainable sparse mixture-of-experts layer.
+ *
+ * The layer (sources: the "Trainable MoE in CUDA" course outline, Parts 1-7;
+ * "AI Infra Kernel Lab" README, sections "Project status" and "Numerical
+ * contracts"):
+ *
+ *   logits  l = X Wg^T                                   (outline Part 3)
+ *   scores  softmax over experts, or elementwise sigmoid  (outline Part 3; Infra Lab grouped gate)
+ *   select  group-limited top-k on the logits; groups are consecutive blocks
+ *           of E/n_groups experts scored by their largest member; ties go to
+ *           the smaller group / expert id                 (Infra Lab "Project status")
+ *   gates   g = w_sel / sum(w_sel), w = the selected scores (outline Part 2)
+ *   dispatch per-expert histogram, exclusive scan, stable slots in ascending
+ *           token order, gather into expert-major rows    (outline Part 4)
+ *   experts ReLU/GELU MLP with biases, or SwiGLU W2(silu(W1 x) * W3 x)
+ *                                                          (outline Part 5; Infra Lab "Numerical contracts")
+ *   combine Y_t = sum_i g_ti EO[slot(t,i)]                (outline Part 4)
+ *   aux     E * sum_e f_e P_e with f_e = count_e/(T k), P_e = mean_t q_te
+ *                                                          (outline Part 6)
+ *   loss    MSE (mean over T*d) + aux_coef * aux; SGD      (outline Part 7)
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer on the current HIP device,
+ *     except the struct pointers themselves (host memory, read during the call).
+ *   - Row-major, densely packed tensors.  "dtype" tensors are float32 when
+ *     cfg->dtype == MOE_DTYPE_F32 and bfloat16 when MOE_DTYPE_BF16.
+ *   - Device pointers must be 16-byte aligned.
+ *   - The caller owns and allocates every buffer, the workspace included.
+ *     The library never allocates, frees, or synchronises the stream, and
+ *     keeps no state between calls.  All work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream).
+ *   - Inputs are never written.  Outputs are overwritten completely
+ *     (gradients of experts that received no rows are written as zeros).
+ *   - All validation happens before the first launch; on an error nothing is
+ *     written.  A launch failure returns MOE_ERR_HIP.
+ *   - Results are deterministic: the same inputs give bitwise identical
+ *     outputs (no floating-point atomics anywhere).
+ *   - T == 0 is valid and returns MOE_OK after writing only zero-sized outputs
+ *     (gradients of the weights are still written, as zeros).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MOE_OK                 0
+#define MOE_ERR_INVALID_ARG   -1  /* shape/config rule broken (see moe_config) */
+#define MOE_ERR_NULL_PTR      -2  /* a required pointer is NULL */
+#define MOE_ERR_MISALIGNED    -3  /* a device pointer is not 16-byte aligned */
+#define MOE_ERR_WORKSPACE     -4  /* workspace NULL or smaller than moe_workspace_bytes() */
+#define MOE_ERR_UNSUPPORTED   -5  /* valid layer, but outside what the kernels support */
+#define MOE_ERR_HIP           -6  /* a HIP launch failed */
+
+/* ---- enums ------------------------------------------------------------- */
+#define MOE_SCORE_SOFTMAX   0
+#define MOE_SCORE_SIGMOID   1
+#define MOE_EXPERT_RELU     0     /* MLP with biases, ReLU */
+#define MOE_EXPERT_GELU     1     /* MLP with biases, exact-erf GELU */
+#define MOE_EXPERT_SWIGLU   2     /* W2 (silu(W1 x) * W3 x), no biases */
+#define MOE_DTYPE_F32       0
+#define MOE_DTYPE_BF16      1     /* bf16 storage and MFMA inputs, fp32 accumulation */
+
+#define MOE_MAX_EXPERTS   256
+#define MOE_MAX_K          16
+
+/*
+ * Layer shape.  Rules (MOE_ERR_INVALID_ARG when broken): T >= 0; d, E, ffn,
+ * k, n_groups, topk_groups >= 1; k <= E; E % n_groups == 0;
+ * topk_groups <= n_groups; k <= topk_groups * (E / n_groups);
+ * T * k < 2^31.
+ * Kernel limits (MOE_ERR_UNSUPPORTED): E <= 256, k <= 16; float32: d and ffn
+ * multiples of 4; bfloat16: d and ffn multiples of 64 and E a multiple of 8.
+ */
+typedef struct moe_config {
+    int32_t T;            /* tokens */
+    int32_t d;            /* model width */
+    int32_t E;            /* experts */
+    int32_t ffn;          /* expert hidden width */
+    int32_t k;            /* experts per token */
+    int32_t n_groups;     /* expert groups (1 = no group limit) */
+    int32_t topk_groups;  /* groups kept per token */
+    int32_t score;        /* MOE_SCORE_* */
+    int32_t expert;       /* MOE_EXPERT_* */
+    int32_t dtype;        /* MOE_DTYPE_* */
+} moe_config;
+
+/*
+ * Weights in the working dtype.  Wg [E,d]; W1 [E,ffn,d]; b1 [E,ffn];
+ * W2 [E,d,ffn]; b2 [E,d]; W3 [E,ffn,d].  b1/b2 are required for the MLP
+ * kinds and ignored (may be NULL) for SwiGLU; W3 is required for SwiGLU only.
+ */
+typedef struct moe_weights {
+    const void* Wg;
+    const void* W1;
+    const void* b1;
+    const void* W2;
+    const void* b2;
+    const void* W3;
+} moe_weights;
+
+/*
+ * Routing outputs of the forward (all written by moe_forward / moe_route):
+ *   logits   float [T,E]   router logits in fp32 (moe_route: ignored, may be NULL)
+ *   topk_idx int32 [T,k]   selected experts, in (-logit, id) order
+ *   gates    float [T,k]   renormalised gates, same order
+ *   counts   int32 [E]     rows per expert
+ *   offsets  int32 [E+1]   exclusive scan of counts
+ *   slot_of  int32 [T,k]   expert-major row of (t, i)
+ *   token_of int32 [T*k]   token of each expert-major row
+ *   aux      float [1]     aux load-balancing loss (unscaled)
+ * moe_backward reads logits, topk_idx, gates, counts, slot_of and token_of.
+ */
+typedef struct moe_routing {
+    float*   logits;
+    int32_t* topk_idx;
+    float*   gates;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* slot_of;
+    int32_t* token_of;
+    float*   aux;
+} moe_routing;
+
+/*
+ * Gradients written by moe_backward / moe_train_step.  dX is dtype [T,d]
+ * (expert path plus router path); the rest are float32 with the shapes of
+ * the weights.  db1/db2 are required for the MLP kinds, dW3 for SwiGLU.
+ */
+typedef struct moe_grads {
+    void*  dX;
+    float* dWg;
+    float* dW1;
+    float* db1;
+    float* dW2;
+    float* db2;
+    float* dW3;
+} moe_grads;
+
+/*
+ * Parameters updated in place by moe_train_step: float32 masters and the
+ * working copies (dtype).  For MOE_DTYPE_F32 a working pointer may equal its
+ * master.  For bf16 the working copy is rewritten as the round-to-nearest-
+ * even conversion of the updated master.
+ */
+typedef struct moe_params {
+    float* Wg;  float* W1;  float* b1;  float* W2;  float* b2;  float* W3;
+    void*  Wg_w; void* W1_w; void* b1_w; void* W2_w; void* b2_w; void* W3_w;
+} moe_params;
+
+/* Workspace buffers whose byte offsets moe_workspace_offset() reports.
+ * They hold the forward's saved activations, read back by moe_backward:
+ *   XP    dtype [T*k, d]    gathered expert-major rows
+ *   H     dtype [T*k, hcols] pre-activations; hcols = 2*ffn for SwiGLU
+ *                           ([H1 | H3] per row), ffn for the MLP kinds
+ *   A     dtype [T*k, ffn]  activations fed to the down projection
+ *   EO    dtype [T*k, d]    expert outputs, expert-major
+ */
+#define MOE_WS_XP   0
+#define MOE_WS_H    1
+#define MOE_WS_A    2
+#define MOE_WS_EO   3
+
+/* Bytes of workspace every entry point needs for this shape (0 on an invalid
+ * shape).  The same workspace must be passed to moe_forward and then to
+ * moe_backward: it carries the saved activations between them. */
+size_t moe_workspace_bytes(const moe_config* cfg);
+
+/* Byte offset of a saved-activation buffer (MOE_WS_*) inside the workspace,
+ * or -1 for an invalid shape or buffer id.  For inspection only. */
+int64_t moe_workspace_offset(const moe_config* cfg, int32_t which);
+
+/*
+ * Routing only, from caller-supplied fp32 logits [T,E]: scores, group-limited
+ * top-k, gates, histogram, scan and slot maps, and the aux value (steps of
+ * outline Parts 2, 3, 4 and 6).  Writes every field of *r except r->logits.
+ */
+int moe_route(const moe_config* cfg, const float* logits, moe_routing* r,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Forward of the layer: router GEMM, routing, gather, expert up and down
+ * projections, combine (outline Parts 3-6).  X dtype [T,d] in; Y dtype [T,d]
+ * and every field of *r out; saved activations go to the workspace.
+ */
+int moe_forward(const moe_config* cfg, const void* X, const moe_weights* w,
+                void* Y, moe_routing* r,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of the layer (outline Parts 1-6 backward passes): from the
+ * caller's dY (dtype [T,d], the gradient of the loss with respect to Y) and
+ * aux_coef (the weight of the aux loss in the total loss), writes every
+ * gradient in *g.  Must follow moe_forward with the same cfg, X, w, *r and
+ * workspace, with no other call on that workspace in between.
+ */
+int moe_backward(const moe_config* cfg, const void* X, const moe_weights* w,
+                 const moe_routing* r, const void* dY, float aux_coef,
+                 moe_grads* g, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One training step (outline Part 7): forward, loss = MSE(Y, Y_target) +
+ * aux_coef * aux, backward, then SGD with learning rate lr on every
+ * parameter (masters, then working copies).  Y_target dtype [T,d].
+ * Writes Y, *r, *g and loss_out (device float[3] = {mse, aux, loss}).
+ */
+int moe_train_step(const moe_config* cfg, const void* X, const void* Y_target,
+                   moe_params* p, float lr, float aux_coef,
+                   void* Y, moe_routing* r, moe_grads* g, float* loss_out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stages of one training step, in launch order (moe_train_step_profiled). */
+#define MOE_STAGE_ROUTER_LOGITS   0   /* F1  l = X Wg^T                          */
+#define MOE_STAGE_ROUTE           1   /* F2-F3 top-k, gates, histogram, scan, slots, aux */
+#define MOE_STAGE_GATHER          2   /* F4  Xp = X[token_of]                    */
+#define MOE_STAGE_UP_FWD          3   /* F5  H = Xp W1^T (|W3^T), A = act(H)      */
+#define MOE_STAGE_DOWN_FWD        4   /* F6  EO = A W2^T (+ b2)                   */
+#define MOE_STAGE_COMBINE_LOSS    5   /* F7-F8 Y, MSE, dY, loss scalars           */
+#define MOE_STAGE_COMBINE_BWD     6   /* B1  dgate, dEO                           */
+#define MOE_STAGE_DOWN_DGRAD      7   /* B2  dA = dEO W2, activation backward     */
+#define MOE_STAGE_DOWN_WGRAD      8   /* B3  dW2 = dEO^T A                        */
+#define MOE_STAGE_UP_DGRAD        9   /* B4  dXp = dH W1 (+ dH3 W3)               */
+#define MOE_STAGE_UP_WGRAD       10   /* B5  dW1 (| dW3) = dH^T Xp                */
+#define MOE_STAGE_BIAS_GRADS     11   /*     db1, db2 (MLP kinds)                 */
+#define MOE_STAGE_ROUTER_BWD     12   /* B7  dlogits                              */
+#define MOE_STAGE_ROUTER_DWG     13   /* B8  dWg = dl^T X                         */
+#define MOE_STAGE_ROUTER_DX      14   /* B8  router part of dX = dl Wg            */
+#define MOE_STAGE_SCATTER        15   /* B6  dX = sum of dXp rows + router part   */
+#define MOE_STAGE_SGD            16   /* S1  masters and working copies           */
+#define MOE_NUM_STAGES           17
+
+/*
+ * moe_train_step with timing marks: the same launches, plus
+ * hipEventRecord(events[i], stream) right before the launches of stage i and
+ * hipEventRecord(events[MOE_NUM_STAGES], stream) after the last one.
+ * `events` holds MOE_NUM_STAGES + 1 hipEvent_t created by the caller
+ * (hipEventCreate); stage i took hipEventElapsedTime(events[i], events[i+1]).
+ * For measurement tools; identical results to moe_train_step.
+ */
+int moe_train_step_profiled(const moe_config* cfg, const void* X, const void* Y_target,
+                            moe_params* p, float lr, float aux_coef,
+                            void* Y, moe_routing* r, moe_grads* g, float* loss_out,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events);
+
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+
+/* ABI version (incremented on any incompatible change). */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

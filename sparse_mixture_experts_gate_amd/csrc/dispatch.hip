@@ -1,0 +1,254 @@
+// Token-major data movement of the sparse MoE layer for gfx950: gather into
+// expert-major rows, gate-weighted combine (with the MSE fused in), combine
+// backward, scatter of row gradients back to tokens, per-expert bias
+// reductions and the SGD update.
+//
+// Sources: "Trainable MoE in CUDA" outline Part 4 (gather, scatter, weighted
+// combine and its backward), Part 5 (bias gradients), Part 7 (MSE, SGD).
+//
+// Every kernel is HBM-bound.  One 64-lane wavefront owns one token and walks
+// its row in 16-byte vectors, so each row is read once and written with
+// coalesced 16-byte stores; the k expert-major rows of a token are visited
+// in the token's top-k order.  Sums run in a fixed order and there are no
+// atomics, so results are bitwise reproducible.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int TOK_WAVES = 4;    // tokens per 256-thread workgroup
+
+__device__ __forceinline__ void load_slots(const int32_t* slot_of, int t, int k, int* sl) {
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_K; ++i) sl[i] = (i < k) ? slot_of[(size_t)t * k + i] : 0;
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) gather_kernel(GatherArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * TOK_WAVES + (threadIdx.x >> 6);
+    if (t >= a.T) return;
+    int sl[MOE_MAX_K];
+    load_slots(a.slot_of, t, a.k, sl);
+    const uint4* src = reinterpret_cast<const uint4*>(a.X) + (size_t)t * a.vec;
+    uint4* dst = reinterpret_cast<uint4*>(a.Xp);
+    for (int v = lane; v < a.vec; v += 64) {
+        uint4 x = src[v];
+#pragma unroll
+        for (int i = 0; i < MOE_MAX_K; ++i) {
+            if (i >= a.k) break;
+            dst[(size_t)sl[i] * a.vec + v] = x;
+        }
+    }
+}
+
+template <class T, bool LOSS>
+__global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
+    __shared__ float s_part[TOK_WAVES];
+    constexpr int N = Vec16<T>::N;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * TOK_WAVES + wave;
+    float sq = 0.f;
+    if (t < a.T) {
+        int sl[MOE_MAX_K];
+        float g[MOE_MAX_K];
+        load_slots(a.slot_of, t, a.k, sl);
+#pragma unroll
+        for (int i = 0; i < MOE_MAX_K; ++i) g[i] = (i < a.k) ? a.gates[(size_t)t * a.k + i] : 0.f;
+        const uint4* eo = reinterpret_cast<const uint4*>(a.EO);
+        for (int v = lane; v < a.vec; v += 64) {
+            float acc[N];
+#pragma unroll
+            for (int j = 0; j < N; ++j) acc[j] = 0.f;
+#pragma unroll
+            for (int i = 0; i < MOE_MAX_K; ++i) {
+                if (i >= a.k) break;
+                float x[N];
+                Vec16<T>::unpack(eo[(size_t)sl[i] * a.vec + v], x);
+#pragma unroll
+                for (int j = 0; j < N; ++j) acc[j] = fmaf(g[i], x[j], acc[j]);
+            }
+            const size_t o = (size_t)t * a.vec + v;
+            reinterpret_cast<uint4*>(a.Y)[o] = Vec16<T>::pack(acc);
+            if (LOSS) {
+                float yt[N], dy[N];
+                Vec16<T>::unpack(reinterpret_cast<const uint4*>(a.Yt)[o], yt);
+#pragma unroll
+                for (int j = 0; j < N; ++j) {
+                    float r = acc[j] - yt[j];
+                    sq = fmaf(r, r, sq);
+                    dy[j] = r * a.inv_n2;
+                }
+                reinterpret_cast<uint4*>(a.dY)[o] = Vec16<T>::pack(dy);
+            }
+        }
+    }
+    if (LOSS) {
+        sq = wave_sum(sq);
+        if (lane == 0) s_part[wave] = sq;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float s = 0.f;
+            for (int w = 0; w < TOK_WAVES; ++w) s += s_part[w];
+            a.lpart[blockIdx.x] = s;
+        }
+    }
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) combine_bwd_kernel(CombineBwdArgs a) {
+    constexpr int N = Vec16<T>::N;
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * TOK_WAVES + (threadIdx.x >> 6);
+    if (t >= a.T) return;
+    int sl[MOE_MAX_K];
+    float g[MOE_MAX_K], dg[MOE_MAX_K];
+    load_slots(a.slot_of, t, a.k, sl);
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_K; ++i) {
+        g[i] = (i < a.k) ? a.gates[(size_t)t * a.k + i] : 0.f;
+        dg[i] = 0.f;
+    }
+    const uint4* dy4 = reinterpret_cast<const uint4*>(a.dY) + (size_t)t * a.vec;
+    const uint4* eo = reinterpret_cast<const uint4*>(a.EO);
+    uint4* deo = reinterpret_cast<uint4*>(a.dEO);
+    for (int v = lane; v < a.vec; v += 64) {
+        float dy[N];
+        Vec16<T>::unpack(dy4[v], dy);
+#pragma unroll
+        for (int i = 0; i < MOE_MAX_K; ++i) {
+            if (i >= a.k) break;
+            float x[N], o[N];
+            const size_t r = (size_t)sl[i] * a.vec + v;
+            Vec16<T>::unpack(eo[r], x);
+#pragma unroll
+            for (int j = 0; j < N; ++j) {
+                dg[i] = fmaf(dy[j], x[j], dg[i]);
+                o[j] = g[i] * dy[j];
+            }
+            deo[r] = Vec16<T>::pack(o);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_K; ++i) {
+        if (i >= a.k) break;
+        float s = wave_sum(dg[i]);
+        if (lane == 0) a.dgate[(size_t)t * a.k + i] = s;
+    }
+}
+
+template <class T>
+__global__ void __launch_bounds__(256) scatter_kernel(ScatterArgs a) {
+    constexpr int N = Vec16<T>::N;
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * TOK_WAVES + (threadIdx.x >> 6);
+    if (t >= a.T) return;
+    int sl[MOE_MAX_K];
+    load_slots(a.slot_of, t, a.k, sl);
+    const uint4* dxp = reinterpret_cast<const uint4*>(a.dXp);
+    // router-path gradient is fp32 [T, d]: N floats per vector of T
+    const float* dxr = a.dXr + (size_t)t * a.vec * N;
+    for (int v = lane; v < a.vec; v += 64) {
+        float acc[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) acc[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < MOE_MAX_K; ++i) {
+            if (i >= a.k) break;
+            float x[N];
+            Vec16<T>::unpack(dxp[(size_t)sl[i] * a.vec + v], x);
+#pragma unroll
+            for (int j = 0; j < N; ++j) acc[j] += x[j];
+        }
+#pragma unroll
+        for (int j = 0; j < N; ++j) acc[j] += dxr[v * N + j];
+        reinterpret_cast<uint4*>(a.dX)[(size_t)t * a.vec + v] = Vec16<T>::pack(acc);
+    }
+}
+
+// Column sums of each expert's row segment (bias gradients), fixed row order.
+template <class T>
+__global__ void __launch_bounds__(256) colsum_kernel(ColSumArgs a) {
+    const int e = blockIdx.y;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= a.ncols) return;
+    const int lo = a.offsets[e], hi = a.offsets[e + 1];
+    const T* src = reinterpret_cast<const T*>(a.src);
+    float s = 0.f;
+    for (int r = lo; r < hi; ++r) s += to_f<T>(src[(size_t)r * a.ld + c]);
+    a.dst[(size_t)e * a.ncols + c] = s;
+}
+
+// theta <- theta - lr * grad on the float32 master; working copy = RNE(master).
+template <class TW>
+__global__ void __launch_bounds__(256) sgd_kernel(SgdArgs a) {
+    const long n4 = a.n / 4;
+    const long stride = (long)gridDim.x * blockDim.x;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        float4 m = reinterpret_cast<float4*>(a.master)[i];
+        float4 g = reinterpret_cast<const float4*>(a.grad)[i];
+        m.x -= a.lr * g.x; m.y -= a.lr * g.y; m.z -= a.lr * g.z; m.w -= a.lr * g.w;
+        reinterpret_cast<float4*>(a.master)[i] = m;
+        TW* w = reinterpret_cast<TW*>(a.work) + 4 * i;
+        w[0] = from_f<TW>(m.x); w[1] = from_f<TW>(m.y);
+        w[2] = from_f<TW>(m.z); w[3] = from_f<TW>(m.w);
+    }
+    // tail (n not a multiple of 4)
+    for (long i = 4 * n4 + (long)blockIdx.x * blockDim.x + threadIdx.x; i < a.n; i += stride) {
+        float m = a.master[i] - a.lr * a.grad[i];
+        a.master[i] = m;
+        reinterpret_cast<TW*>(a.work)[i] = from_f<TW>(m);
+    }
+}
+
+// ---- host launchers ------------------------------------------------------------
+static inline dim3 tok_grid(int T) { return dim3((T + TOK_WAVES - 1) / TOK_WAVES); }
+int combine_loss_blocks(int T) { return (T + TOK_WAVES - 1) / TOK_WAVES; }
+
+hipError_t launch_gather(const GatherArgs& a, int dtype, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(gather_kernel<float>, tok_grid(a.T), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(gather_kernel<bf16>, tok_grid(a.T), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    const bool loss = a.Yt != nullptr;
+    if (dtype == MOE_DTYPE_F32) {
+        if (loss) hipLaunchKernelGGL((combine_kernel<float, true>), tok_grid(a.T), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((combine_kernel<float, false>), tok_grid(a.T), dim3(256), 0, s, a);
+    } else {
+        if (loss) hipLaunchKernelGGL((combine_kernel<bf16, true>), tok_grid(a.T), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((combine_kernel<bf16, false>), tok_grid(a.T), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, int dtype, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(combine_bwd_kernel<float>, tok_grid(a.T), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(combine_bwd_kernel<bf16>, tok_grid(a.T), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+hipError_t launch_scatter(const ScatterArgs& a, int dtype, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(scatter_kernel<float>, tok_grid(a.T), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(scatter_kernel<bf16>, tok_grid(a.T), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+hipError_t launch_colsum(const ColSumArgs& a, int dtype, hipStream_t s) {
+    dim3 grid((a.ncols + 255) / 256, a.E);
+    if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+hipError_t launch_sgd(const SgdArgs& a, int dtype, hipStream_t s) {
+    if (a.n == 0) return hipSuccess;
+    long blocks = (a.n / 4 + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 8192) blocks = 8192;
+    if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(sgd_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(sgd_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

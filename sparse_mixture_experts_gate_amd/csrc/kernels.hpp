@@ -1,0 +1,141 @@
+// Argument blocks and host launchers of the gfx950 kernels (internal to libmoe).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---- routing ------------------------------------------------------------------
+struct RouteArgs {
+    const float* logits;   // [T,E]
+    int32_t* topk_idx;     // [T,k]
+    float* gates;          // [T,k]
+    int32_t* hist;         // [E][nchunk]
+    float* qpart;          // [nchunk][E]
+    int T, E, k, n_groups, topk_groups, score, nchunk;
+};
+struct ScanArgs {
+    const int32_t* hist;   // [E][nchunk]
+    int32_t* cbase;        // [E][nchunk] exclusive prefix within each expert
+    int32_t* counts;       // [E]
+    int nchunk;
+};
+struct SlotArgs {
+    const int32_t* counts;
+    const int32_t* cbase;
+    const int32_t* topk_idx;
+    const float* gates;
+    int32_t* offsets;      // [E+1]
+    int32_t* tile_prefix;  // [3][MOE_MAX_EXPERTS+1]: m-tile prefix for 64/128/256-row tiles
+    int32_t* slot_of;      // [T,k]
+    int32_t* token_of;     // [T*k]
+    float* gate_of;        // [T*k]
+    int T, E, k, nchunk;
+};
+struct FinalizeArgs {
+    const float* qpart;
+    const int32_t* counts;
+    const float* lpart;    // NULL: no MSE
+    int nlpart;
+    float* aux_out;        // may be NULL
+    float* loss_out;       // may be NULL; [mse, aux, mse + aux_coef*aux]
+    float aux_coef;
+    int T, d, E, k, nchunk;
+};
+struct RouterBwdArgs {
+    const float* logits;
+    const int32_t* topk_idx;
+    const float* gates;
+    const float* dgate;
+    const int32_t* counts;
+    void* dlogits;         // [T,E] dtype
+    float aux_coef;
+    int T, E, k, score;
+};
+
+hipError_t launch_route_topk(const RouteArgs& a, hipStream_t s);
+hipError_t launch_expert_scan(const ScanArgs& a, int E, hipStream_t s);
+hipError_t launch_slot_assign(const SlotArgs& a, hipStream_t s);
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
+hipError_t launch_router_bwd(const RouterBwdArgs& a, int dtype, hipStream_t s);
+
+// ---- dispatch / combine / elementwise ------------------------------------------
+struct GatherArgs {
+    const void* X; const int32_t* slot_of; void* Xp;
+    int T, k, vec;         // vec = 16-byte vectors per row
+};
+struct CombineArgs {
+    const void* EO; const int32_t* slot_of; const float* gates; void* Y;
+    const void* Yt;        // NULL: no loss
+    void* dY;              // written when Yt != NULL: 2 (Y - Yt) / (T d)
+    float* lpart;          // per-workgroup sum of squared residuals
+    float inv_n2;          // 2 / (T d)
+    int T, k, vec;
+};
+struct CombineBwdArgs {
+    const void* dY; const void* EO; const int32_t* slot_of; const float* gates;
+    float* dgate; void* dEO;
+    int T, k, vec;
+};
+struct ScatterArgs {
+    const void* dXp; const int32_t* slot_of; const float* dXr; void* dX;
+    int T, k, vec;
+};
+struct ColSumArgs {
+    const void* src; long ld; const int32_t* offsets; float* dst; int ncols, E;
+};
+struct SgdArgs {
+    float* master; const float* grad; void* work; long n; float lr;
+};
+
+hipError_t launch_gather(const GatherArgs& a, int dtype, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s);
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, int dtype, hipStream_t s);
+hipError_t launch_scatter(const ScatterArgs& a, int dtype, hipStream_t s);
+hipError_t launch_colsum(const ColSumArgs& a, int dtype, hipStream_t s);
+hipError_t launch_sgd(const SgdArgs& a, int dtype, hipStream_t s);
+int combine_loss_blocks(int T);
+
+// ---- expert / router contractions -------------------------------------------------
+enum GemmEpi {
+    EPI_STORE = 0,         // C = acc (+ bias per column), dtype or fp32
+    EPI_UP_SWIGLU = 1,     // H1|H3 and A = silu(H1) * H3
+    EPI_UP_RELU = 2,       // H = acc + b1, A = relu(H)
+    EPI_UP_GELU = 3,       // H = acc + b1, A = gelu(H)
+    EPI_DN_SWIGLU = 4,     // dH1 = dA*H3*silu'(H1), dH3 = dA*silu(H1)
+    EPI_DN_RELU = 5,       // dH = dA * relu'(H)
+    EPI_DN_GELU = 6,       // dH = dA * gelu'(H)
+};
+
+// Expert contractions of the layer.  All row-major; see each field.
+struct ExpertGemmArgs {
+    int T, d, E, ffn, k, rows;       // rows = T*k
+    const int32_t* offsets;          // [E+1]
+    const int32_t* tile_prefix;      // [3][MOE_MAX_EXPERTS+1]
+    const void* Xp; const void* W1; const void* W3; const void* b1;
+    const void* W2; const void* b2;
+    void* H; void* A; void* EO;      // forward outputs / saved
+    const void* dEO; void* dH; void* dXp;  // backward
+    float* dW1; float* dW3; float* dW2;
+    int expert;                      // MOE_EXPERT_*
+};
+hipError_t launch_up_fwd(const ExpertGemmArgs& a, int dtype, hipStream_t s);
+hipError_t launch_down_fwd(const ExpertGemmArgs& a, int dtype, hipStream_t s);
+hipError_t launch_down_dgrad(const ExpertGemmArgs& a, int dtype, hipStream_t s);
+hipError_t launch_up_dgrad(const ExpertGemmArgs& a, int dtype, hipStream_t s);
+hipError_t launch_down_wgrad(const ExpertGemmArgs& a, int dtype, hipStream_t s);
+hipError_t launch_up_wgrad(const ExpertGemmArgs& a, int dtype, hipStream_t s);
+
+struct RouterGemmArgs {
+    int T, d, E;
+    const void* X; const void* Wg; const void* dl;
+    float* logits; float* dXr; float* dWg;
+};
+hipError_t launch_router_logits(const RouterGemmArgs& a, int dtype, hipStream_t s);
+hipError_t launch_router_dx(const RouterGemmArgs& a, int dtype, hipStream_t s);
+hipError_t launch_router_dwg(const RouterGemmArgs& a, int dtype, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,437 @@
+// C ABI of the sparse MoE layer: validation, workspace layout and the launch
+// sequence of each entry point (declared in include/moe.h).
+//
+// Sources: "Trainable MoE in CUDA" outline Parts 1-7 (the steps, in order:
+// router, top-k gating, dispatch/combine, expert MLP, aux loss, loss and SGD);
+// "AI Infra Kernel Lab" README "Quick start" (one public call that routes,
+// packs, computes experts and combines; explicit native paths fail rather
+// than fall back) and "Project status".
+//
+// Every call validates all of its arguments before the first launch, then
+// enqueues its kernels on the caller's stream with no host synchronisation:
+// counts, offsets and the expert GEMM tile schedule never leave the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace moe {
+// float32 layer contractions (gemm_simple.hip) and bfloat16 MFMA contractions
+// (gemm_mfma.hip)
+hipError_t simple_up_fwd(const ExpertGemmArgs&, hipStream_t);
+hipError_t simple_down_fwd(const ExpertGemmArgs&, hipStream_t);
+hipError_t simple_down_dgrad(const ExpertGemmArgs&, hipStream_t);
+hipError_t simple_up_dgrad(const ExpertGemmArgs&, hipStream_t);
+hipError_t simple_down_wgrad(const ExpertGemmArgs&, hipStream_t);
+hipError_t simple_up_wgrad(const ExpertGemmArgs&, hipStream_t);
+hipError_t simple_router_logits(const RouterGemmArgs&, hipStream_t);
+hipError_t simple_router_dx(const RouterGemmArgs&, hipStream_t);
+hipError_t simple_router_dwg(const RouterGemmArgs&, hipStream_t);
+hipError_t mfma_up_fwd(const ExpertGemmArgs&, hipStream_t);
+hipError_t mfma_down_fwd(const ExpertGemmArgs&, hipStream_t);
+hipError_t mfma_down_dgrad(const ExpertGemmArgs&, hipStream_t);
+hipError_t mfma_up_dgrad(const ExpertGemmArgs&, hipStream_t);
+hipError_t mfma_down_wgrad(const ExpertGemmArgs&, hipStream_t);
+hipError_t mfma_up_wgrad(const ExpertGemmArgs&, hipStream_t);
+hipError_t mfma_router_logits(const RouterGemmArgs&, hipStream_t);
+hipError_t mfma_router_dx(const RouterGemmArgs&, hipStream_t);
+hipError_t mfma_router_dwg(const RouterGemmArgs&, hipStream_t);
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+constexpr int kChunk = 64;
+
+enum WsBuf {
+    B_XP = 0, B_H, B_A, B_EO, B_DEO, B_DH, B_DXP, B_DY, B_DXR, B_DL, B_DGATE, B_GATEOF,
+    B_HIST, B_CBASE, B_QPART, B_LPART, B_TPREFIX, B_COUNT
+};
+
+struct Layout {
+    size_t off[B_COUNT];
+    size_t total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool shape_ok(const moe_config* c) {
+    if (!c) return false;
+    if (c->T < 0 || c->d < 1 || c->E < 1 || c->ffn < 1 || c->k < 1 || c->n_groups < 1 ||
+        c->topk_groups < 1)
+        return false;
+    if (c->k > c->E || c->E % c->n_groups != 0 || c->topk_groups > c->n_groups) return false;
+    if ((int64_t)c->k > (int64_t)c->topk_groups * (c->E / c->n_groups)) return false;
+    if ((int64_t)c->T * c->k >= (int64_t(1) << 31)) return false;
+    if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID) return false;
+    if (c->expert < MOE_EXPERT_RELU || c->expert > MOE_EXPERT_SWIGLU) return false;
+    if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16) return false;
+    return true;
+}
+
+int supported(const moe_config* c) {
+    if (c->E > MOE_MAX_EXPERTS || c->k > MOE_MAX_K || c->n_groups > 128) return MOE_ERR_UNSUPPORTED;
+    if (c->dtype == MOE_DTYPE_F32) {
+        if (c->d % 4 || c->ffn % 4) return MOE_ERR_UNSUPPORTED;
+    } else {
+        if (c->d % 64 || c->ffn % 64 || c->E % 8) return MOE_ERR_UNSUPPORTED;
+    }
+    return MOE_OK;
+}
+
+inline int esize(const moe_config* c) { return c->dtype == MOE_DTYPE_F32 ? 4 : 2; }
+inline int hcols(const moe_config* c) { return c->expert == MOE_EXPERT_SWIGLU ? 2 * c->ffn : c->ffn; }
+inline int nchunk(const moe_config* c) { return (c->T + kChunk - 1) / kChunk; }
+
+Layout layout(const moe_config* c) {
+    Layout L;
+    const size_t s = esize(c), T = c->T, rows = (size_t)c->T * c->k, d = c->d, E = c->E;
+    const size_t nc = nchunk(c);
+    size_t sz[B_COUNT];
+    sz[B_XP] = rows * d * s;
+    sz[B_H] = rows * hcols(c) * s;
+    sz[B_A] = rows * c->ffn * s;
+    sz[B_EO] = rows * d * s;
+    sz[B_DEO] = rows * d * s;
+    sz[B_DH] = rows * hcols(c) * s;
+    sz[B_DXP] = rows * d * s;
+    sz[B_DY] = T * d * s;
+    sz[B_DXR] = T * d * 4;
+    sz[B_DL] = T * E * s;
+    sz[B_DGATE] = T * c->k * 4;
+    sz[B_GATEOF] = rows * 4;
+    sz[B_HIST] = E * nc * 4;
+    sz[B_CBASE] = E * nc * 4;
+    sz[B_QPART] = nc * E * 4;
+    sz[B_LPART] = (size_t)combine_loss_blocks(c->T) * 4;
+    sz[B_TPREFIX] = 3 * (MOE_MAX_EXPERTS + 1) * 4;
+    size_t o = 0;
+    for (int b = 0; b < B_COUNT; ++b) {
+        L.off[b] = o;
+        o += align256(sz[b] > 0 ? sz[b] : 1);
+    }
+    L.total = o;
+    return L;
+}
+
+template <class P> inline bool aligned16(const P* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Device pointers of one call.  Token-sized tensors (tok = true) may be NULL
+// when T == 0, since they then hold no elements.
+struct Ptrs {
+    const void* list[40];
+    bool tok[40];
+    int n = 0;
+    void add(const void* p, bool t = false) { list[n] = p; tok[n] = t; ++n; }
+    int check(int T) const {
+        for (int i = 0; i < n; ++i) {
+            if (!list[i]) {
+                if (tok[i] && T == 0) continue;
+                return MOE_ERR_NULL_PTR;
+            }
+            if (!aligned16(list[i])) return MOE_ERR_MISALIGNED;
+        }
+        return MOE_OK;
+    }
+};
+
+int check_common(const moe_config* c, void* ws, size_t ws_bytes) {
+    if (!shape_ok(c)) return MOE_ERR_INVALID_ARG;
+    int st = supported(c);
+    if (st != MOE_OK) return st;
+    if (!ws || ws_bytes < layout(c).total) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
+    return MOE_OK;
+}
+
+void add_weights(Ptrs& P, const moe_config* c, const moe_weights* w) {
+    P.add(w->Wg); P.add(w->W1); P.add(w->W2);
+    if (c->expert == MOE_EXPERT_SWIGLU) P.add(w->W3);
+    else { P.add(w->b1); P.add(w->b2); }
+}
+
+void add_routing(Ptrs& P, const moe_routing* r, bool logits) {
+    if (logits) P.add(r->logits, true);
+    P.add(r->topk_idx, true); P.add(r->gates, true); P.add(r->counts); P.add(r->offsets);
+    P.add(r->slot_of, true); P.add(r->token_of, true); P.add(r->aux);
+}
+
+void add_grads(Ptrs& P, const moe_config* c, const moe_grads* g) {
+    P.add(g->dX, true); P.add(g->dWg); P.add(g->dW1); P.add(g->dW2);
+    if (c->expert == MOE_EXPERT_SWIGLU) P.add(g->dW3);
+    else { P.add(g->db1); P.add(g->db2); }
+}
+
+struct Ctx {
+    const moe_config* c;
+    char* ws;
+    Layout L;
+    hipStream_t s;
+    void* const* ev = nullptr;    // optional stage events (moe_train_step_profiled)
+    template <class T> T* buf(int b) const { return reinterpret_cast<T*>(ws + L.off[b]); }
+    hipError_t mark(int stage) const {
+        return ev ? hipEventRecord((hipEvent_t)ev[stage], s) : hipSuccess;
+    }
+};
+
+#define TRY(x)                                   \
+    do {                                         \
+        hipError_t _e = (x);                     \
+        if (_e != hipSuccess) return MOE_ERR_HIP; \
+    } while (0)
+
+// Routing from logits: top-k, gates, histogram, scan, slots, aux.
+int run_routing(const Ctx& x, const float* logits, moe_routing* r) {
+    const moe_config* c = x.c;
+    RouteArgs ra = {logits, r->topk_idx, r->gates, x.buf<int32_t>(B_HIST), x.buf<float>(B_QPART),
+                    c->T, c->E, c->k, c->n_groups, c->topk_groups, c->score, nchunk(c)};
+    TRY(launch_route_topk(ra, x.s));
+    ScanArgs sa = {x.buf<int32_t>(B_HIST), x.buf<int32_t>(B_CBASE), r->counts, nchunk(c)};
+    TRY(launch_expert_scan(sa, c->E, x.s));
+    SlotArgs sl = {r->counts, x.buf<int32_t>(B_CBASE), r->topk_idx, r->gates, r->offsets,
+                   x.buf<int32_t>(B_TPREFIX), r->slot_of, r->token_of, x.buf<float>(B_GATEOF),
+                   c->T, c->E, c->k, nchunk(c)};
+    TRY(launch_slot_assign(sl, x.s));
+    FinalizeArgs fa = {x.buf<float>(B_QPART), r->counts, nullptr, 0, r->aux, nullptr, 0.f,
+                       c->T, c->d, c->E, c->k, nchunk(c)};
+    TRY(launch_finalize(fa, x.s));
+    return MOE_OK;
+}
+
+ExpertGemmArgs expert_args(const Ctx& x, const moe_weights* w, const moe_routing* r) {
+    const moe_config* c = x.c;
+    ExpertGemmArgs a = {};
+    a.T = c->T; a.d = c->d; a.E = c->E; a.ffn = c->ffn; a.k = c->k; a.rows = c->T * c->k;
+    a.offsets = r->offsets;
+    a.tile_prefix = x.buf<int32_t>(B_TPREFIX);
+    a.Xp = x.buf<void>(B_XP);
+    a.W1 = w->W1; a.W3 = w->W3; a.W2 = w->W2;
+    a.b1 = c->expert == MOE_EXPERT_SWIGLU ? nullptr : w->b1;
+    a.b2 = c->expert == MOE_EXPERT_SWIGLU ? nullptr : w->b2;
+    a.H = x.buf<void>(B_H); a.A = x.buf<void>(B_A); a.EO = x.buf<void>(B_EO);
+    a.dEO = x.buf<void>(B_DEO); a.dH = x.buf<void>(B_DH); a.dXp = x.buf<void>(B_DXP);
+    a.expert = c->expert;
+    return a;
+}
+
+int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_routing* r,
+                const void* Yt, float aux_coef, float* loss_out) {
+    const moe_config* c = x.c;
+    const bool f32 = c->dtype == MOE_DTYPE_F32;
+    const int vec = c->d * esize(c) / 16;
+    RouterGemmArgs rg = {c->T, c->d, c->E, X, w->Wg, nullptr, r->logits, nullptr, nullptr};
+    TRY(x.mark(MOE_STAGE_ROUTER_LOGITS));
+    TRY(f32 ? simple_router_logits(rg, x.s) : mfma_router_logits(rg, x.s));
+    TRY(x.mark(MOE_STAGE_ROUTE));
+    int st = run_routing(x, r->logits, r);
+    if (st != MOE_OK) return st;
+    GatherArgs ga = {X, r->slot_of, x.buf<void>(B_XP), c->T, c->k, vec};
+    TRY(x.mark(MOE_STAGE_GATHER));
+    TRY(launch_gather(ga, c->dtype, x.s));
+    ExpertGemmArgs ea = expert_args(x, w, r);
+    TRY(x.mark(MOE_STAGE_UP_FWD));
+    TRY(f32 ? simple_up_fwd(ea, x.s) : mfma_up_fwd(ea, x.s));
+    TRY(x.mark(MOE_STAGE_DOWN_FWD));
+    TRY(f32 ? simple_down_fwd(ea, x.s) : mfma_down_fwd(ea, x.s));
+    TRY(x.mark(MOE_STAGE_COMBINE_LOSS));
+    CombineArgs ca = {x.buf<void>(B_EO), r->slot_of, r->gates, Y, Yt, x.buf<void>(B_DY),
+                      x.buf<float>(B_LPART), c->T > 0 ? 2.0f / ((float)c->T * (float)c->d) : 0.f,
+                      c->T, c->k, vec};
+    TRY(launch_combine(ca, c->dtype, x.s));
+    if (Yt) {
+        FinalizeArgs fa = {x.buf<float>(B_QPART), r->counts, x.buf<float>(B_LPART),
+                           combine_loss_blocks(c->T), nullptr, loss_out, aux_coef,
+                           c->T, c->d, c->E, c->k, nchunk(c)};
+        TRY(launch_finalize(fa, x.s));
+    }
+    return MOE_OK;
+}
+
+int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_routing* r,
+                 const void* dY, float aux_coef, moe_grads* g) {
+    const moe_config* c = x.c;
+    const bool f32 = c->dtype == MOE_DTYPE_F32;
+    const int vec = c->d * esize(c) / 16;
+    CombineBwdArgs cb = {dY, x.buf<void>(B_EO), r->slot_of, r->gates, x.buf<float>(B_DGATE),
+                         x.buf<void>(B_DEO), c->T, c->k, vec};
+    TRY(x.mark(MOE_STAGE_COMBINE_BWD));
+    TRY(launch_combine_bwd(cb, c->dtype, x.s));
+    ExpertGemmArgs ea = expert_args(x, w, r);
+    ea.dW1 = g->dW1; ea.dW2 = g->dW2; ea.dW3 = g->dW3;
+    TRY(x.mark(MOE_STAGE_DOWN_DGRAD));
+    TRY(f32 ? simple_down_dgrad(ea, x.s) : mfma_down_dgrad(ea, x.s));
+    TRY(x.mark(MOE_STAGE_DOWN_WGRAD));
+    TRY(f32 ? simple_down_wgrad(ea, x.s) : mfma_down_wgrad(ea, x.s));
+    TRY(x.mark(MOE_STAGE_UP_DGRAD));
+    TRY(f32 ? simple_up_dgrad(ea, x.s) : mfma_up_dgrad(ea, x.s));
+    TRY(x.mark(MOE_STAGE_UP_WGRAD));
+    TRY(f32 ? simple_up_wgrad(ea, x.s) : mfma_up_wgrad(ea, x.s));
+    TRY(x.mark(MOE_STAGE_BIAS_GRADS));
+    if (c->expert != MOE_EXPERT_SWIGLU) {
+        ColSumArgs b2 = {x.buf<void>(B_DEO), c->d, r->offsets, g->db2, c->d, c->E};
+        TRY(launch_colsum(b2, c->dtype, x.s));
+        ColSumArgs b1 = {x.buf<void>(B_DH), c->ffn, r->offsets, g->db1, c->ffn, c->E};
+        TRY(launch_colsum(b1, c->dtype, x.s));
+    }
+    RouterBwdArgs rb = {r->logits, r->topk_idx, r->gates, x.buf<float>(B_DGATE), r->counts,
+                        x.buf<void>(B_DL), aux_coef, c->T, c->E, c->k, c->score};
+    TRY(x.mark(MOE_STAGE_ROUTER_BWD));
+    TRY(launch_router_bwd(rb, c->dtype, x.s));
+    RouterGemmArgs rg = {c->T, c->d, c->E, X, w->Wg, x.buf<void>(B_DL), nullptr,
+                         x.buf<float>(B_DXR), g->dWg};
+    TRY(x.mark(MOE_STAGE_ROUTER_DWG));
+    TRY(f32 ? simple_router_dwg(rg, x.s) : mfma_router_dwg(rg, x.s));
+    TRY(x.mark(MOE_STAGE_ROUTER_DX));
+    TRY(f32 ? simple_router_dx(rg, x.s) : mfma_router_dx(rg, x.s));
+    ScatterArgs sa = {x.buf<void>(B_DXP), r->slot_of, x.buf<float>(B_DXR), g->dX, c->T, c->k, vec};
+    TRY(x.mark(MOE_STAGE_SCATTER));
+    TRY(launch_scatter(sa, c->dtype, x.s));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return 1; }
+
+const char* moe_status_string(int st) {
+    switch (st) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument: layer shape or config rule broken";
+        case MOE_ERR_NULL_PTR: return "a required pointer is NULL";
+        case MOE_ERR_MISALIGNED: return "a device pointer is not 16-byte aligned";
+        case MOE_ERR_WORKSPACE: return "workspace missing or smaller than moe_workspace_bytes()";
+        case MOE_ERR_UNSUPPORTED: return "shape outside what the gfx950 kernels support";
+        case MOE_ERR_HIP: return "a HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t moe_workspace_bytes(const moe_config* cfg) {
+    if (!shape_ok(cfg)) return 0;
+    return layout(cfg).total;
+}
+
+int64_t moe_workspace_offset(const moe_config* cfg, int32_t which) {
+    if (!shape_ok(cfg)) return -1;
+    Layout L = layout(cfg);
+    switch (which) {
+        case MOE_WS_XP: return (int64_t)L.off[B_XP];
+        case MOE_WS_H: return (int64_t)L.off[B_H];
+        case MOE_WS_A: return (int64_t)L.off[B_A];
+        case MOE_WS_EO: return (int64_t)L.off[B_EO];
+        default: return -1;
+    }
+}
+
+int moe_route(const moe_config* cfg, const float* logits, moe_routing* r, void* workspace,
+              size_t workspace_bytes, void* stream) {
+    int st = check_common(cfg, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    if (!r) return MOE_ERR_NULL_PTR;
+    Ptrs P;
+    P.add(logits, true);
+    add_routing(P, r, false);
+    if ((st = P.check(cfg->T)) != MOE_OK) return st;
+    Ctx x{cfg, (char*)workspace, layout(cfg), (hipStream_t)stream};
+    return run_routing(x, logits, r);
+}
+
+int moe_forward(const moe_config* cfg, const void* X, const moe_weights* w, void* Y,
+                moe_routing* r, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_common(cfg, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    if (!w || !r) return MOE_ERR_NULL_PTR;
+    Ptrs P;
+    P.add(X, true); P.add(Y, true);
+    add_weights(P, cfg, w);
+    add_routing(P, r, true);
+    if ((st = P.check(cfg->T)) != MOE_OK) return st;
+    Ctx x{cfg, (char*)workspace, layout(cfg), (hipStream_t)stream};
+    return run_forward(x, X, w, Y, r, nullptr, 0.f, nullptr);
+}
+
+int moe_backward(const moe_config* cfg, const void* X, const moe_weights* w, const moe_routing* r,
+                 const void* dY, float aux_coef, moe_grads* g, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    int st = check_common(cfg, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    if (!w || !r || !g) return MOE_ERR_NULL_PTR;
+    Ptrs P;
+    P.add(X, true); P.add(dY, true);
+    add_weights(P, cfg, w);
+    add_routing(P, r, true);
+    add_grads(P, cfg, g);
+    if ((st = P.check(cfg->T)) != MOE_OK) return st;
+    Ctx x{cfg, (char*)workspace, layout(cfg), (hipStream_t)stream};
+    return run_backward(x, X, w, r, dY, aux_coef, g);
+}
+
+static int train_step_impl(const moe_config* cfg, const void* X, const void* Y_target,
+                           moe_params* p, float lr, float aux_coef, void* Y, moe_routing* r,
+                           moe_grads* g, float* loss_out, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* events) {
+    int st = check_common(cfg, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    if (!p || !r || !g) return MOE_ERR_NULL_PTR;
+    const bool glu = cfg->expert == MOE_EXPERT_SWIGLU;
+    Ptrs P;
+    P.add(X, true); P.add(Y_target, true); P.add(Y, true); P.add(loss_out);
+    P.add(p->Wg); P.add(p->W1); P.add(p->W2); P.add(p->Wg_w); P.add(p->W1_w); P.add(p->W2_w);
+    if (glu) { P.add(p->W3); P.add(p->W3_w); }
+    else { P.add(p->b1); P.add(p->b2); P.add(p->b1_w); P.add(p->b2_w); }
+    add_routing(P, r, true);
+    add_grads(P, cfg, g);
+    if ((st = P.check(cfg->T)) != MOE_OK) return st;
+    if (events) {
+        for (int i = 0; i <= MOE_NUM_STAGES; ++i)
+            if (!events[i]) return MOE_ERR_NULL_PTR;
+    }
+    Ctx x{cfg, (char*)workspace, layout(cfg), (hipStream_t)stream, events};
+    moe_weights w = {p->Wg_w, p->W1_w, glu ? nullptr : p->b1_w, p->W2_w, glu ? nullptr : p->b2_w,
+                     glu ? p->W3_w : nullptr};
+    st = run_forward(x, X, &w, Y, r, Y_target, aux_coef, loss_out);
+    if (st != MOE_OK) return st;
+    st = run_backward(x, X, &w, r, x.buf<void>(B_DY), aux_coef, g);
+    if (st != MOE_OK) return st;
+    const long E = cfg->E, d = cfg->d, ffn = cfg->ffn;
+    struct { float* m; const float* g; void* w; long n; } upd[6] = {
+        {p->Wg, g->dWg, p->Wg_w, E * d},
+        {p->W1, g->dW1, p->W1_w, E * ffn * d},
+        {p->W2, g->dW2, p->W2_w, E * d * ffn},
+        {glu ? p->W3 : nullptr, g->dW3, p->W3_w, E * ffn * d},
+        {glu ? nullptr : p->b1, g->db1, p->b1_w, E * ffn},
+        {glu ? nullptr : p->b2, g->db2, p->b2_w, E * d},
+    };
+    TRY(x.mark(MOE_STAGE_SGD));
+    for (auto& u : upd) {
+        if (!u.m) continue;
+        SgdArgs sa = {u.m, u.g, u.w, u.n, lr};
+        TRY(launch_sgd(sa, cfg->dtype, x.s));
+    }
+    TRY(x.mark(MOE_NUM_STAGES));
+    return MOE_OK;
+}
+
+int moe_train_step(const moe_config* cfg, const void* X, const void* Y_target, moe_params* p,
+                   float lr, float aux_coef, void* Y, moe_routing* r, moe_grads* g,
+                   float* loss_out, void* workspace, size_t workspace_bytes, void* stream) {
+    return train_step_impl(cfg, X, Y_target, p, lr, aux_coef, Y, r, g, loss_out, workspace,
+                           workspace_bytes, stream, nullptr);
+}
+
+int moe_train_step_profiled(const moe_config* cfg, const void* X, const void* Y_target,
+                            moe_params* p, float lr, float aux_coef, void* Y, moe_routing* r,
+                            moe_grads* g, float* loss_out, void* workspace, size_t workspace_bytes,
+                            void* stream, void* const* events) {
+    if (!events) return MOE_ERR_NULL_PTR;
+    return train_step_impl(cfg, X, Y_target, p, lr, aux_coef, Y, r, g, loss_out, workspace,
+                           workspace_bytes, stream, events);
+}
+
+}  // extern "C"

@@ -1,0 +1,443 @@
+// Router scoring, group-limited top-k, gate renormalisation, dispatch tables,
+// aux loss and the router backward, for gfx950.
+//
+// Sources: "Trainable MoE in CUDA" outline Part 2 (top-k and gate
+// normalisation with its backward), Part 3 (router), Part 4 (counts, offsets,
+// slots), Part 6 (aux loss); "AI Infra Kernel Lab" README, "Project status"
+// (group-limited selection, ties to the smaller group/expert id).
+//
+// Layout: one 64-lane wavefront owns one token at a time; lane j holds the
+// logits of experts j, j+64, j+128, j+192.  A workgroup of four wavefronts
+// owns a chunk of 64 consecutive tokens, which is the unit of the histogram
+// and of the stable slot ranking.  No floating-point atomics anywhere; the
+// integer LDS histogram is order-independent and every float sum runs in a
+// fixed order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int CHUNK = 64;       // tokens per histogram chunk
+constexpr int RT_WAVES = 4;     // wavefronts per routing workgroup
+constexpr int EPL = MOE_MAX_EXPERTS / 64;  // expert values held per lane
+
+// a beats b in the selection order (-value, id): larger value, then smaller id.
+__device__ __forceinline__ bool beats(float va, int ia, float vb, int ib) {
+    return (va > vb) || (va == vb && ia < ib);
+}
+
+// Wave-wide arg-max under (-value, id); every lane gets the winner.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        float vo = __shfl_xor(v, o, MOE_WAVE);
+        int io = __shfl_xor(i, o, MOE_WAVE);
+        if (beats(vo, io, v, i)) { v = vo; i = io; }
+    }
+}
+
+struct TokenScores {
+    float l[EPL];     // logits
+    float s[EPL];     // softmax p, or sigmoid s
+    float q[EPL];     // aux probabilities
+    float mx, z;      // softmax max and denominator; sigmoid: z = sum of s
+};
+
+__device__ __forceinline__ void score_token(const float* __restrict__ lrow, int E, int score,
+                                            TokenScores& ts) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) {
+        int e = lane + 64 * m;
+        ts.l[m] = (e < E) ? lrow[e] : -INFINITY;
+    }
+    if (score == MOE_SCORE_SOFTMAX) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) mx = fmaxf(mx, ts.l[m]);
+        mx = wave_max(mx);
+        float z = 0.f;
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) {
+            int e = lane + 64 * m;
+            ts.s[m] = (e < E) ? expf(ts.l[m] - mx) : 0.f;
+            z += ts.s[m];
+        }
+        z = wave_sum(z);
+        float inv = 1.0f / z;
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) { ts.s[m] *= inv; ts.q[m] = ts.s[m]; }
+        ts.mx = mx; ts.z = z;
+    } else {
+        float z = 0.f;
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) {
+            int e = lane + 64 * m;
+            ts.s[m] = (e < E) ? 1.0f / (1.0f + expf(-ts.l[m])) : 0.f;
+            z += ts.s[m];
+        }
+        z = wave_sum(z);
+        float inv = 1.0f / z;
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) ts.q[m] = ts.s[m] * inv;
+        ts.mx = 0.f; ts.z = z;
+    }
+}
+
+// Score of expert e (owned by some lane) without a shuffle: recompute from its logit.
+__device__ __forceinline__ float selected_score(float l, const TokenScores& ts, int score) {
+    if (score == MOE_SCORE_SOFTMAX) return expf(l - ts.mx) / ts.z;
+    return 1.0f / (1.0f + expf(-l));
+}
+
+__global__ void __launch_bounds__(256)
+route_topk_kernel(RouteArgs a) {
+    __shared__ int s_hist[MOE_MAX_EXPERTS];
+    __shared__ float s_q[RT_WAVES][MOE_MAX_EXPERTS];
+    __shared__ float s_l[RT_WAVES][MOE_MAX_EXPERTS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.E, k = a.k, G = a.n_groups;
+    const int chunk = blockIdx.x;
+    for (int e = tid; e < E; e += blockDim.x) s_hist[e] = 0;
+    __syncthreads();
+
+    float qacc[EPL];
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) qacc[m] = 0.f;
+
+    const int gsize = E / G;
+    for (int it = 0; it < CHUNK / RT_WAVES; ++it) {
+        const int t = chunk * CHUNK + wave * (CHUNK / RT_WAVES) + it;
+        if (t >= a.T) break;                        // wave-uniform
+        TokenScores ts;
+        score_token(a.logits + (size_t)t * E, E, a.score, ts);
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) qacc[m] += ts.q[m];
+
+        // group limit: keep topk_groups groups by (-max member logit, group id)
+        uint64_t kept_lo = ~0ull, kept_hi = ~0ull;   // bit per group (G <= 128 supported)
+        if (G > 1) {
+#pragma unroll
+            for (int m = 0; m < EPL; ++m) {
+                int e = lane + 64 * m;
+                if (e < E) s_l[wave][e] = ts.l[m];
+            }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float gv0 = -INFINITY, gv1 = -INFINITY;    // lanes own groups lane, lane+64
+            if (lane < G) {
+                for (int j = 0; j < gsize; ++j) gv0 = fmaxf(gv0, s_l[wave][lane * gsize + j]);
+            }
+            if (lane + 64 < G) {
+                for (int j = 0; j < gsize; ++j) gv1 = fmaxf(gv1, s_l[wave][(lane + 64) * gsize + j]);
+            }
+            kept_lo = kept_hi = 0;
+            bool t0 = lane >= G, t1 = lane + 64 >= G;  // taken / absent
+            for (int r = 0; r < a.topk_groups; ++r) {
+                float bv = -INFINITY; int bi = 0x7fffffff;
+                if (!t0 && beats(gv0, lane, bv, bi)) { bv = gv0; bi = lane; }
+                if (!t1 && beats(gv1, lane + 64, bv, bi)) { bv = gv1; bi = lane + 64; }
+                wave_argmax(bv, bi);
+                if (bi < 64) kept_lo |= 1ull << bi; else kept_hi |= 1ull << (bi - 64);
+                if (bi == lane) t0 = true;
+                if (bi == lane + 64) t1 = true;
+            }
+        }
+
+        // top-k over eligible experts by (-logit, id)
+        bool taken[EPL];
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) {
+            int e = lane + 64 * m;
+            bool elig = e < E;
+            if (G > 1 && elig) {
+                int g = e / gsize;
+                elig = (g < 64) ? ((kept_lo >> g) & 1) : ((kept_hi >> (g - 64)) & 1);
+            }
+            taken[m] = !elig;
+        }
+        int sel_e = -1;      // lane i < k keeps the i-th pick
+        float sel_l = 0.f;
+        for (int i = 0; i < k; ++i) {
+            float bv = -INFINITY; int bi = 0x7fffffff;
+#pragma unroll
+            for (int m = 0; m < EPL; ++m) {
+                int e = lane + 64 * m;
+                if (!taken[m] && beats(ts.l[m], e, bv, bi)) { bv = ts.l[m]; bi = e; }
+            }
+            wave_argmax(bv, bi);
+#pragma unroll
+            for (int m = 0; m < EPL; ++m)
+                if (bi == lane + 64 * m) taken[m] = true;
+            if (lane == i) { sel_e = bi; sel_l = bv; }
+        }
+        // finite logits always leave k eligible experts; keep indices in range even
+        // for malformed (NaN) input so that no later kernel indexes out of bounds
+        if (lane < k && (sel_e < 0 || sel_e >= E)) sel_e = 0;
+        float w = (lane < k) ? selected_score(sel_l, ts, a.score) : 0.f;
+        float S = wave_sum(w);
+        if (lane < k) {
+            a.topk_idx[(size_t)t * k + lane] = sel_e;
+            a.gates[(size_t)t * k + lane] = w / S;
+            atomicAdd(&s_hist[sel_e], 1);
+        }
+    }
+
+    // aux partial sums: waves' running sums (token order) added in wave order
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) {
+        int e = lane + 64 * m;
+        if (e < E) s_q[wave][e] = qacc[m];
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) {
+        float v = 0.f;
+        for (int w = 0; w < RT_WAVES; ++w) v += s_q[w][e];
+        a.qpart[(size_t)chunk * E + e] = v;
+        a.hist[(size_t)e * a.nchunk + chunk] = s_hist[e];
+    }
+}
+
+// One workgroup per expert: exclusive scan of its per-chunk counts.
+__global__ void __launch_bounds__(256)
+expert_scan_kernel(ScanArgs a) {
+    __shared__ int s_wave[4];
+    const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int* h = a.hist + (size_t)e * a.nchunk;
+    int* cb = a.cbase + (size_t)e * a.nchunk;
+    int running = 0;
+    for (int base = 0; base < a.nchunk; base += 256) {
+        int c = base + tid;
+        int v = (c < a.nchunk) ? h[c] : 0;
+        int inc = wave_incl_scan(v);
+        if (lane == 63) s_wave[wave] = inc;
+        __syncthreads();
+        int before = running;
+        for (int w = 0; w < wave; ++w) before += s_wave[w];
+        if (c < a.nchunk) cb[c] = before + inc - v;
+        int tot = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+        __syncthreads();
+        running += tot;
+    }
+    if (tid == 0) a.counts[e] = running;
+}
+
+// One wavefront per chunk of 64 tokens: stable slots in ascending token order.
+__global__ void __launch_bounds__(64)
+slot_assign_kernel(SlotArgs a) {
+    __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+    const int lane = threadIdx.x, chunk = blockIdx.x, E = a.E, k = a.k;
+    // offsets = exclusive scan of counts (lane owns experts 4*lane .. 4*lane+3)
+    int c4[4], loc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int e = lane * 4 + j;
+        c4[j] = (e < E) ? a.counts[e] : 0;
+        loc += c4[j];
+    }
+    int incl = wave_incl_scan(loc);
+    int run = incl - loc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        int e = lane * 4 + j;
+        if (e < E) s_off[e] = run;
+        run += c4[j];
+    }
+    if (lane == 63) s_off[E] = incl;
+    __syncthreads();
+    if (chunk == 0) {
+        for (int e = lane; e <= E; e += 64) a.offsets[e] = s_off[e];
+        // m-tile prefix of every supported tile height (64, 128, 256 rows)
+        for (int b = 0; b < 3; ++b) {
+            const int bm = 64 << b;
+            int tl = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) tl += (c4[j] + bm - 1) / bm;
+            int ti = wave_incl_scan(tl);
+            int tr = ti - tl;
+            int* tp = a.tile_prefix + b * (MOE_MAX_EXPERTS + 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int e = lane * 4 + j;
+                if (e < E) tp[e] = tr;
+                tr += (c4[j] + bm - 1) / bm;
+            }
+            if (lane == 63) tp[E] = ti;
+        }
+    }
+    const int t = chunk * CHUNK + lane;
+    const bool valid = t < a.T;
+    int ex[MOE_MAX_K];
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_K; ++i) ex[i] = (valid && i < k) ? a.topk_idx[(size_t)t * k + i] : -1;
+    int cnt[MOE_MAX_K];
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_K; ++i) cnt[i] = 0;
+    // rank among earlier tokens of the chunk that chose the same expert
+    for (int src = 0; src < 63; ++src) {
+        const bool before = src < lane;
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_K; ++j) {
+            if (j >= k) break;
+            int ej = __builtin_amdgcn_readlane(ex[j], src);
+#pragma unroll
+            for (int i = 0; i < MOE_MAX_K; ++i) {
+                if (i >= k) break;
+                cnt[i] += (before && ej == ex[i]) ? 1 : 0;
+            }
+        }
+    }
+    if (!valid) return;
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_K; ++i) {
+        if (i >= k) break;
+        const int e = ex[i];
+        const int slot = s_off[e] + a.cbase[(size_t)e * a.nchunk + chunk] + cnt[i];
+        a.slot_of[(size_t)t * k + i] = slot;
+        a.token_of[slot] = t;
+        a.gate_of[slot] = a.gates[(size_t)t * k + i];
+    }
+}
+
+// Single workgroup: P_e, f_e, aux and (optionally) the MSE from partial sums.
+__global__ void __launch_bounds__(256)
+finalize_kernel(FinalizeArgs a) {
+    __shared__ float s_red[256];
+    const int tid = threadIdx.x;
+    float part = 0.f;
+    if (a.T > 0) {
+        for (int e = tid; e < a.E; e += 256) {
+            float P = 0.f;
+            for (int c = 0; c < a.nchunk; ++c) P += a.qpart[(size_t)c * a.E + e];
+            P /= (float)a.T;
+            float f = (float)a.counts[e] / ((float)a.T * (float)a.k);
+            part += f * P;
+        }
+    }
+    s_red[tid] = part;
+    __syncthreads();
+    for (int s = 128; s >= 1; s >>= 1) {
+        if (tid < s) s_red[tid] += s_red[tid + s];
+        __syncthreads();
+    }
+    float aux = (float)a.E * s_red[0];
+    __syncthreads();
+    float mse = 0.f;
+    if (a.lpart != nullptr) {
+        float v = 0.f;
+        for (int b = tid; b < a.nlpart; b += 256) v += a.lpart[b];
+        s_red[tid] = v;
+        __syncthreads();
+        for (int s = 128; s >= 1; s >>= 1) {
+            if (tid < s) s_red[tid] += s_red[tid + s];
+            __syncthreads();
+        }
+        double n = (double)a.T * (double)a.d;
+        mse = (n > 0) ? (float)((double)s_red[0] / n) : 0.f;
+    }
+    if (tid == 0) {
+        if (a.aux_out) a.aux_out[0] = aux;
+        if (a.loss_out) {
+            a.loss_out[0] = mse;
+            a.loss_out[1] = aux;
+            a.loss_out[2] = mse + a.aux_coef * aux;
+        }
+    }
+}
+
+// Router backward: renormalisation, aux gradient and score Jacobian -> dlogits.
+template <class TD>
+__global__ void __launch_bounds__(256)
+router_bwd_kernel(RouterBwdArgs a) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= a.T) return;
+    const int E = a.E, k = a.k;
+    TokenScores ts;
+    score_token(a.logits + (size_t)t * E, E, a.score, ts);
+    int e_i = -1;
+    float g_i = 0.f, dg_i = 0.f, w_i = 0.f;
+    if (lane < k) {
+        e_i = a.topk_idx[(size_t)t * k + lane];
+        g_i = a.gates[(size_t)t * k + lane];
+        dg_i = a.dgate[(size_t)t * k + lane];
+        w_i = selected_score(a.logits[(size_t)t * E + e_i], ts, a.score);
+    }
+    const float S = wave_sum(w_i);
+    const float gdg = wave_sum(g_i * dg_i);
+    const float dw_i = (lane < k) ? (dg_i - gdg) / S : 0.f;
+    // aux gradient: dq_te = aux_coef * E * f_e / T, f_e = counts_e / (T k)
+    const float c0 = a.aux_coef * (float)E / ((float)a.T * (float)a.T * (float)k);
+    float sel[EPL], dq[EPL];
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) {
+        int e = lane + 64 * m;
+        sel[m] = 0.f;
+        dq[m] = (e < E) ? c0 * (float)a.counts[e] : 0.f;
+    }
+    for (int i = 0; i < k; ++i) {
+        int ei = __builtin_amdgcn_readlane(e_i, i);
+        float dwi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dw_i), i));
+#pragma unroll
+        for (int m = 0; m < EPL; ++m)
+            if (ei == lane + 64 * m) sel[m] += dwi;
+    }
+    float out[EPL];
+    if (a.score == MOE_SCORE_SOFTMAX) {
+        float dot = 0.f;
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) dot += (dq[m] + sel[m]) * ts.s[m];
+        dot = wave_sum(dot);
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) out[m] = ts.s[m] * (dq[m] + sel[m] - dot);
+    } else {
+        float dot = 0.f;
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) dot += dq[m] * ts.q[m];
+        dot = wave_sum(dot);
+        const float invZ = 1.0f / ts.z;
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) {
+            float ds = sel[m] + (dq[m] - dot) * invZ;
+            out[m] = ds * ts.s[m] * (1.0f - ts.s[m]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) {
+        int e = lane + 64 * m;
+        if (e < E) reinterpret_cast<TD*>(a.dlogits)[(size_t)t * E + e] = from_f<TD>(out[m]);
+    }
+}
+
+// ---- host launchers ------------------------------------------------------------
+hipError_t launch_route_topk(const RouteArgs& a, hipStream_t s) {
+    if (a.nchunk == 0) return hipSuccess;
+    hipLaunchKernelGGL(route_topk_kernel, dim3(a.nchunk), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+hipError_t launch_expert_scan(const ScanArgs& a, int E, hipStream_t s) {
+    hipLaunchKernelGGL(expert_scan_kernel, dim3(E), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+hipError_t launch_slot_assign(const SlotArgs& a, hipStream_t s) {
+    // one workgroup at least, so that offsets and tile prefixes are written for T == 0
+    int grid = a.nchunk > 0 ? a.nchunk : 1;
+    hipLaunchKernelGGL(slot_assign_kernel, dim3(grid), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+hipError_t launch_router_bwd(const RouterBwdArgs& a, int dtype, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    dim3 grid((a.T + 3) / 4);
+    if (dtype == MOE_DTYPE_F32)
+        hipLaunchKernelGGL(router_bwd_kernel<float>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(router_bwd_kernel<bf16>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -132,35 +132,41 @@ def make_expert(w: Workload, which: str, e: int, seed: int = 0, device="cpu") ->
     return _normal(shape, expert_std(w, which), tensor_seed(seed, which, e), device)
 
 
-def make_inputs(w: Workload, seed: int = 0, device="cpu") -> Dict[str, Optional[torch.Tensor]]:
+def make_inputs(w: Workload, seed: int = 0, device="cpu",
+                masters: bool = True) -> Dict[str, Optional[torch.Tensor]]:
     """All inputs of one layer step: activations, targets, master and working weights.
 
     Returned keys: X, Yt (working dtype); Wg, W1, b1, W2, b2, W3 (float32
     masters); and the same names with a ``_w`` suffix for the working copies.
-    Tensors that the expert kind does not use are None.
+    Tensors that the expert kind does not use are None.  With masters=False
+    the float32 masters are not kept (their keys hold None) and only the
+    working copies are built, one expert at a time.
     """
     wd = w.torch_dtype
     out: Dict[str, Optional[torch.Tensor]] = {}
     out["X"] = _normal((w.T, w.d), 1.0, tensor_seed(seed, "X"), device).to(wd)
     out["Yt"] = _normal((w.T, w.d), 1.0, tensor_seed(seed, "Yt"), device).to(wd)
-    out["Wg"] = make_gate(w, seed, device)
-    names = ["W1", "W2"] + (["W3"] if w.expert == "swiglu" else [])
+    gate = make_gate(w, seed, device)
+    out["Wg"], out["Wg_w"] = (gate if masters else None), gate.to(wd)
     for n in ("W1", "W2", "W3"):
-        if n not in names:
-            out[n] = None
+        if n == "W3" and w.expert != "swiglu":
+            out[n] = out[n + "_w"] = None
             continue
         shape = (w.E, w.d, w.ffn) if n == "W2" else (w.E, w.ffn, w.d)
-        t = torch.empty(shape, dtype=torch.float32, device=device)
+        master = torch.empty(shape, dtype=torch.float32, device=device) if masters else None
+        work = torch.empty(shape, dtype=wd, device=device)
         for e in range(w.E):
-            t[e] = make_expert(w, n, e, seed, device)
-        out[n] = t
+            t = make_expert(w, n, e, seed, device)
+            if masters:
+                master[e] = t
+            work[e] = t.to(wd)
+        out[n], out[n + "_w"] = master, work
     if w.has_bias:
-        out["b1"] = torch.zeros((w.E, w.ffn), dtype=torch.float32, device=device)
-        out["b2"] = torch.zeros((w.E, w.d), dtype=torch.float32, device=device)
+        for n, shape in (("b1", (w.E, w.ffn)), ("b2", (w.E, w.d))):
+            z = torch.zeros(shape, dtype=torch.float32, device=device)
+            out[n], out[n + "_w"] = (z if masters else None), z.to(wd)
     else:
-        out["b1"] = out["b2"] = None
-    for n in ("Wg", "W1", "b1", "W2", "b2", "W3"):
-        out[n + "_w"] = None if out[n] is None else out[n].to(wd)
+        out["b1"] = out["b2"] = out["b1_w"] = out["b2_w"] = None
     return out
 
 

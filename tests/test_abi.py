@@ -1,0 +1,127 @@
+"""The C-ABI library loads and exports what include/moe.h declares (no GPU needed).
+
+Only host-side entry points are called here: workspace sizing, status
+strings, and argument validation, which returns before any launch.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_mixture_experts_gate_amd import _lib as L
+from sparse_mixture_experts_gate_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(moe_[a-z_]+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libmoe.so is not built (python -m sparse_mixture_experts_gate_amd.build)")
+    return L.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == sorted(L.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (moe_[a-z_]+)\b", out))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings_and_version(lib):
+    assert L.abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert L.status_string(code) and L.status_string(code) != "unknown status"
+    assert L.status_string(12345) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    for w in W.WORKLOADS:
+        n = L.workspace_bytes(L.config(w))
+        # the saved activations alone: Xp, H, A, EO
+        s = 4 if w.dtype == "f32" else 2
+        hc = 2 * w.ffn if w.expert == "swiglu" else w.ffn
+        assert n >= w.T * w.k * (2 * w.d + hc + w.ffn) * s
+        offs = [L.workspace_offset(L.config(w), b) for b in ("XP", "H", "A", "EO")]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    bad = W.WORKLOADS[0].replace(k=5)            # k > E
+    assert L.workspace_bytes(L.config(bad)) == 0
+    assert L.workspace_offset(L.config(bad), "H") == -1
+
+
+def _call_forward(cfg, ws_bytes=1 << 30, ptr=4096, ws_ptr=4096):
+    lib = L.load()
+    w = L.moe_weights(ptr, ptr, ptr, ptr, ptr, ptr)
+    r = L.moe_routing(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr)
+    return lib.moe_forward(ctypes.byref(cfg), ctypes.c_void_p(ptr), ctypes.byref(w), ctypes.c_void_p(ptr),
+                           ctypes.byref(r), ctypes.c_void_p(ws_ptr), ws_bytes, None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(k=5), -1),                           # k > E
+    (dict(n_groups=3), -1),                    # E % n_groups
+    (dict(n_groups=2, topk_groups=3), -1),     # topk_groups > n_groups
+    (dict(n_groups=4, topk_groups=1, k=2), -1),  # k > topk_groups * E / n_groups
+    (dict(T=-1), -1),
+    (dict(score=7), -1),
+    (dict(E=512, k=2), -5),                    # more experts than the kernels hold
+    (dict(k=17, E=32), -5),
+    (dict(d=30), -5),                          # float32 rows must be 16-byte vectors
+])
+def test_invalid_configs_are_rejected_before_launch(lib, change, code):
+    cfg = L.config(W.WORKLOADS[0].replace(**change))
+    assert _call_forward(cfg) == code
+
+
+def test_bf16_shape_rules(lib):
+    w = W.BY_NAME["gelu_mlp_t4096_d1024_e8"]
+    assert _call_forward(L.config(w.replace(d=1000))) == -5
+    assert _call_forward(L.config(w.replace(ffn=4000))) == -5
+    assert _call_forward(L.config(w.replace(E=12, k=2))) == -5
+
+
+def test_pointer_and_workspace_errors(lib):
+    cfg = L.config(W.WORKLOADS[0])
+    need = L.workspace_bytes(cfg)
+    assert _call_forward(cfg, ws_bytes=need - 1) == -4
+    assert _call_forward(cfg, ws_ptr=0) == -4
+    assert _call_forward(cfg, ptr=4100) == -3           # not 16-byte aligned
+    lib = L.load()
+    w = L.moe_weights(4096, None, None, 4096, None, None)   # W1 missing
+    r = L.moe_routing(*([4096] * 8))
+    st = lib.moe_forward(ctypes.byref(cfg), ctypes.c_void_p(4096), ctypes.byref(w), ctypes.c_void_p(4096),
+                         ctypes.byref(r), ctypes.c_void_p(4096), need, None)
+    assert st == -2
+
+
+def test_binding_raises_on_error_status(lib):
+    with pytest.raises(L.MoeError) as ei:
+        L._check(-4, "moe_forward")
+    assert ei.value.status == -4 and "MOE_ERR_WORKSPACE" in str(ei.value)
+
+
+def test_one_hip_runtime_per_process(lib):
+    """libmoe.so and the event helper bind to the HIP runtime torch loaded, so
+    torch's stream handles are valid inside the library."""
+    import torch  # noqa: F401
+    L.StageEvents.__init__  # the helper opens the runtime by its SONAME
+    ctypes.CDLL("libamdhip64.so.7")
+    maps = open("/proc/self/maps").read()
+    hips = sorted(set(re.findall(r"\S*libamdhip64\S*", maps)))
+    assert len(hips) == 1, hips
