@@ -65,9 +65,9 @@ def test_route_bit_exact(T, E, k, G, TG, score, kind):
     assert np.array_equal(r["token_of"].numpy(), rt.token_of)
     if T:
         g, _ = O.gate_weights(l64, ref, score)
-        assert_close("gates", r["gates"].double().numpy(), g, 1e-5, 1e-6)
+        assert_close("gates", r["gates"].double().numpy(), g, 1e-5, 1e-5)
         aux, _, _ = O.aux_loss(rt.counts, O.aux_probs(l64, score), k)
-        assert_close("aux", r["aux"].double().numpy(), [aux], 1e-5, 0)
+        assert_close("aux", r["aux"].double().numpy(), [aux], 1e-5, 1e-5)
     else:
         assert float(r["aux"][0]) == 0.0
 
