@@ -180,24 +180,47 @@ __global__ void __launch_bounds__(256) colsum_kernel(ColSumArgs a) {
 }
 
 // theta <- theta - lr * grad on the float32 master; working copy = RNE(master).
+// Streaming kernel: each thread moves 8 parameters per step with 16-byte
+// accesses only (two float4 of master, two of gradient, one 16-byte vector of
+// bf16 working copy), two steps in flight; gradients are read once and the
+// outputs are not re-read, so those accesses carry the nontemporal hint.
+__device__ __forceinline__ float4 ld_nt(const float4* p) { return __builtin_nontemporal_load(p); }
+
+template <class TW>
+__device__ __forceinline__ void sgd8(float* master, const float* grad, void* work, long i, float lr) {
+    float4* m4 = reinterpret_cast<float4*>(master) + 2 * i;
+    const float4* g4 = reinterpret_cast<const float4*>(grad) + 2 * i;
+    float4 m0 = m4[0], m1 = m4[1];
+    const float4 g0 = ld_nt(g4), g1 = ld_nt(g4 + 1);
+    m0.x -= lr * g0.x; m0.y -= lr * g0.y; m0.z -= lr * g0.z; m0.w -= lr * g0.w;
+    m1.x -= lr * g1.x; m1.y -= lr * g1.y; m1.z -= lr * g1.z; m1.w -= lr * g1.w;
+    m4[0] = m0;
+    m4[1] = m1;
+    if constexpr (sizeof(TW) == 2) {
+        const float f[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        __builtin_nontemporal_store(Vec16<bf16>::pack(f), reinterpret_cast<uint4*>(work) + i);
+    } else if (work != master) {
+        float4* w4 = reinterpret_cast<float4*>(work) + 2 * i;
+        __builtin_nontemporal_store(m0, w4);
+        __builtin_nontemporal_store(m1, w4 + 1);
+    }
+}
+
 template <class TW>
 __global__ void __launch_bounds__(256) sgd_kernel(SgdArgs a) {
-    const long n4 = a.n / 4;
+    const long n8 = a.n / 8;
     const long stride = (long)gridDim.x * blockDim.x;
-    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-        float4 m = reinterpret_cast<float4*>(a.master)[i];
-        float4 g = reinterpret_cast<const float4*>(a.grad)[i];
-        m.x -= a.lr * g.x; m.y -= a.lr * g.y; m.z -= a.lr * g.z; m.w -= a.lr * g.w;
-        reinterpret_cast<float4*>(a.master)[i] = m;
-        TW* w = reinterpret_cast<TW*>(a.work) + 4 * i;
-        w[0] = from_f<TW>(m.x); w[1] = from_f<TW>(m.y);
-        w[2] = from_f<TW>(m.z); w[3] = from_f<TW>(m.w);
+    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + stride < n8; i += 2 * stride) {
+        sgd8<TW>(a.master, a.grad, a.work, i, a.lr);
+        sgd8<TW>(a.master, a.grad, a.work, i + stride, a.lr);
     }
-    // tail (n not a multiple of 4)
-    for (long i = 4 * n4 + (long)blockIdx.x * blockDim.x + threadIdx.x; i < a.n; i += stride) {
-        float m = a.master[i] - a.lr * a.grad[i];
-        a.master[i] = m;
-        reinterpret_cast<TW*>(a.work)[i] = from_f<TW>(m);
+    if (i < n8) sgd8<TW>(a.master, a.grad, a.work, i, a.lr);
+    // tail (n not a multiple of 8)
+    for (long t = 8 * n8 + (long)blockIdx.x * blockDim.x + threadIdx.x; t < a.n; t += stride) {
+        float m = a.master[t] - a.lr * a.grad[t];
+        a.master[t] = m;
+        reinterpret_cast<TW*>(a.work)[t] = from_f<TW>(m);
     }
 }
 
@@ -243,9 +266,9 @@ hipError_t launch_colsum(const ColSumArgs& a, int dtype, hipStream_t s) {
 }
 hipError_t launch_sgd(const SgdArgs& a, int dtype, hipStream_t s) {
     if (a.n == 0) return hipSuccess;
-    long blocks = (a.n / 4 + 255) / 256;
+    long blocks = (a.n / 8 + 255) / 256;
     if (blocks < 1) blocks = 1;
-    if (blocks > 8192) blocks = 8192;
+    if (blocks > 16384) blocks = 16384;
     if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(sgd_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(sgd_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
     return hipGetLastError();

@@ -12,13 +12,17 @@
 //   * workgroup tile 256 x 256 x 64, 256 threads = 4 wavefronts in a 2 x 2
 //     grid, each wavefront a 128 x 128 block of 4 x 4 MFMA 32x32x16 tiles with
 //     fp32 accumulators;
-//   * both operands sit in LDS K-contiguous ([rows][64] bf16, 16-byte chunks
-//     XOR-swizzled by row & 7 so that the 8 lanes of a ds_read_b128 phase hit
-//     8 distinct bank groups), double buffered (2 x 64 KB);
-//   * K-contiguous operands are copied global -> registers -> LDS with
-//     16-byte loads; K-strided operands ([K][M] or [K][N] in memory) are
-//     loaded as 8 x 8 blocks and transposed in registers on the way, so the
-//     MFMA loop is the same for every layout;
+//   * both operands sit in LDS K-contiguous ([rows][64] bf16, 128-byte rows of
+//     eight 16-byte chunks, chunk XOR-swizzled by (row >> 1) & 7: the LDS has
+//     64 four-byte banks, so the 16 lanes served together by a ds_read_b128
+//     (16 consecutive rows, one chunk each) hit 16 distinct 16-byte bank
+//     groups), double buffered (2 x 64 KB);
+//   * every operand goes straight from global memory into LDS (buffer loads
+//     with an LDS destination, bounds checked by the buffer descriptor so
+//     ragged rows and k tails read as zero); K-contiguous operands are read
+//     back with ds_read_b128, K-strided operands ([K][M] or [K][N] in memory,
+//     kept in their natural layout) with the gfx950 transpose read
+//     ds_read_b64_tr_b16, so the MFMA loop is the same for every layout;
 //   * the MFMA is issued with the N operand first, so each lane's
 //     accumulators hold 4 consecutive output columns: epilogue stores are
 //     8-byte (bf16) or 16-byte (fp32) vectors;
@@ -35,8 +39,11 @@ namespace moe {
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int NTHR = 256;
 constexpr int TILE_ELEMS = 256 * BK;            // one operand tile in LDS (bf16)
+constexpr int GROUP_N = 8;                      // n-tiles per tile group (L2 reuse)
 
 enum { MODE_ROWS = 0, MODE_KSEG = 1, MODE_DENSE = 2 };
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 struct GemmParams {
     // A operand (M x K).  AT = false: element (m, k) at A[m * lda + k];
@@ -58,95 +65,125 @@ struct GemmParams {
     const bf16* H; long ldh; int ffn;
 };
 
-// ---- global -> register -> LDS movers ----------------------------------------
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// K-contiguous tile: 256 rows x 64 k.  Thread owns chunk c = tid & 7 of rows
-// r0 + 32 i.  Row pointers come from a callable (segment / pairing aware).
-struct KContig {
-    uint4 v[8];
-    template <class RowPtr>
-    __device__ __forceinline__ void load(RowPtr rowptr, int k0, int k_valid) {
-        const int c = threadIdx.x & 7, r0 = threadIdx.x >> 3;
-        const bool kin = c * 8 < k_valid;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const bf16* p = rowptr(r0 + 32 * i);
-            v[i] = (kin && p) ? *reinterpret_cast<const uint4*>(p + k0 + c * 8) : make_uint4(0, 0, 0, 0);
-        }
-    }
-    __device__ __forceinline__ void store(bf16* lds) const {
-        const int c = threadIdx.x & 7, r0 = threadIdx.x >> 3;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = r0 + 32 * i;
-            *reinterpret_cast<uint4*>(lds + r * BK + ((c ^ (r & 7)) << 3)) = v[i];
-        }
-    }
+// Buffer resource over [base, base + bytes): loads past the end return zeros,
+// which is how ragged rows, ragged k and column tails read as zero.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, long bytes) {
+    if (bytes < 0) bytes = 0;
+    if (bytes > 0x7fffffffL) bytes = 0x7fffffffL;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ void bload_lds(rsrc_t r, const bf16* lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds), 16, voff, soff, 0, 0);
+}
+
+// ---- K-contiguous operand: straight from global memory into the LDS stage ----------
+// One wave instruction fills 8 LDS rows (1 KB, lane l -> row l/8, physical chunk
+// l%8); the lane therefore loads the logical chunk that the swizzle places at
+// that physical chunk.  Wave w fills row blocks 8w .. 8w+7.
+struct DirectOp {
+    rsrc_t r0, r1;          // r1: second source of paired rows (W3)
+    uint32_t ld_bytes;      // row pitch
+    int paired;
 };
-
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-
-// K-strided tile: 64 k-rows x 256 columns in memory ([k][col], col contiguous).
-// Thread owns the 8 x 8 block (k-block kb = tid & 7, column block mb = tid >> 3)
-// and transposes it so LDS again holds [col][k].
-struct KStrided {
-    uint4 v[8];
-    __device__ __forceinline__ void load(const bf16* base, long ld, int k_valid, int col_valid) {
-        const int kb = threadIdx.x & 7, mb = threadIdx.x >> 3;
-        const bool cin = mb * 8 < col_valid;
+__device__ __forceinline__ void issue_direct(const DirectOp& op, const bf16* stage, int k0) {
+    const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
+    // row 8j + l/8 has swizzle key ((8j + l/8) >> 1) & 7 = (4 (j & 1) + (l >> 4)) & 7
+    const uint32_t row_off = (uint32_t)(lane >> 3) * op.ld_bytes;
+    const uint32_t vo_even = row_off + ((uint32_t)((lane & 7) ^ (lane >> 4)) << 4);
+    const uint32_t vo_odd = row_off + ((uint32_t)((lane & 7) ^ ((4 + (lane >> 4)) & 7)) << 4);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int k = kb * 8 + r;
-            v[r] = (cin && k < k_valid) ? *reinterpret_cast<const uint4*>(base + (long)k * ld + mb * 8)
-                                        : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+        const int j = wave * 8 + i;                       // row block: rows 8j .. 8j+7
+        const uint32_t vo = (i & 1) ? vo_odd : vo_even;   // wave * 8 is even: j & 1 == i & 1
+        int rowbase = 8 * j;
+        rsrc_t r = op.r0;
+        if (op.paired) {                                  // rows r: W1/W3 by (r >> 6) & 1
+            rowbase = ((j >> 4) << 6) + ((8 * j) & 63);
+            if ((j >> 3) & 1) r = op.r1;
         }
+        bload_lds(r, stage + j * 512, vo, (uint32_t)rowbase * op.ld_bytes + (uint32_t)k0 * 2u);
     }
-    __device__ __forceinline__ void store(bf16* lds) const {
-        const int kb = threadIdx.x & 7, mb = threadIdx.x >> 3;
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(v);   // w[4 r + c/2]
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            uint4 o;
-            const int q = c >> 1;
-            if ((c & 1) == 0) {
-                o.x = lo_pair(w[0 * 4 + q], w[1 * 4 + q]);
-                o.y = lo_pair(w[2 * 4 + q], w[3 * 4 + q]);
-                o.z = lo_pair(w[4 * 4 + q], w[5 * 4 + q]);
-                o.w = lo_pair(w[6 * 4 + q], w[7 * 4 + q]);
-            } else {
-                o.x = hi_pair(w[0 * 4 + q], w[1 * 4 + q]);
-                o.y = hi_pair(w[2 * 4 + q], w[3 * 4 + q]);
-                o.z = hi_pair(w[4 * 4 + q], w[5 * 4 + q]);
-                o.w = hi_pair(w[6 * 4 + q], w[7 * 4 + q]);
-            }
-            const int r = mb * 8 + c;
-            *reinterpret_cast<uint4*>(lds + r * BK + ((kb ^ c) << 3)) = o;
-        }
-    }
+}
+
+// ---- K-strided operand: natural [k][col] layout in LDS, transpose reads -------------
+// Memory holds [k][col] with col contiguous.  A stage keeps 64 k-rows of 256
+// columns (512-byte rows of 32 chunks), chunk XOR-swizzled by 2 * (row & 3).
+// One wave instruction fills 2 rows (lane l -> row l/32, physical chunk l%32).
+// Fragments come from ds_read_b64_tr_b16: inside each 16-lane group, lane l
+// receives element (l & 3) of the 8-byte reads of lanes 4j + (l >> 2), j = 0..3.
+// With lane 4j + m reading row k0 + j, columns c0 + 4m .. c0 + 4m + 3, lane l
+// gets the four k values k0 .. k0 + 3 of column c0 + l: two reads give the eight
+// consecutive k of one MFMA operand lane.  The swizzle keeps the four rows
+// touched by one 16-lane group on 16 distinct bank pairs.
+struct StridedOp {
+    rsrc_t r0, r1;          // r1: rows k >= kswitch (W3 after W1 along k)
+    uint32_t ld_bytes;
+    int kswitch;
 };
+__device__ __forceinline__ void issue_strided(const StridedOp& op, const bf16* stage, int k0) {
+    const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
+    const uint32_t row_off = (uint32_t)(lane >> 5) * op.ld_bytes;
+    const uint32_t vo_even = row_off + ((uint32_t)((lane & 31) ^ (2 * (lane >> 5))) << 4);
+    const uint32_t vo_odd = row_off + ((uint32_t)((lane & 31) ^ (4 + 2 * (lane >> 5))) << 4);
+    rsrc_t r = op.r0;
+    int kk = k0;
+    if (k0 >= op.kswitch) { r = op.r1; kk = k0 - op.kswitch; }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int j = wave * 8 + i;                       // rows 2j, 2j + 1 of the stage
+        const uint32_t vo = (i & 1) ? vo_odd : vo_even;   // row & 3 = 2 (j & 1) + lane/32
+        bload_lds(r, stage + j * 512, vo, (uint32_t)(kk + 2 * j) * op.ld_bytes);
+    }
+}
 
-// ---- MFMA on one LDS stage -------------------------------------------------------
-__device__ __forceinline__ void mma_stage(const bf16* As, const bf16* Bs, f32x16 (&acc)[4][4],
-                                          int wm, int wn) {
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+
+// 32 columns [colbase, colbase + 32) x 16 k of k-step ks, in MFMA operand layout.
+__device__ __forceinline__ bf16x8 read_strided(const bf16* T, int colbase, int ks) {
+    const int lane = threadIdx.x & 63;
+    const int L = lane & 15;
+    const int col = colbase + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+    const int pc = (col >> 3) ^ (2 * (L >> 2));           // k & 3 == L >> 2
+    const int k = 16 * ks + 8 * (lane >> 5) + (L >> 2);
+    const bf16* p0 = T + k * 256 + pc * 8 + (col & 7);
+    const bf16* p1 = p0 + 4 * 256;                         // k + 4: same swizzle
+    v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(p0));
+    v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(p1));
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    v8s v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---- MFMA fragments ----------------------------------------------------------------------
+struct Frags { bf16x8 a[4], b[4]; };
+__device__ __forceinline__ bf16x8 read_contig(const bf16* T, int rowbase, int ks) {
     const int lane = threadIdx.x & 63;
     const int rr = lane & 31, hk = lane >> 5;
+    const int ch = ((2 * ks + hk) ^ ((rr >> 1) & 7)) << 3;
+    return *reinterpret_cast<const bf16x8*>(T + (rowbase + rr) * BK + ch);
+}
+template <bool AT, bool BT>
+__device__ __forceinline__ void read_frags(const bf16* As, const bf16* Bs, int ks, int wm, int wn, Frags& f) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-        const int ch = ((2 * ks + hk) ^ (rr & 7)) << 3;
-        bf16x8 af[4], bfr[4];
+    for (int i = 0; i < 4; ++i)
+        f.a[i] = AT ? read_strided(As, wm * 128 + i * 32, ks) : read_contig(As, wm * 128 + i * 32, ks);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            af[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + i * 32 + rr) * BK + ch);
+    for (int j = 0; j < 4; ++j)
+        f.b[j] = BT ? read_strided(Bs, wn * 128 + j * 32, ks) : read_contig(Bs, wn * 128 + j * 32, ks);
+}
+__device__ __forceinline__ void mma(const Frags& f, f32x16 (&acc)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 128 + j * 32 + rr) * BK + ch);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-    }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
 // ---- epilogue helpers -----------------------------------------------------------------
@@ -165,40 +202,58 @@ __device__ __forceinline__ void load4(const bf16* p, float* v) {
     v[0] = (float)b[0]; v[1] = (float)b[1]; v[2] = (float)b[2]; v[3] = (float)b[3];
 }
 
+// Grouped tile order inside an mt x nt tile grid: groups of GROUP_N n-tiles, all
+// m-tiles of a group before the next group, so concurrently running tiles share
+// A row blocks and B column blocks in L2.
+__device__ __forceinline__ void grouped(int q, int mt, int nt, int& tm, int& tn) {
+    const int gn = min(GROUP_N, nt);
+    const int ng = q / (mt * gn);
+    const int rem = q - ng * mt * gn;
+    const int gsz = min(gn, nt - ng * gn);
+    tm = rem / gsz;
+    tn = ng * gn + (rem - tm * gsz);
+}
+
 // ---- the kernel ------------------------------------------------------------------------
 template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32>
-__global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(16))) bf16 lds[2][2][TILE_ELEMS];   // [stage][A/B]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ void __launch_bounds__(NTHR, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_bf16_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) bf16 lds[2][2][TILE_ELEMS];   // [stage][A/B]
+    const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    // ---- which tile -----------------------------------------------------------
+    // ---- which tile: workgroups are dealt round-robin to the 8 XCDs, so give each
+    // XCD a contiguous run of logical tiles (tiles that share operands meet in its L2)
+    const int nwg = gridDim.x;
+    int L = blockIdx.x;
+    if ((nwg & 7) == 0) L = (L & 7) * (nwg >> 3) + (L >> 3);
     const int NT = p.paired ? (p.ffn + 127) / 128 : (p.N + BN - 1) / BN;
     int e = 0, m0 = 0, n_t = 0;
     long row_base = 0;        // absolute row of the segment start (ROWS) / K start (KSEG)
     int rows_valid = 0;       // valid rows of this tile in M
     int K = p.K;
-    const int L = blockIdx.x;
     if (MODE == MODE_ROWS) {
-        const int tm = L / NT;
-        n_t = L - tm * NT;
-        if (tm >= p.tile_prefix[p.E]) return;
-        int lo = 0, hi = p.E;   // largest e with tile_prefix[e] <= tm
+        const int tmg = L / NT;
+        if (tmg >= p.tile_prefix[p.E]) return;
+        int lo = 0, hi = p.E;   // largest e with tile_prefix[e] <= tmg
         while (hi - lo > 1) {
             int mid = (lo + hi) >> 1;
-            if (p.tile_prefix[mid] <= tm) lo = mid; else hi = mid;
+            if (p.tile_prefix[mid] <= tmg) lo = mid; else hi = mid;
         }
         e = lo;
-        m0 = (tm - p.tile_prefix[e]) * BM;
+        const int mt = p.tile_prefix[e + 1] - p.tile_prefix[e];
+        int tm;
+        grouped(L - p.tile_prefix[e] * NT, mt, NT, tm, n_t);
+        m0 = tm * BM;
         row_base = p.offsets[e];
         const int seg = p.offsets[e + 1] - p.offsets[e];
         rows_valid = min(BM, seg - m0);
     } else if (MODE == MODE_KSEG) {
         const int MT = (p.M + BM - 1) / BM;
         e = L / (MT * NT);
-        const int rem = L - e * MT * NT;
-        const int tm = rem / NT;
-        n_t = rem - tm * NT;
+        if (e >= p.E) return;
+        int tm;
+        grouped(L - e * MT * NT, MT, NT, tm, n_t);
         m0 = tm * BM;
         rows_valid = min(BM, p.M - m0);
         if (p.offsets) {
@@ -206,15 +261,64 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(GemmParams p) {
             K = p.offsets[e + 1] - p.offsets[e];
         }
     } else {
-        const int tm = L / NT;
-        n_t = L - tm * NT;
+        const int MT = (p.M + BM - 1) / BM;
+        if (L >= MT * NT) return;
+        int tm;
+        grouped(L, MT, NT, tm, n_t);
         m0 = tm * BM;
         rows_valid = min(BM, p.M - m0);
     }
+    e = uni(e); m0 = uni(m0); n_t = uni(n_t); rows_valid = uni(rows_valid); K = uni(K);
+    row_base = (long)uni((int)row_base);
     const int n0 = n_t * BN;
+    const int hid0 = n_t * 128;   // paired: first hidden unit of the tile
     const bf16* Be = p.B + (long)e * p.bes;
     const bf16* B2e = p.B2 ? p.B2 + (long)e * p.bes : nullptr;
-    const int hid0 = n_t * 128;   // paired: first hidden unit of the tile
+
+    // ---- operand sources -----------------------------------------------------------------
+    DirectOp da = {}, db = {};
+    StridedOp sa = {}, sb = {};
+    if (AT) {   // A[k][m]: k rows of the segment, columns m0 ..
+        const bf16* base = p.A + row_base * p.lda + m0;
+        sa.r0 = make_rsrc(base, ((long)K * p.lda - m0) * 2);
+        sa.r1 = sa.r0;
+        sa.ld_bytes = (uint32_t)(p.lda * 2);
+        sa.kswitch = 0x7fffffff;
+    } else {    // A[m][k]: rows m0 .. m0 + rows_valid of the segment
+        const bf16* base = p.A + (row_base + m0) * p.lda;
+        da.r0 = make_rsrc(base, (long)rows_valid * p.lda * 2);
+        da.r1 = da.r0;
+        da.ld_bytes = (uint32_t)(p.lda * 2);
+        da.paired = 0;
+    }
+    if (BT) {   // B[k][n]
+        if (MODE == MODE_KSEG) {
+            const bf16* base = p.B + row_base * p.ldb + n0;
+            sb.r0 = make_rsrc(base, ((long)K * p.ldb - n0) * 2);
+            sb.r1 = sb.r0;
+            sb.kswitch = 0x7fffffff;
+        } else if (p.b2_kstart >= 0) {
+            sb.r0 = make_rsrc(Be + n0, ((long)p.b2_kstart * p.ldb - n0) * 2);
+            sb.r1 = make_rsrc(B2e + n0, ((long)(K - p.b2_kstart) * p.ldb - n0) * 2);
+            sb.kswitch = p.b2_kstart;
+        } else {
+            sb.r0 = make_rsrc(Be + n0, ((long)K * p.ldb - n0) * 2);
+            sb.r1 = sb.r0;
+            sb.kswitch = 0x7fffffff;
+        }
+        sb.ld_bytes = (uint32_t)(p.ldb * 2);
+    } else {    // B[n][k]
+        if (p.paired) {
+            db.r0 = make_rsrc(Be + (long)hid0 * p.ldb, (long)(p.ffn - hid0) * p.ldb * 2);
+            db.r1 = make_rsrc(B2e + (long)hid0 * p.ldb, (long)(p.ffn - hid0) * p.ldb * 2);
+            db.paired = 1;
+        } else {
+            db.r0 = make_rsrc(Be + (long)n0 * p.ldb, (long)min(BN, p.N - n0) * p.ldb * 2);
+            db.r1 = db.r0;
+            db.paired = 0;
+        }
+        db.ld_bytes = (uint32_t)(p.ldb * 2);
+    }
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -224,58 +328,43 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // operand row pointers (K-contiguous cases)
-    auto a_row = [&](int r) -> const bf16* {
-        const int rr = min(r, rows_valid - 1);
-        return p.A + (row_base + m0 + rr) * p.lda;
-    };
-    auto b_row = [&](int r) -> const bf16* {
-        if (p.paired) {
-            const int hid = hid0 + (r >> 7) * 64 + (r & 63);
-            const int h = min(hid, p.ffn - 1);
-            return (((r >> 6) & 1) ? B2e : Be) + (long)h * p.ldb;
-        }
-        const int n = min(n0 + r, p.N - 1);
-        return Be + (long)n * p.ldb;
-    };
-
-    KContig ga, gb;
-    KStrided ta, tb;
     const int nk = (K + BK - 1) / BK;
-
-    auto load_tile = [&](int kt) {
+    // the loads of tile kt go straight into LDS stage st
+    auto issue = [&](int kt, int st) {
         const int k0 = kt * BK;
-        const int kv = K - k0;
-        if (AT) {
-            // A[k][m]: rows k = row_base + k0 .., columns m0 ..
-            ta.load(p.A + (row_base + k0) * p.lda + m0, p.lda, kv, rows_valid);
-        } else {
-            ga.load(a_row, k0, kv);
-        }
-        if (BT) {
-            const bf16* bb = Be;
-            int kk = k0;
-            if (p.b2_kstart >= 0 && k0 >= p.b2_kstart) { bb = B2e; kk = k0 - p.b2_kstart; }
-            if (MODE == MODE_KSEG) bb = p.B + row_base * p.ldb;     // B[k][n] rows of the segment
-            tb.load(bb + (long)kk * p.ldb + n0, p.ldb, kv, p.N - n0);
-        } else {
-            gb.load(b_row, k0, kv);
-        }
-    };
-    auto store_tile = [&](int stage) {
-        if (AT) ta.store(lds[stage][0]); else ga.store(lds[stage][0]);
-        if (BT) tb.store(lds[stage][1]); else gb.store(lds[stage][1]);
+        if (AT) issue_strided(sa, lds[st][0], k0); else issue_direct(da, lds[st][0], k0);
+        if (BT) issue_strided(sb, lds[st][1], k0); else issue_direct(db, lds[st][1], k0);
     };
 
     if (nk > 0) {
-        load_tile(0);
-        store_tile(0);
+        issue(0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
-            if (kt + 1 < nk) load_tile(kt + 1);
-            mma_stage(lds[cur][0], lds[cur][1], acc, wm, wn);
-            if (kt + 1 < nk) store_tile(cur ^ 1);
+            const bool more = kt + 1 < nk;
+            if (more) issue(kt + 1, cur ^ 1);
+            const bf16* As = lds[cur][0];
+            const bf16* Bs = lds[cur][1];
+            // fragments of k-step s+1 are read while the MFMAs of k-step s run; the
+            // scheduling fences keep the compiler from serialising reads and MFMAs
+            Frags f0, f1;
+            read_frags<AT, BT>(As, Bs, 0, wm, wn, f0);
+            read_frags<AT, BT>(As, Bs, 1, wm, wn, f1);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(f0, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags<AT, BT>(As, Bs, 2, wm, wn, f0);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(f1, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags<AT, BT>(As, Bs, 3, wm, wn, f1);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(f0, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(f1, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            if (more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         }
     }
@@ -369,6 +458,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_bf16_kernel(GemmParams p) {
 template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32>
 static hipError_t run(const GemmParams& p, int grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
+    grid = (grid + 7) & ~7;   // whole XCD rounds; surplus workgroups exit at once
     hipLaunchKernelGGL((gemm_bf16_kernel<MODE, AT, BT, EPI, OUT_F32>), dim3(grid), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
