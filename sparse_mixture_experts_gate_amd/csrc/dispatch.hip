@@ -184,23 +184,26 @@ __global__ void __launch_bounds__(256) colsum_kernel(ColSumArgs a) {
 // accesses only (two float4 of master, two of gradient, one 16-byte vector of
 // bf16 working copy), two steps in flight; gradients are read once and the
 // outputs are not re-read, so those accesses carry the nontemporal hint.
-__device__ __forceinline__ float4 ld_nt(const float4* p) { return __builtin_nontemporal_load(p); }
+typedef float nf4 __attribute__((ext_vector_type(4)));
+typedef unsigned int nu4 __attribute__((ext_vector_type(4)));
 
 template <class TW>
 __device__ __forceinline__ void sgd8(float* master, const float* grad, void* work, long i, float lr) {
-    float4* m4 = reinterpret_cast<float4*>(master) + 2 * i;
-    const float4* g4 = reinterpret_cast<const float4*>(grad) + 2 * i;
-    float4 m0 = m4[0], m1 = m4[1];
-    const float4 g0 = ld_nt(g4), g1 = ld_nt(g4 + 1);
-    m0.x -= lr * g0.x; m0.y -= lr * g0.y; m0.z -= lr * g0.z; m0.w -= lr * g0.w;
-    m1.x -= lr * g1.x; m1.y -= lr * g1.y; m1.z -= lr * g1.z; m1.w -= lr * g1.w;
+    nf4* m4 = reinterpret_cast<nf4*>(master) + 2 * i;
+    const nf4* g4 = reinterpret_cast<const nf4*>(grad) + 2 * i;
+    nf4 m0 = m4[0], m1 = m4[1];
+    const nf4 g0 = __builtin_nontemporal_load(g4), g1 = __builtin_nontemporal_load(g4 + 1);
+    m0 -= lr * g0;
+    m1 -= lr * g1;
     m4[0] = m0;
     m4[1] = m1;
     if constexpr (sizeof(TW) == 2) {
         const float f[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-        __builtin_nontemporal_store(Vec16<bf16>::pack(f), reinterpret_cast<uint4*>(work) + i);
+        const uint4 u = Vec16<bf16>::pack(f);
+        const nu4 v = {u.x, u.y, u.z, u.w};
+        __builtin_nontemporal_store(v, reinterpret_cast<nu4*>(work) + i);
     } else if (work != master) {
-        float4* w4 = reinterpret_cast<float4*>(work) + 2 * i;
+        nf4* w4 = reinterpret_cast<nf4*>(work) + 2 * i;
         __builtin_nontemporal_store(m0, w4);
         __builtin_nontemporal_store(m1, w4 + 1);
     }
