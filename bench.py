@@ -66,6 +66,32 @@ def stage_work(w):
 
 GEMM_STAGES = ("up_fwd", "down_fwd", "down_dgrad", "down_wgrad", "up_dgrad", "up_wgrad")
 
+# source file of the kernels behind each stage (the HBM byte counts measured with
+# rocprofv3 hold only while that file is unchanged)
+STAGE_SOURCE = {s: "gemm_mfma.hip" for s in GEMM_STAGES + ("router_logits", "router_dwg", "router_dx")}
+STAGE_SOURCE.update({s: "dispatch.hip" for s in ("gather", "combine_loss", "combine_bwd", "scatter",
+                                                  "bias_grads", "sgd")})
+STAGE_SOURCE.update({s: "routing.hip" for s in ("route", "router_bwd")})
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_train_step_t32768_d7168_e256.json")
+
+
+def measured_traffic(stage: str, workload: str):
+    """HBM bytes per step of a stage from the committed counter summary, or None when
+    there is none or the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or stage not in rec.get("stages", {}):
+        return None
+    src = os.path.join(ROOT, "sparse_mixture_experts_gate_amd", "csrc", STAGE_SOURCE[stage])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    ent = rec["stages"][stage]
+    if ent.get("source_sha256") != sha:
+        return None
+    return ent["hbm_bytes"]
+
 
 def cpu_baseline(w, inp, budget_s: float):
     """The oracle, as it stands, on a bounded sample of the workload (host cores).
@@ -131,6 +157,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="grouped_sigmoid_t32768_d7168_e256")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the steps (outside "
+                         "the timed region), a known-size reference for hardware byte counters")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print("bench.py runs on one GPU only: this layer is built and measured on a single "
@@ -159,6 +188,12 @@ def main(argv=None) -> int:
             params[n] = inp[n]
             params[n + "_w"] = inp[n + "_w"]
     X, Yt = inp["X"], inp["Yt"]
+    if a.copy_calibration_mib:
+        src = torch.ones(a.copy_calibration_mib * 2**18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
     print(f"[bench] {w.name}: inputs ready, workspace {ws.numel() / 2**30:.1f} GiB", file=sys.stderr,
           flush=True)
@@ -200,15 +235,16 @@ def main(argv=None) -> int:
         stages[s] = ent
     dom = max(L.STAGES, key=lambda s: avg[s])
     kind, n = work[dom]
+    traffic = measured_traffic(dom, w.name)
     if kind == "flop":
         ach = n / (avg[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": dom, "work_per_launch": n}
     else:
         ach = n / (avg[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom,
                 "work_per_launch": n}
     gemm_ms = sum(avg[s] for s in GEMM_STAGES)
     gemm_flop = sum(work[s][1] for s in GEMM_STAGES)

@@ -1,0 +1,179 @@
+"""Per-stage HBM traffic of one training step from two rocprofv3 counter runs.
+
+    rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o fetch --output-format csv -- \\
+        python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration-mib 1024
+    rocprofv3 --pmc WRITE_SIZE -d OUT/write -o write --output-format csv -- \\
+        python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration-mib 1024
+    python -m sparse_mixture_experts_gate_amd.profile_summary OUT/fetch/fetch_counter_collection.csv \\
+        OUT/write/write_counter_collection.csv --calibration-mib 1024 --json J --markdown M
+
+FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch.  Each is scaled by
+the factor that makes the known-size device copy (--copy-calibration-mib)
+read and write exactly its size.  The library's kernels of the one timed
+training step are mapped to the stages of the step in launch order, and each
+stage records the SHA-256 of its kernel source so that a later change to the
+kernel invalidates the figure.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+STAGE_SOURCE = {
+    "router_logits": "gemm_mfma.hip", "route": "routing.hip", "gather": "dispatch.hip",
+    "up_fwd": "gemm_mfma.hip", "down_fwd": "gemm_mfma.hip", "combine_loss": "dispatch.hip",
+    "combine_bwd": "dispatch.hip", "down_dgrad": "gemm_mfma.hip", "down_wgrad": "gemm_mfma.hip",
+    "up_dgrad": "gemm_mfma.hip", "up_wgrad": "gemm_mfma.hip", "bias_grads": "dispatch.hip",
+    "router_bwd": "routing.hip", "router_dwg": "gemm_mfma.hip", "router_dx": "gemm_mfma.hip",
+    "scatter": "dispatch.hip", "sgd": "dispatch.hip",
+}
+
+
+def _rows(path, counter):
+    out = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        out.append({"name": r["Kernel_Name"], "kib": float(r["Counter_Value"]),
+                    "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                    "dispatch": int(r["Dispatch_Id"])})
+    out.sort(key=lambda x: x["dispatch"])
+    return out
+
+
+def _calibration(rows, mib):
+    """Scale factor: known bytes / counter bytes of the largest plain copy."""
+    copies = [r for r in rows if "copyBuffer" in r["name"] or ("at::native" in r["name"] and "copy" in r["name"])]
+    if not copies:
+        raise SystemExit("no copy kernel found for calibration")
+    # the calibration copy moves mib MiB; pick the copy whose counter is largest
+    big = max(copies, key=lambda r: r["kib"])
+    return (mib * 1024.0) / big["kib"], big
+
+
+def _stage_of(name, state):
+    """Stage of a library kernel, given the kernels of the step seen so far."""
+    if "gemm_bf16_kernel<2, false, false" in name or "s_router_logits" in name:
+        return "router_logits"
+    if any(k in name for k in ("route_topk", "expert_scan", "slot_assign")):
+        return "route"
+    if "finalize_kernel" in name:
+        return "route" if state["stage"] in ("route",) else "combine_loss"
+    if "gather_kernel" in name:
+        return "gather"
+    if "gemm_bf16_kernel<0, false, false, 0" in name:
+        return "down_fwd"
+    if "gemm_bf16_kernel<0, false, false" in name:
+        return "up_fwd"
+    if "combine_kernel" in name:
+        return "combine_loss"
+    if "combine_bwd_kernel" in name:
+        return "combine_bwd"
+    if "gemm_bf16_kernel<0, false, true, 0" in name:
+        return "up_dgrad"
+    if "gemm_bf16_kernel<0, false, true" in name:
+        return "down_dgrad"
+    if "gemm_bf16_kernel<1, true, true" in name:
+        state["wgrad"] += 1
+        return {1: "down_wgrad", 2: "up_wgrad"}.get(state["wgrad"], "router_dwg")
+    if "colsum_kernel" in name:
+        return "bias_grads"
+    if "router_bwd_kernel" in name:
+        return "router_bwd"
+    if "gemm_bf16_kernel<2, false, true" in name:
+        return "router_dx"
+    if "scatter_kernel" in name:
+        return "scatter"
+    if "sgd_kernel" in name:
+        return "sgd"
+    return None
+
+
+def summarize(fetch_csv, write_csv, mib):
+    f_rows, w_rows = _rows(fetch_csv, "FETCH_SIZE"), _rows(write_csv, "WRITE_SIZE")
+    f_scale, f_copy = _calibration(f_rows, mib)
+    w_scale, w_copy = _calibration(w_rows, mib)
+
+    def per_stage(rows, scale):
+        state = {"stage": None, "wgrad": 0}
+        acc = {}
+        started = False
+        for r in rows:
+            st = _stage_of(r["name"], state)
+            if st == "router_logits":
+                if started:
+                    break          # the next step: keep the first one only
+                started = True
+            if not started or st is None:
+                continue
+            state["stage"] = st
+            e = acc.setdefault(st, {"bytes": 0.0, "ns": 0, "launches": 0})
+            e["bytes"] += r["kib"] * 1024.0 * scale
+            e["ns"] += r["ns"]
+            e["launches"] += 1
+        return acc
+
+    fs, ws = per_stage(f_rows, f_scale), per_stage(w_rows, w_scale)
+    stages = {}
+    for st in fs:
+        src = os.path.join(PKG, "csrc", STAGE_SOURCE[st])
+        stages[st] = {
+            "fetch_bytes": round(fs[st]["bytes"]), "write_bytes": round(ws.get(st, {}).get("bytes", 0.0)),
+            "hbm_bytes": round(fs[st]["bytes"] + ws.get(st, {}).get("bytes", 0.0)),
+            "launches": fs[st]["launches"], "ms_under_counters": round(fs[st]["ns"] / 1e6, 3),
+            "source": STAGE_SOURCE[st],
+            "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        }
+    return {"calibration": {"copy_mib": mib, "fetch_scale": round(f_scale, 4),
+                            "write_scale": round(w_scale, 4),
+                            "copy_fetch_kib": f_copy["kib"], "copy_write_kib": w_copy["kib"]},
+            "stages": stages}
+
+
+def markdown(rec, title, command):
+    lines = [f"# {title}", "", "Commands (repository root, one MI355X):", "", "```", command, "```", "",
+             f"Calibration: a {rec['calibration']['copy_mib']} MiB device copy reads "
+             f"{rec['calibration']['copy_fetch_kib'] / 1024:.1f} MiB by FETCH_SIZE and writes "
+             f"{rec['calibration']['copy_write_kib'] / 1024:.1f} MiB by WRITE_SIZE, so FETCH_SIZE is "
+             f"scaled by {rec['calibration']['fetch_scale']} and WRITE_SIZE by "
+             f"{rec['calibration']['write_scale']}.", "",
+             "| stage | launches | HBM read (GB) | HBM write (GB) | total (GB) | ms (under counters) |",
+             "|---|---|---|---|---|---|"]
+    for st, e in rec["stages"].items():
+        lines.append(f"| {st} | {e['launches']} | {e['fetch_bytes'] / 1e9:.3f} | {e['write_bytes'] / 1e9:.3f} | "
+                     f"{e['hbm_bytes'] / 1e9:.3f} | {e['ms_under_counters']} |")
+    return "\n".join(lines) + "\n"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("fetch_csv")
+    ap.add_argument("write_csv")
+    ap.add_argument("--calibration-mib", type=int, required=True)
+    ap.add_argument("--workload", default="grouped_sigmoid_t32768_d7168_e256")
+    ap.add_argument("--json")
+    ap.add_argument("--markdown")
+    ap.add_argument("--command", default="")
+    a = ap.parse_args(argv)
+    rec = summarize(a.fetch_csv, a.write_csv, a.calibration_mib)
+    rec["workload"] = a.workload
+    rec["command"] = a.command
+    if a.json:
+        json.dump(rec, open(a.json, "w"), indent=1)
+    if a.markdown:
+        open(a.markdown, "w").write(markdown(rec, f"HBM traffic per stage, training step, {a.workload}",
+                                             a.command))
+    print(json.dumps(rec["calibration"]))
+    for st, e in rec["stages"].items():
+        print(f"{st:14s} {e['hbm_bytes'] / 1e9:8.3f} GB")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
