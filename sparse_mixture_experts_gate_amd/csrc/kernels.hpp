@@ -122,20 +122,31 @@ struct ExpertGemmArgs {
     float* dW1; float* dW3; float* dW2;
     int expert;                      // MOE_EXPERT_*
 };
-hipError_t launch_up_fwd(const ExpertGemmArgs& a, int dtype, hipStream_t s);
-hipError_t launch_down_fwd(const ExpertGemmArgs& a, int dtype, hipStream_t s);
-hipError_t launch_down_dgrad(const ExpertGemmArgs& a, int dtype, hipStream_t s);
-hipError_t launch_up_dgrad(const ExpertGemmArgs& a, int dtype, hipStream_t s);
-hipError_t launch_down_wgrad(const ExpertGemmArgs& a, int dtype, hipStream_t s);
-hipError_t launch_up_wgrad(const ExpertGemmArgs& a, int dtype, hipStream_t s);
+// float32 layer (gemm_simple.hip): one thread per output element, fp32 accumulate.
+hipError_t simple_up_fwd(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t simple_down_fwd(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t simple_down_dgrad(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t simple_up_dgrad(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t simple_down_wgrad(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t simple_up_wgrad(const ExpertGemmArgs& a, hipStream_t s);
+// bfloat16 layer (gemm_mfma.hip): grouped MFMA tiles scheduled on the device.
+hipError_t mfma_up_fwd(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t mfma_down_fwd(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t mfma_down_dgrad(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t mfma_up_dgrad(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t mfma_down_wgrad(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t mfma_up_wgrad(const ExpertGemmArgs& a, hipStream_t s);
 
 struct RouterGemmArgs {
     int T, d, E;
     const void* X; const void* Wg; const void* dl;
     float* logits; float* dXr; float* dWg;
 };
-hipError_t launch_router_logits(const RouterGemmArgs& a, int dtype, hipStream_t s);
-hipError_t launch_router_dx(const RouterGemmArgs& a, int dtype, hipStream_t s);
-hipError_t launch_router_dwg(const RouterGemmArgs& a, int dtype, hipStream_t s);
+hipError_t simple_router_logits(const RouterGemmArgs& a, hipStream_t s);
+hipError_t simple_router_dx(const RouterGemmArgs& a, hipStream_t s);
+hipError_t simple_router_dwg(const RouterGemmArgs& a, hipStream_t s);
+hipError_t mfma_router_logits(const RouterGemmArgs& a, hipStream_t s);
+hipError_t mfma_router_dx(const RouterGemmArgs& a, hipStream_t s);
+hipError_t mfma_router_dwg(const RouterGemmArgs& a, hipStream_t s);
 
 }  // namespace moe

@@ -18,29 +18,6 @@
 #include "../../include/moe.h"
 #include "kernels.hpp"
 
-namespace moe {
-// float32 layer contractions (gemm_simple.hip) and bfloat16 MFMA contractions
-// (gemm_mfma.hip)
-hipError_t simple_up_fwd(const ExpertGemmArgs&, hipStream_t);
-hipError_t simple_down_fwd(const ExpertGemmArgs&, hipStream_t);
-hipError_t simple_down_dgrad(const ExpertGemmArgs&, hipStream_t);
-hipError_t simple_up_dgrad(const ExpertGemmArgs&, hipStream_t);
-hipError_t simple_down_wgrad(const ExpertGemmArgs&, hipStream_t);
-hipError_t simple_up_wgrad(const ExpertGemmArgs&, hipStream_t);
-hipError_t simple_router_logits(const RouterGemmArgs&, hipStream_t);
-hipError_t simple_router_dx(const RouterGemmArgs&, hipStream_t);
-hipError_t simple_router_dwg(const RouterGemmArgs&, hipStream_t);
-hipError_t mfma_up_fwd(const ExpertGemmArgs&, hipStream_t);
-hipError_t mfma_down_fwd(const ExpertGemmArgs&, hipStream_t);
-hipError_t mfma_down_dgrad(const ExpertGemmArgs&, hipStream_t);
-hipError_t mfma_up_dgrad(const ExpertGemmArgs&, hipStream_t);
-hipError_t mfma_down_wgrad(const ExpertGemmArgs&, hipStream_t);
-hipError_t mfma_up_wgrad(const ExpertGemmArgs&, hipStream_t);
-hipError_t mfma_router_logits(const RouterGemmArgs&, hipStream_t);
-hipError_t mfma_router_dx(const RouterGemmArgs&, hipStream_t);
-hipError_t mfma_router_dwg(const RouterGemmArgs&, hipStream_t);
-}  // namespace moe
-
 using namespace moe;
 
 namespace {
