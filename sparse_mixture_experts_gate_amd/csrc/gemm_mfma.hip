@@ -9,20 +9,25 @@
 // (SwiGLU W2(silu(W1 x) * W3 x)).
 //
 // One kernel template covers every contraction:
-//   * workgroup tile 256 x 256 x 64, 256 threads = 4 wavefronts in a 2 x 2
-//     grid, each wavefront a 128 x 128 block of 4 x 4 MFMA 32x32x16 tiles with
-//     fp32 accumulators;
-//   * both operands sit in LDS K-contiguous ([rows][64] bf16, 128-byte rows of
-//     eight 16-byte chunks, chunk XOR-swizzled by (row >> 1) & 7: the LDS has
-//     64 four-byte banks, so the 16 lanes served together by a ds_read_b128
-//     (16 consecutive rows, one chunk each) hit 16 distinct 16-byte bank
-//     groups), double buffered (2 x 64 KB);
+//   * workgroup tile 256 x 256, k-tiles of 32, 256 threads = 4 wavefronts in a
+//     2 x 2 grid, each wavefront a 128 x 128 block of 4 x 4 MFMA 32x32x16 tiles
+//     with fp32 accumulators;
 //   * every operand goes straight from global memory into LDS (buffer loads
 //     with an LDS destination, bounds checked by the buffer descriptor so
-//     ragged rows and k tails read as zero); K-contiguous operands are read
-//     back with ds_read_b128, K-strided operands ([K][M] or [K][N] in memory,
-//     kept in their natural layout) with the gfx950 transpose read
-//     ds_read_b64_tr_b16, so the MFMA loop is the same for every layout;
+//     ragged rows and k tails read as zero) through a ring of 4 LDS stages,
+//     k-tiles loaded 2 ahead of the one in use; K-contiguous operands are kept
+//     as [rows][32] (64-byte rows of four 16-byte chunks, chunk XOR-swizzled by
+//     (row >> 2) & 3: the LDS has 64 four-byte banks and the 16 lanes served
+//     together by a ds_read_b128 read 16 consecutive rows, which then hit 16
+//     distinct 16-byte bank groups) and read with ds_read_b128; K-strided
+//     operands ([K][M] or [K][N] in memory) keep their natural [k][256] layout
+//     and are read with the gfx950 transpose read ds_read_b64_tr_b16, so the
+//     MFMA loop is the same for every layout;
+//   * each k-step is 16 issue slots of one MFMA followed by either one
+//     fragment read for the next k-step or one load of a later k-tile, so
+//     neither the LDS nor the load queue ever holds up a run of MFMAs; one
+//     barrier per k-tile publishes the next stage, with the first fragments of
+//     that stage read under the last MFMAs of the current one;
 //   * the MFMA is issued with the N operand first, so each lane's
 //     accumulators hold 4 consecutive output columns: epilogue stores are
 //     8-byte (bf16) or 16-byte (fp32) vectors;
@@ -30,163 +35,157 @@
 //     walks the m-tiles of every expert's row segment (prefix of per-expert
 //     tile counts, binary search per workgroup); KSEG mode gives each expert
 //     its own output and runs K over its row segment (empty segment -> the
-//     output is written as zeros); DENSE is one plain GEMM.
+//     output is written as zeros); DENSE is one plain GEMM.  Workgroups are
+//     dealt round-robin to the 8 XCDs; in KSEG mode each XCD is given a
+//     contiguous, equal share of the tiles so that tiles of one expert meet
+//     in its L2.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int NS = 4;                           // LDS stages (ring)
+constexpr int DIST = 2;                         // k-tiles loaded ahead of the one in use
 constexpr int NTHR = 256;
+constexpr int KSTEPS = BK / 16;                 // MFMA k-steps per k-tile
 constexpr int TILE_ELEMS = 256 * BK;            // one operand tile in LDS (bf16)
+constexpr int CHUNKS = BK / 8;                  // 16-byte chunks per K-contiguous row
+constexpr int ROWS_PER_WIN = 256 / (BK * 2);    // rows per 256-byte bank window
+constexpr int DIRECT_ROWS = 1024 / (BK * 2);    // K-contiguous rows filled by one wave load
+constexpr int DIRECT_IPW = 256 / DIRECT_ROWS / 4;   // loads per wave per operand tile
+constexpr int STRIDED_IPW = BK / 2 / 4;             // K-strided: two k-rows per load
 constexpr int GROUP_N = 8;                      // n-tiles per tile group (L2 reuse)
+static_assert(DIST >= 1 && DIST <= NS - 1, "prefetch distance");
+static_assert(NS * 2 * TILE_ELEMS * 2 <= 160 * 1024, "LDS");
 
 enum { MODE_ROWS = 0, MODE_KSEG = 1, MODE_DENSE = 2 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 struct GemmParams {
-    // A operand (M x K).  AT = false: element (m, k) at A[m * lda + k];
-    // AT = true: at A[k * lda + m].  m, k are absolute (segment offsets added).
     const bf16* A; long lda;
-    // B operand (N x K).  BT = false: element (n, k) at B[e * bes + n * ldb + k];
-    // BT = true: at B[e * bes + k * ldb + n].
     const bf16* B; const bf16* B2; long ldb; long bes;
-    int b2_kstart;     // BT: rows k >= b2_kstart come from B2 at k - b2_kstart
-    int paired;        // !BT: SwiGLU pairing, 128 hidden units per tile from B and B2
+    int b2_kstart;
+    int paired;
     int M, N, K, E;
-    const int32_t* offsets;       // [E+1]
-    const int32_t* tile_prefix;   // [E+1] m-tile prefix for BM-row tiles
-    int mtiles_ub;                // upper bound of m-tiles (ROWS)
-    // outputs
-    void* C; void* C2; void* C3; long ldc; long ces;  // ces: per-expert stride (KSEG)
-    int c2_mstart;     // KSEG: output rows m >= c2_mstart go to C2 at m - c2_mstart
+    const int32_t* offsets;
+    const int32_t* tile_prefix;
+    int mtiles_ub;
+    int xcd_balance;              // deal each XCD a contiguous, equal share of the tiles
+    void* C; void* C2; void* C3; long ldc; long ces;
+    int c2_mstart;
     const bf16* bias; long bias_es;
     const bf16* H; long ldh; int ffn;
 };
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// Buffer resource over [base, base + bytes): loads past the end return zeros,
-// which is how ragged rows, ragged k and column tails read as zero.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, long bytes) {
     if (bytes < 0) bytes = 0;
     if (bytes > 0x7fffffffL) bytes = 0x7fffffffL;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ void bload_lds(rsrc_t r, const bf16* lds, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds), 16, voff, soff, 0, 0);
 }
-
-// ---- K-contiguous operand: straight from global memory into the LDS stage ----------
-// One wave instruction fills 8 LDS rows (1 KB, lane l -> row l/8, physical chunk
-// l%8); the lane therefore loads the logical chunk that the swizzle places at
-// that physical chunk.  Wave w fills row blocks 8w .. 8w+7.
-struct DirectOp {
-    rsrc_t r0, r1;          // r1: second source of paired rows (W3)
-    uint32_t ld_bytes;      // row pitch
-    int paired;
-};
-__device__ __forceinline__ void issue_direct(const DirectOp& op, const bf16* stage, int k0) {
-    const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
-    // row 8j + l/8 has swizzle key ((8j + l/8) >> 1) & 7 = (4 (j & 1) + (l >> 4)) & 7
-    const uint32_t row_off = (uint32_t)(lane >> 3) * op.ld_bytes;
-    const uint32_t vo_even = row_off + ((uint32_t)((lane & 7) ^ (lane >> 4)) << 4);
-    const uint32_t vo_odd = row_off + ((uint32_t)((lane & 7) ^ ((4 + (lane >> 4)) & 7)) << 4);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int j = wave * 8 + i;                       // row block: rows 8j .. 8j+7
-        const uint32_t vo = (i & 1) ? vo_odd : vo_even;   // wave * 8 is even: j & 1 == i & 1
-        int rowbase = 8 * j;
-        rsrc_t r = op.r0;
-        if (op.paired) {                                  // rows r: W1/W3 by (r >> 6) & 1
-            rowbase = ((j >> 4) << 6) + ((8 * j) & 63);
-            if ((j >> 3) & 1) r = op.r1;
-        }
-        bload_lds(r, stage + j * 512, vo, (uint32_t)rowbase * op.ld_bytes + (uint32_t)k0 * 2u);
-    }
+// s_waitcnt with only vmcnt constrained / only lgkmcnt constrained
+template <int N> __device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
-// ---- K-strided operand: natural [k][col] layout in LDS, transpose reads -------------
-// Memory holds [k][col] with col contiguous.  A stage keeps 64 k-rows of 256
-// columns (512-byte rows of 32 chunks), chunk XOR-swizzled by 2 * (row & 3).
-// One wave instruction fills 2 rows (lane l -> row l/32, physical chunk l%32).
-// Fragments come from ds_read_b64_tr_b16: inside each 16-lane group, lane l
-// receives element (l & 3) of the 8-byte reads of lanes 4j + (l >> 2), j = 0..3.
-// With lane 4j + m reading row k0 + j, columns c0 + 4m .. c0 + 4m + 3, lane l
-// gets the four k values k0 .. k0 + 3 of column c0 + l: two reads give the eight
-// consecutive k of one MFMA operand lane.  The swizzle keeps the four rows
-// touched by one 16-lane group on 16 distinct bank pairs.
-struct StridedOp {
-    rsrc_t r0, r1;          // r1: rows k >= kswitch (W3 after W1 along k)
+// One wave load: 64 lanes x 16 bytes from a buffer straight into LDS at lds_addr + lane * 16.
+// Issued through inline assembly so that the compiler's wait-count insertion does not
+// turn every later LDS read into a full drain of the load queue: the kernel counts
+// these loads itself (s_waitcnt vmcnt) before the barrier that publishes a stage.
+// M0 (the LDS destination register) is written here and used by nothing else in
+// these kernels; it is listed as clobbered, which clang reports as a reserved register.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// Where this wave's loads of one operand tile come from.  K-contiguous operands:
+// load i fills DIRECT_ROWS rows (lane -> row lane / CHUNKS, physical chunk lane % CHUNKS,
+// holding the logical chunk that the swizzle puts there); K-strided operands: load i
+// fills k-rows 2j, 2j + 1 of a natural [k][256] tile.
+struct OpPlan {
+    rsrc_t r0, r1;          // r1: second source (paired rows, or k >= kswitch)
     uint32_t ld_bytes;
-    int kswitch;
+    int paired, kswitch, strided;
+    uint32_t vo[2];         // lane offsets for even / odd loads
 };
-__device__ __forceinline__ void issue_strided(const StridedOp& op, const bf16* stage, int k0) {
-    const int lane = threadIdx.x & 63, wave = uni(threadIdx.x >> 6);
-    const uint32_t row_off = (uint32_t)(lane >> 5) * op.ld_bytes;
-    const uint32_t vo_even = row_off + ((uint32_t)((lane & 31) ^ (2 * (lane >> 5))) << 4);
-    const uint32_t vo_odd = row_off + ((uint32_t)((lane & 31) ^ (4 + 2 * (lane >> 5))) << 4);
-    rsrc_t r = op.r0;
-    int kk = k0;
-    if (k0 >= op.kswitch) { r = op.r1; kk = k0 - op.kswitch; }
+__device__ __forceinline__ OpPlan plan_direct(rsrc_t r0, rsrc_t r1, uint32_t ld, int paired) {
+    OpPlan o;
+    o.r0 = r0; o.r1 = r1; o.ld_bytes = ld; o.paired = paired; o.kswitch = 0x7fffffff; o.strided = 0;
+    const int lane = threadIdx.x & 63;
+    const uint32_t row_off = (uint32_t)(lane / CHUNKS) * ld;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int j = wave * 8 + i;                       // rows 2j, 2j + 1 of the stage
-        const uint32_t vo = (i & 1) ? vo_odd : vo_even;   // row & 3 = 2 (j & 1) + lane/32
-        bload_lds(r, stage + j * 512, vo, (uint32_t)(kk + 2 * j) * op.ld_bytes);
+    for (int par = 0; par < 2; ++par) {
+        const int key = (((DIRECT_ROWS * par) + lane / CHUNKS) / ROWS_PER_WIN) & (CHUNKS - 1);
+        o.vo[par] = row_off + ((uint32_t)((lane % CHUNKS) ^ key) << 4);
+    }
+    return o;
+}
+__device__ __forceinline__ OpPlan plan_strided(rsrc_t r0, rsrc_t r1, uint32_t ld, int kswitch) {
+    OpPlan o;
+    o.r0 = r0; o.r1 = r1; o.ld_bytes = ld; o.paired = 0; o.kswitch = kswitch; o.strided = 1;
+    const int lane = threadIdx.x & 63;
+    const uint32_t row_off = (uint32_t)(lane >> 5) * ld;
+    o.vo[0] = row_off + ((uint32_t)((lane & 31) ^ (2 * (lane >> 5))) << 4);
+    o.vo[1] = row_off + ((uint32_t)((lane & 31) ^ (4 + 2 * (lane >> 5))) << 4);
+    return o;
+}
+// load i (0 .. IPW-1) of this wave for k-tile starting at k0, into the tile at lds byte address t
+template <bool STRIDED>
+__device__ __forceinline__ void dma_one(const OpPlan& o, int i, uint32_t t, int k0, int wave) {
+    if (STRIDED) {
+        const int j = wave * STRIDED_IPW + i;
+        rsrc_t r = o.r0;
+        int kk = k0;
+        if (k0 >= o.kswitch) { r = o.r1; kk = k0 - o.kswitch; }
+        dma16(r, t + j * 1024, o.vo[i & 1], (uint32_t)(kk + 2 * j) * o.ld_bytes);
+    } else {
+        const int j = wave * DIRECT_IPW + i;
+        const int row0 = DIRECT_ROWS * j;
+        int rowbase = row0;
+        rsrc_t r = o.r0;
+        if (o.paired) {
+            rowbase = ((row0 >> 7) << 6) + (row0 & 63);
+            if ((row0 >> 6) & 1) r = o.r1;
+        }
+        dma16(r, t + j * 1024, o.vo[i & 1], (uint32_t)rowbase * o.ld_bytes + (uint32_t)k0 * 2u);
     }
 }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
-
-// 32 columns [colbase, colbase + 32) x 16 k of k-step ks, in MFMA operand layout.
 __device__ __forceinline__ bf16x8 read_strided(const bf16* T, int colbase, int ks) {
     const int lane = threadIdx.x & 63;
     const int L = lane & 15;
     const int col = colbase + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
-    const int pc = (col >> 3) ^ (2 * (L >> 2));           // k & 3 == L >> 2
+    const int pc = (col >> 3) ^ (2 * (L >> 2));
     const int k = 16 * ks + 8 * (lane >> 5) + (L >> 2);
     const bf16* p0 = T + k * 256 + pc * 8 + (col & 7);
-    const bf16* p1 = p0 + 4 * 256;                         // k + 4: same swizzle
+    const bf16* p1 = p0 + 4 * 256;
     v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(p0));
     v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(p1));
     typedef short v8s __attribute__((ext_vector_type(8)));
     v8s v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
 }
-
-// ---- MFMA fragments ----------------------------------------------------------------------
 struct Frags { bf16x8 a[4], b[4]; };
 __device__ __forceinline__ bf16x8 read_contig(const bf16* T, int rowbase, int ks) {
     const int lane = threadIdx.x & 63;
     const int rr = lane & 31, hk = lane >> 5;
-    const int ch = ((2 * ks + hk) ^ ((rr >> 1) & 7)) << 3;
+    const int key = ((rowbase + rr) / ROWS_PER_WIN) & (CHUNKS - 1);
+    const int ch = ((2 * ks + hk) ^ key) << 3;
     return *reinterpret_cast<const bf16x8*>(T + (rowbase + rr) * BK + ch);
 }
-template <bool AT, bool BT>
-__device__ __forceinline__ void read_frags(const bf16* As, const bf16* Bs, int ks, int wm, int wn, Frags& f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        f.a[i] = AT ? read_strided(As, wm * 128 + i * 32, ks) : read_contig(As, wm * 128 + i * 32, ks);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        f.b[j] = BT ? read_strided(Bs, wn * 128 + j * 32, ks) : read_contig(Bs, wn * 128 + j * 32, ks);
-}
-__device__ __forceinline__ void mma(const Frags& f, f32x16 (&acc)[4][4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
-}
-
-// ---- epilogue helpers -----------------------------------------------------------------
 __device__ __forceinline__ void store4(bf16* p, const float* v) {
     uint2 u;
     bf16* b = reinterpret_cast<bf16*>(&u);
@@ -201,10 +200,6 @@ __device__ __forceinline__ void load4(const bf16* p, float* v) {
     const bf16* b = reinterpret_cast<const bf16*>(&u);
     v[0] = (float)b[0]; v[1] = (float)b[1]; v[2] = (float)b[2]; v[3] = (float)b[3];
 }
-
-// Grouped tile order inside an mt x nt tile grid: groups of GROUP_N n-tiles, all
-// m-tiles of a group before the next group, so concurrently running tiles share
-// A row blocks and B column blocks in L2.
 __device__ __forceinline__ void grouped(int q, int mt, int nt, int& tm, int& tn) {
     const int gn = min(GROUP_N, nt);
     const int ng = q / (mt * gn);
@@ -214,28 +209,33 @@ __device__ __forceinline__ void grouped(int q, int mt, int nt, int& tm, int& tn)
     tn = ng * gn + (rem - tm * gsz);
 }
 
-// ---- the kernel ------------------------------------------------------------------------
 template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32>
 __global__ void __launch_bounds__(NTHR, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) bf16 lds[2][2][TILE_ELEMS];   // [stage][A/B]
+    __shared__ __attribute__((aligned(1024))) bf16 lds[NS][2][TILE_ELEMS];
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    // ---- which tile: workgroups are dealt round-robin to the 8 XCDs, so give each
-    // XCD a contiguous run of logical tiles (tiles that share operands meet in its L2)
-    const int nwg = gridDim.x;
-    int L = blockIdx.x;
-    if ((nwg & 7) == 0) L = (L & 7) * (nwg >> 3) + (L >> 3);
     const int NT = p.paired ? (p.ffn + 127) / 128 : (p.N + BN - 1) / BN;
+    int nreal;
+    if (MODE == MODE_ROWS) nreal = p.tile_prefix[p.E] * NT;
+    else if (MODE == MODE_KSEG) nreal = p.E * ((p.M + BM - 1) / BM) * NT;
+    else nreal = ((p.M + BM - 1) / BM) * NT;
+    nreal = uni(nreal);
+    int L = blockIdx.x;
+    if (p.xcd_balance) {   // XCD x (= blockIdx % 8) takes a contiguous, equal share of the tiles
+        const int x = L & 7, i = L >> 3, q = nreal >> 3, r = nreal & 7;
+        if (i >= q + (x < r ? 1 : 0)) return;
+        L = x * q + min(x, r) + i;
+    } else if (L >= nreal) return;
+
     int e = 0, m0 = 0, n_t = 0;
-    long row_base = 0;        // absolute row of the segment start (ROWS) / K start (KSEG)
-    int rows_valid = 0;       // valid rows of this tile in M
+    long row_base = 0;
+    int rows_valid = 0;
     int K = p.K;
     if (MODE == MODE_ROWS) {
         const int tmg = L / NT;
-        if (tmg >= p.tile_prefix[p.E]) return;
-        int lo = 0, hi = p.E;   // largest e with tile_prefix[e] <= tmg
+        int lo = 0, hi = p.E;
         while (hi - lo > 1) {
             int mid = (lo + hi) >> 1;
             if (p.tile_prefix[mid] <= tmg) lo = mid; else hi = mid;
@@ -251,7 +251,6 @@ gemm_bf16_kernel(GemmParams p) {
     } else if (MODE == MODE_KSEG) {
         const int MT = (p.M + BM - 1) / BM;
         e = L / (MT * NT);
-        if (e >= p.E) return;
         int tm;
         grouped(L - e * MT * NT, MT, NT, tm, n_t);
         m0 = tm * BM;
@@ -262,7 +261,6 @@ gemm_bf16_kernel(GemmParams p) {
         }
     } else {
         const int MT = (p.M + BM - 1) / BM;
-        if (L >= MT * NT) return;
         int tm;
         grouped(L, MT, NT, tm, n_t);
         m0 = tm * BM;
@@ -271,53 +269,42 @@ gemm_bf16_kernel(GemmParams p) {
     e = uni(e); m0 = uni(m0); n_t = uni(n_t); rows_valid = uni(rows_valid); K = uni(K);
     row_base = (long)uni((int)row_base);
     const int n0 = n_t * BN;
-    const int hid0 = n_t * 128;   // paired: first hidden unit of the tile
+    const int hid0 = n_t * 128;
     const bf16* Be = p.B + (long)e * p.bes;
     const bf16* B2e = p.B2 ? p.B2 + (long)e * p.bes : nullptr;
 
-    // ---- operand sources -----------------------------------------------------------------
-    DirectOp da = {}, db = {};
-    StridedOp sa = {}, sb = {};
-    if (AT) {   // A[k][m]: k rows of the segment, columns m0 ..
+    OpPlan pa, pb;
+    if (AT) {   // A[k][m]
         const bf16* base = p.A + row_base * p.lda + m0;
-        sa.r0 = make_rsrc(base, ((long)K * p.lda - m0) * 2);
-        sa.r1 = sa.r0;
-        sa.ld_bytes = (uint32_t)(p.lda * 2);
-        sa.kswitch = 0x7fffffff;
-    } else {    // A[m][k]: rows m0 .. m0 + rows_valid of the segment
+        rsrc_t r = make_rsrc(base, ((long)K * p.lda - m0) * 2);
+        pa = plan_strided(r, r, (uint32_t)(p.lda * 2), 0x7fffffff);
+    } else {    // A[m][k]
         const bf16* base = p.A + (row_base + m0) * p.lda;
-        da.r0 = make_rsrc(base, (long)rows_valid * p.lda * 2);
-        da.r1 = da.r0;
-        da.ld_bytes = (uint32_t)(p.lda * 2);
-        da.paired = 0;
+        rsrc_t r = make_rsrc(base, (long)rows_valid * p.lda * 2);
+        pa = plan_direct(r, r, (uint32_t)(p.lda * 2), 0);
     }
     if (BT) {   // B[k][n]
         if (MODE == MODE_KSEG) {
             const bf16* base = p.B + row_base * p.ldb + n0;
-            sb.r0 = make_rsrc(base, ((long)K * p.ldb - n0) * 2);
-            sb.r1 = sb.r0;
-            sb.kswitch = 0x7fffffff;
+            rsrc_t r = make_rsrc(base, ((long)K * p.ldb - n0) * 2);
+            pb = plan_strided(r, r, (uint32_t)(p.ldb * 2), 0x7fffffff);
         } else if (p.b2_kstart >= 0) {
-            sb.r0 = make_rsrc(Be + n0, ((long)p.b2_kstart * p.ldb - n0) * 2);
-            sb.r1 = make_rsrc(B2e + n0, ((long)(K - p.b2_kstart) * p.ldb - n0) * 2);
-            sb.kswitch = p.b2_kstart;
+            pb = plan_strided(make_rsrc(Be + n0, ((long)p.b2_kstart * p.ldb - n0) * 2),
+                              make_rsrc(B2e + n0, ((long)(K - p.b2_kstart) * p.ldb - n0) * 2),
+                              (uint32_t)(p.ldb * 2), p.b2_kstart);
         } else {
-            sb.r0 = make_rsrc(Be + n0, ((long)K * p.ldb - n0) * 2);
-            sb.r1 = sb.r0;
-            sb.kswitch = 0x7fffffff;
+            rsrc_t r = make_rsrc(Be + n0, ((long)K * p.ldb - n0) * 2);
+            pb = plan_strided(r, r, (uint32_t)(p.ldb * 2), 0x7fffffff);
         }
-        sb.ld_bytes = (uint32_t)(p.ldb * 2);
     } else {    // B[n][k]
-        if (p.paired) {
-            db.r0 = make_rsrc(Be + (long)hid0 * p.ldb, (long)(p.ffn - hid0) * p.ldb * 2);
-            db.r1 = make_rsrc(B2e + (long)hid0 * p.ldb, (long)(p.ffn - hid0) * p.ldb * 2);
-            db.paired = 1;
-        } else {
-            db.r0 = make_rsrc(Be + (long)n0 * p.ldb, (long)min(BN, p.N - n0) * p.ldb * 2);
-            db.r1 = db.r0;
-            db.paired = 0;
+        if (p.paired)
+            pb = plan_direct(make_rsrc(Be + (long)hid0 * p.ldb, (long)(p.ffn - hid0) * p.ldb * 2),
+                             make_rsrc(B2e + (long)hid0 * p.ldb, (long)(p.ffn - hid0) * p.ldb * 2),
+                             (uint32_t)(p.ldb * 2), 1);
+        else {
+            rsrc_t r = make_rsrc(Be + (long)n0 * p.ldb, (long)min(BN, p.N - n0) * p.ldb * 2);
+            pb = plan_direct(r, r, (uint32_t)(p.ldb * 2), 0);
         }
-        db.ld_bytes = (uint32_t)(p.ldb * 2);
     }
 
     f32x16 acc[4][4];
@@ -328,45 +315,79 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    constexpr int IPW_A = AT ? STRIDED_IPW : DIRECT_IPW;
+    constexpr int IPW_B = BT ? STRIDED_IPW : DIRECT_IPW;
+    constexpr int LPW = IPW_A + IPW_B;                 // loads per wave per k-tile
+    static_assert(LPW % KSTEPS == 0 && LPW / KSTEPS <= 8, "load parts");
+    constexpr int PART = LPW / KSTEPS;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&lds[0][0][0];
     const int nk = (K + BK - 1) / BK;
-    // the loads of tile kt go straight into LDS stage st
-    auto issue = [&](int kt, int st) {
-        const int k0 = kt * BK;
-        if (AT) issue_strided(sa, lds[st][0], k0); else issue_direct(da, lds[st][0], k0);
-        if (BT) issue_strided(sb, lds[st][1], k0); else issue_direct(db, lds[st][1], k0);
+    // load q (0 .. LPW-1) of k-tile kt; tiles past the end load harmless data (the buffer
+    // bounds make them zeros or rows of this operand) into a stage nobody reads again
+    auto dma = [&](int q, int kt) {
+        const uint32_t st = (uint32_t)(kt % NS) * (2 * TILE_ELEMS * 2);
+        if (q < IPW_A) dma_one<AT>(pa, q, lds_base + st, kt * BK, wave);
+        else dma_one<BT>(pb, q - IPW_A, lds_base + st + TILE_ELEMS * 2, kt * BK, wave);
+    };
+    auto read_one = [&](const bf16* As, const bf16* Bs, int ks, Frags& f, int idx) {
+        if (idx < 4) f.a[idx] = AT ? read_strided(As, wm * 128 + idx * 32, ks) : read_contig(As, wm * 128 + idx * 32, ks);
+        else f.b[idx - 4] = BT ? read_strided(Bs, wn * 128 + (idx - 4) * 32, ks) : read_contig(Bs, wn * 128 + (idx - 4) * 32, ks);
+    };
+    auto mfma_one = [&](const Frags& f, int i) {
+        acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[i & 3], f.a[i >> 2], acc[i >> 2][i & 3], 0, 0, 0);
     };
 
     if (nk > 0) {
-        issue(0, 0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int t = 0; t < DIST; ++t)
+#pragma unroll
+            for (int q = 0; q < LPW; ++q) dma(q, t);
+        wait_vm<LPW * (DIST - 1)>();
         __syncthreads();
+        Frags fa, fb;
+#pragma unroll
+        for (int idx = 0; idx < 8; ++idx) read_one(lds[0][0], lds[0][1], 0, fa, idx);
         for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            const bool more = kt + 1 < nk;
-            if (more) issue(kt + 1, cur ^ 1);
-            const bf16* As = lds[cur][0];
-            const bf16* Bs = lds[cur][1];
-            // fragments of k-step s+1 are read while the MFMAs of k-step s run; the
-            // scheduling fences keep the compiler from serialising reads and MFMAs
-            Frags f0, f1;
-            read_frags<AT, BT>(As, Bs, 0, wm, wn, f0);
-            read_frags<AT, BT>(As, Bs, 1, wm, wn, f1);
-            __builtin_amdgcn_sched_barrier(0);
-            mma(f0, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            read_frags<AT, BT>(As, Bs, 2, wm, wn, f0);
-            __builtin_amdgcn_sched_barrier(0);
-            mma(f1, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            read_frags<AT, BT>(As, Bs, 3, wm, wn, f1);
-            __builtin_amdgcn_sched_barrier(0);
-            mma(f0, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            mma(f1, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            if (more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
+            const int st = kt % NS;
+            const bf16* As = lds[st][0];
+            const bf16* Bs = lds[st][1];
+            const int pf = kt + DIST;
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                Frags& cur = (s & 1) ? fb : fa;
+                Frags& nxt = (s & 1) ? fa : fb;
+                if (s + 1 < KSTEPS) {
+                    // 16 slots: MFMA i, then fragment i of step s+1 (slots 0-7) or a load (8-15)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        mfma_one(cur, i);
+                        if (i < 8) read_one(As, Bs, s + 1, nxt, i);
+                        else if (i - 8 < PART) dma(s * PART + i - 8, pf);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                } else {
+                    // last step: loads under the first half, then publish tile kt+1 and read
+                    // its first fragments under the second half
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        mfma_one(cur, i);
+                        if (i < PART) dma(s * PART + i, pf);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    wait_vm<LPW * (DIST - 1)>();
+                    wait_lgkm0();
+                    __syncthreads();
+                    const int sn = (kt + 1) % NS;
+#pragma unroll
+                    for (int i = 8; i < 16; ++i) {
+                        mfma_one(cur, i);
+                        read_one(lds[sn][0], lds[sn][1], 0, nxt, i - 8);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
         }
+        wait_vm<0>();
     }
 
     // ---- epilogue ----------------------------------------------------------------------
@@ -544,6 +565,7 @@ hipError_t mfma_down_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     p.M = a.d; p.N = a.ffn;
     p.C = a.dW2; p.ldc = a.ffn; p.ces = (long)a.d * a.ffn;
     const int grid = a.E * ((a.d + BM - 1) / BM) * ((a.ffn + BN - 1) / BN);
+    p.xcd_balance = 1;
     return run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
 }
 
@@ -559,6 +581,7 @@ hipError_t mfma_up_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     p.C = a.dW1; p.ldc = a.d; p.ces = (long)a.ffn * a.d;
     if (glu) { p.C2 = a.dW3; p.c2_mstart = a.ffn; }
     const int grid = a.E * ((hcols + BM - 1) / BM) * ((a.d + BN - 1) / BN);
+    p.xcd_balance = 1;
     return run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
 }
 
