@@ -211,19 +211,26 @@ __device__ __forceinline__ void sgd8(float* master, const float* grad, void* wor
 
 template <class TW>
 __global__ void __launch_bounds__(256) sgd_kernel(SgdArgs a) {
-    const long n8 = a.n / 8;
-    const long stride = (long)gridDim.x * blockDim.x;
-    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    int sg = 0;
+    while (sg + 1 < a.nseg && (int)blockIdx.x >= a.blk0[sg + 1]) ++sg;
+    float* master = a.seg[sg].master;
+    const float* grad = a.seg[sg].grad;
+    void* work = a.seg[sg].work;
+    const long n = a.seg[sg].n;
+    const long n8 = n / 8;
+    const long stride = (long)(a.blk0[sg + 1] - a.blk0[sg]) * blockDim.x;
+    long i = (long)(blockIdx.x - a.blk0[sg]) * blockDim.x + threadIdx.x;
+    const long i0 = i;
     for (; i + stride < n8; i += 2 * stride) {
-        sgd8<TW>(a.master, a.grad, a.work, i, a.lr);
-        sgd8<TW>(a.master, a.grad, a.work, i + stride, a.lr);
+        sgd8<TW>(master, grad, work, i, a.lr);
+        sgd8<TW>(master, grad, work, i + stride, a.lr);
     }
-    if (i < n8) sgd8<TW>(a.master, a.grad, a.work, i, a.lr);
+    if (i < n8) sgd8<TW>(master, grad, work, i, a.lr);
     // tail (n not a multiple of 8)
-    for (long t = 8 * n8 + (long)blockIdx.x * blockDim.x + threadIdx.x; t < a.n; t += stride) {
-        float m = a.master[t] - a.lr * a.grad[t];
-        a.master[t] = m;
-        reinterpret_cast<TW*>(a.work)[t] = from_f<TW>(m);
+    for (long t = 8 * n8 + i0; t < n; t += stride) {
+        float m = master[t] - a.lr * grad[t];
+        master[t] = m;
+        reinterpret_cast<TW*>(work)[t] = from_f<TW>(m);
     }
 }
 
@@ -267,13 +274,23 @@ hipError_t launch_colsum(const ColSumArgs& a, int dtype, hipStream_t s) {
     else hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
-hipError_t launch_sgd(const SgdArgs& a, int dtype, hipStream_t s) {
-    if (a.n == 0) return hipSuccess;
-    long blocks = (a.n / 8 + 255) / 256;
-    if (blocks < 1) blocks = 1;
-    if (blocks > 16384) blocks = 16384;
-    if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(sgd_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(sgd_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
+hipError_t launch_sgd(SgdArgs& a, int dtype, hipStream_t s) {
+    // workgroups per segment in proportion to its size, about 16384 in all
+    long total = 0;
+    for (int i = 0; i < a.nseg; ++i) total += a.seg[i].n;
+    if (total == 0) return hipSuccess;
+    int b = 0;
+    for (int i = 0; i < a.nseg; ++i) {
+        a.blk0[i] = b;
+        long want = (a.seg[i].n / 8 + 255) / 256;
+        long share = (long)((16384.0 * (double)a.seg[i].n) / (double)total) + 1;
+        long nb = want < share ? want : share;
+        if (nb < 1) nb = 1;
+        b += (int)nb;
+    }
+    a.blk0[a.nseg] = b;
+    if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(sgd_kernel<float>, dim3(b), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(sgd_kernel<bf16>, dim3(b), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -87,8 +87,17 @@ struct ScatterArgs {
 struct ColSumArgs {
     const void* src; long ld; const int32_t* offsets; float* dst; int ncols, E;
 };
+// One SGD launch updates up to MOE_SGD_MAX_SEG parameter tensors; segment s owns
+// workgroups [blk0[s], blk0[s+1]).
+constexpr int MOE_SGD_MAX_SEG = 6;
+struct SgdSeg {
+    float* master; const float* grad; void* work; long n;
+};
 struct SgdArgs {
-    float* master; const float* grad; void* work; long n; float lr;
+    SgdSeg seg[MOE_SGD_MAX_SEG];
+    int blk0[MOE_SGD_MAX_SEG + 1];
+    int nseg;
+    float lr;
 };
 
 hipError_t launch_gather(const GatherArgs& a, int dtype, hipStream_t s);
@@ -96,7 +105,8 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s);
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_scatter(const ScatterArgs& a, int dtype, hipStream_t s);
 hipError_t launch_colsum(const ColSumArgs& a, int dtype, hipStream_t s);
-hipError_t launch_sgd(const SgdArgs& a, int dtype, hipStream_t s);
+// Fills blk0 from the segment sizes and launches one SGD kernel over all segments.
+hipError_t launch_sgd(SgdArgs& a, int dtype, hipStream_t s);
 int combine_loss_blocks(int T);
 
 // ---- expert / router contractions -------------------------------------------------

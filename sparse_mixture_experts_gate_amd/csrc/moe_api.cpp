@@ -386,11 +386,13 @@ static int train_step_impl(const moe_config* cfg, const void* X, const void* Y_t
         {glu ? nullptr : p->b2, g->db2, p->b2_w, E * d},
     };
     TRY(x.mark(MOE_STAGE_SGD));
+    SgdArgs sa = {};
+    sa.lr = lr;
     for (auto& u : upd) {
-        if (!u.m) continue;
-        SgdArgs sa = {u.m, u.g, u.w, u.n, lr};
-        TRY(launch_sgd(sa, cfg->dtype, x.s));
+        if (!u.m || u.n == 0) continue;
+        sa.seg[sa.nseg++] = SgdSeg{u.m, u.g, u.w, u.n};
     }
+    TRY(launch_sgd(sa, cfg->dtype, x.s));
     TRY(x.mark(MOE_NUM_STAGES));
     return MOE_OK;
 }

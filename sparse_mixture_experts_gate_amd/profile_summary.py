@@ -1,4 +1,6 @@
-"""Per-stage HBM traffic of one training step from two rocprofv3 counter runs.
+"""Summaries of rocprofv3 runs of the training step.
+
+HBM traffic per stage, from two counter runs:
 
     rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o fetch --output-format csv -- \\
         python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration-mib 1024
@@ -6,6 +8,13 @@
         python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration-mib 1024
     python -m sparse_mixture_experts_gate_amd.profile_summary OUT/fetch/fetch_counter_collection.csv \\
         OUT/write/write_counter_collection.csv --calibration-mib 1024 --json J --markdown M
+
+Kernel time per kernel, from one kernel-trace run:
+
+    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o kt -- \\
+        python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline
+    python -m sparse_mixture_experts_gate_amd.profile_summary --stats OUT/trace/kt_kernel_stats.csv \\
+        --steps 7 --markdown M --command "..."
 
 FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch.  Each is scaled by
 the factor that makes the known-size device copy (--copy-calibration-mib)
@@ -143,7 +152,8 @@ def markdown(rec, title, command):
              f"{rec['calibration']['copy_write_kib'] / 1024:.1f} MiB by WRITE_SIZE, so FETCH_SIZE is "
              f"scaled by {rec['calibration']['fetch_scale']} and WRITE_SIZE by "
              f"{rec['calibration']['write_scale']}.", "",
-             "| stage | launches | HBM read (GB) | HBM write (GB) | total (GB) | ms (under counters) |",
+             "FETCH_SIZE counts L2 misses (served by the MALL or HBM), WRITE_SIZE the L2 write-back traffic.", "",
+             "| stage | launches | fabric read (GB) | fabric write (GB) | total (GB) | ms (under counters) |",
              "|---|---|---|---|---|---|"]
     for st, e in rec["stages"].items():
         lines.append(f"| {st} | {e['launches']} | {e['fetch_bytes'] / 1e9:.3f} | {e['write_bytes'] / 1e9:.3f} | "
@@ -151,7 +161,44 @@ def markdown(rec, title, command):
     return "\n".join(lines) + "\n"
 
 
+def _short(name):
+    """Kernel name without argument lists of library (torch) kernels."""
+    if "at::native" in name:
+        return name.split("(")[0][:100]
+    return name[:120]
+
+
+def stats_markdown(path, steps, title, command):
+    """Per-kernel calls / total / average / min / max from a rocprofv3 kernel_stats.csv."""
+    rows = list(csv.DictReader(open(path)))
+    lines = [f"# {title}", "", "Command (repository root, one MI355X):", "", "```", command, "```", "",
+             f"{steps} training steps are traced (warm-up and timed); per-step time = total / {steps}.",
+             "Kernels named `at::native::...` and `__amd_rocclr_copyBuffer` are torch's input generation and",
+             "copies before the steps; they are not part of a step.", "",
+             "| kernel | calls | total (ms) | per step (ms) | average (ms) | min (ms) | max (ms) | % of GPU time |",
+             "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        tot = float(r["TotalDurationNs"]) / 1e6
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {tot:.2f} | {tot / steps:.3f} | "
+                     f"{float(r['AverageNs']) / 1e6:.3f} | {float(r['MinNs']) / 1e6:.3f} | "
+                     f"{float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
+    if argv is None:
+        argv = sys.argv[1:]
+    if argv and argv[0] == "--stats":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("--stats", required=True)
+        ap.add_argument("--steps", type=int, required=True)
+        ap.add_argument("--workload", default="grouped_sigmoid_t32768_d7168_e256")
+        ap.add_argument("--markdown", required=True)
+        ap.add_argument("--command", default="")
+        a = ap.parse_args(argv)
+        open(a.markdown, "w").write(stats_markdown(a.stats, a.steps, f"Kernel trace, training step, {a.workload}",
+                                                   a.command))
+        return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("fetch_csv")
     ap.add_argument("write_csv")
