@@ -39,6 +39,16 @@ the design notes of the repository.
   R11 the loss of every step is MSE + aux_coef * aux.
   R12 no intermediate rounding: inputs are taken at the exact values the
       caller holds (bfloat16 decoded exactly) and all arithmetic is float64.
+  R17 correction bias (optional, sigmoid scoring only): it enters selection
+      and nothing else.  Selection then ranks fp32 values v = fl32(s) + b
+      (one fp32 addition of the correctly rounded sigmoid score and the fp32
+      bias), the precision in which the kernel takes that integer decision;
+      the gates and their gradients come from the unbiased scores.
+  R18 top-2-sum group score (optional): a group's score is the sum of its two
+      largest member values (fp32 when selection runs on fp32 values).  With
+      this rule and no bias, selection ranks fl32(s).
+  R19 route scale: the renormalised gates are multiplied by a constant
+      (default 1); its gradient enters through the renormalisation.
 
 Parity pins (tests/test_oracle_*.py): brute-force top-k over all subsets,
 gates summing to one and closed forms of the renormalisation, routing
@@ -140,19 +150,42 @@ def aux_probs(l, score):
     return s
 
 
-def select_topk(l, k, n_groups=1, topk_groups=1):
-    """Group-limited top-k on logits (R1, R2).
+def selection_values(l, score, e_bias=None, group_score="max"):
+    """What selection ranks: the logits (R2), or fp32 scores plus the bias (R17, R18).
+
+    With no bias and the max group score the logits are ranked exactly.
+    Otherwise every score is rounded once to fp32 and the fp32 bias is added
+    with one fp32 addition.
+    """
+    if e_bias is None and group_score == "max":
+        return l
+    v = scores(l, score).astype(np.float32)
+    if e_bias is not None:
+        v = (v + np.asarray(e_bias, dtype=np.float32)[None, :]).astype(np.float32)
+    return v
+
+
+def select_topk(l, k, n_groups=1, topk_groups=1, group_score="max"):
+    """Group-limited top-k on the values l (logits, or selection_values) (R1, R2, R18).
 
     Groups are consecutive blocks of E / n_groups experts.  A group's score is
-    its largest member logit; the topk_groups groups first in the order
-    (-score, group id) stay eligible.  Eligible experts are ordered by
-    (-logit, expert id) and the first k are returned in that order.
+    its largest member value (R1), or the sum of its two largest (R18); the
+    topk_groups groups first in the order (-score, group id) stay eligible.
+    Eligible experts are ordered by (-value, expert id) and the first k are
+    returned in that order.
     """
     T, E = l.shape
     gsize = E // n_groups
     eligible = np.ones((T, E), dtype=bool)
     if n_groups > 1:
-        gscore = l.reshape(T, n_groups, gsize).max(axis=2)
+        blocks = l.reshape(T, n_groups, gsize)
+        if group_score == "max":
+            gscore = blocks.max(axis=2)
+        elif group_score == "top2":
+            top2 = np.sort(blocks, axis=2)[:, :, -2:]
+            gscore = top2[:, :, 1] + top2[:, :, 0]
+        else:
+            raise ValueError(group_score)
         gid = np.broadcast_to(np.arange(n_groups), (T, n_groups))
         kept = np.zeros((T, n_groups), dtype=bool)
         for t in range(T):
@@ -167,10 +200,10 @@ def select_topk(l, k, n_groups=1, topk_groups=1):
     return idx
 
 
-def gate_weights(l, topk_idx, score):
-    """g_ti = w_ti / sum_j w_tj, with w the selected experts' scores (R3)."""
+def gate_weights(l, topk_idx, score, route_scale=1.0):
+    """g_ti = c * w_ti / sum_j w_tj, w the selected experts' unbiased scores (R3, R17, R19)."""
     w = np.take_along_axis(scores(l, score), topk_idx, axis=1)
-    return w / w.sum(axis=1, keepdims=True), w
+    return route_scale * w / w.sum(axis=1, keepdims=True), w
 
 
 # ----------------------------------------------------------------------------
@@ -326,10 +359,10 @@ def mse(Y, Yt):
     return float((r * r).sum() / n), 2.0 * r / n
 
 
-def renorm_backward(dgate, gates, w):
-    """dw_i = (dg_i - sum_j g_j dg_j) / S with S = sum_j w_j."""
+def renorm_backward(dgate, gates, w, route_scale=1.0):
+    """dw_i = (c dg_i - sum_j g_j dg_j) / S with S = sum_j w_j and g = c w / S (R19)."""
     S = w.sum(axis=1, keepdims=True)
-    return (dgate - (gates * dgate).sum(axis=1, keepdims=True)) / S
+    return (route_scale * dgate - (gates * dgate).sum(axis=1, keepdims=True)) / S
 
 
 def router_backward(l, topk_idx, dw, dq, score):
@@ -371,27 +404,32 @@ class Shape:
     topk_groups: int = 1
     score: str = "softmax"
     expert: str = "relu"
+    group_score: str = "max"      # R1 or R18
+    route_scale: float = 1.0      # R19
 
 
-def route(X, Wg, shp: Shape, topk_idx=None):
+def route(X, Wg, shp: Shape, topk_idx=None, e_bias=None):
     """Router + selection + gates + routing tables.
 
     topk_idx may be supplied by the caller (a resolved routing, see the
     parity tests); it must be a valid top-k of these logits up to the logit
-    error of the device arithmetic.
+    error of the device arithmetic.  e_bias is the optional correction bias
+    (R17).
     """
     l = router_logits(X, Wg)
     if topk_idx is None:
-        topk_idx = select_topk(l, shp.k, shp.n_groups, shp.topk_groups)
-    g, w = gate_weights(l, topk_idx, shp.score)
+        v = selection_values(l, shp.score, e_bias, shp.group_score)
+        topk_idx = select_topk(v, shp.k, shp.n_groups, shp.topk_groups, group_score=shp.group_score)
+    g, w = gate_weights(l, topk_idx, shp.score, shp.route_scale)
     r = routing_tables(topk_idx, shp.E)
     return {"logits": l, "topk_idx": topk_idx, "gates": g, "w": w, "routing": r,
             "q": aux_probs(l, shp.score)}
 
 
 def layer_forward(X, P: Dict[str, Optional[np.ndarray]], shp: Shape, topk_idx=None):
-    """Forward of the whole layer.  P holds Wg, W1, b1, W2, b2, W3 (float64)."""
-    fw = route(X, P["Wg"], shp, topk_idx)
+    """Forward of the whole layer.  P holds Wg, W1, b1, W2, b2, W3 (float64) and
+    optionally e_bias, the correction bias (R17), which no gradient reaches."""
+    fw = route(X, P["Wg"], shp, topk_idx, P.get("e_bias"))
     r = fw["routing"]
     T, d = X.shape
     EO = np.zeros((T * shp.k, d))
@@ -436,7 +474,7 @@ def layer_backward(X, P, shp: Shape, fw, dY, aux_coef):
                 grads[n][e] = g[n]
         dXp[lo:hi] = g["dXp"]
     dX = scatter_rows(dXp, r.slot_of)
-    dw = renorm_backward(dgate, fw["gates"], fw["w"])
+    dw = renorm_backward(dgate, fw["gates"], fw["w"], shp.route_scale)
     dq = aux_grad_q(r.counts, T, shp.k, E, aux_coef)
     dl = router_backward(fw["logits"], r.topk_idx, dw, dq, shp.score)
     grads["dWg"] = dl.T @ X

@@ -10,9 +10,10 @@ from oracle import moe_oracle as O
 
 import tests.test_oracle_layer as L
 import tests.test_oracle_routing as R
+import tests.test_oracle_variants as V
 
 
-def _larger_id_wins(l, k, n_groups=1, topk_groups=1):
+def _larger_id_wins(l, k, n_groups=1, topk_groups=1, **kw):
     # tie rule flipped: among equal logits the larger id comes first
     T, E = l.shape
     idx = np.empty((T, k), dtype=np.int64)
@@ -22,7 +23,7 @@ def _larger_id_wins(l, k, n_groups=1, topk_groups=1):
     return idx
 
 
-def _no_renorm(l, topk_idx, score):
+def _no_renorm(l, topk_idx, score, route_scale=1.0):
     w = np.take_along_axis(O.scores(l, score), topk_idx, axis=1)
     return w, w
 
@@ -60,7 +61,7 @@ def _router_backward_wrong_sign(l, topk_idx, dw, dq, score):
 _orig_select = O.select_topk
 
 
-def _orig_select_min(l, k, n_groups=1, topk_groups=1):
+def _orig_select_min(l, k, n_groups=1, topk_groups=1, **kw):
     T, E = l.shape
     gsize = E // n_groups
     gscore = l.reshape(T, n_groups, gsize).min(axis=2)
@@ -72,6 +73,27 @@ def _orig_select_min(l, k, n_groups=1, topk_groups=1):
     for t in range(T):
         idx[t] = np.lexsort((np.arange(E), -l[t], ~elig[t]))[:k]
     return idx
+
+
+_orig_selection_values = O.selection_values
+_orig_gate_weights = O.gate_weights
+_orig_renorm_backward = O.renorm_backward
+
+
+def _bias_ignored(l, score, e_bias=None, group_score="max"):
+    return _orig_selection_values(l, score, None, "top2" if e_bias is not None else group_score)
+
+
+def _group_rule_ignored(l, k, n_groups=1, topk_groups=1, group_score="max"):
+    return _orig_select(l, k, n_groups, topk_groups)
+
+
+def _scale_dropped(l, topk_idx, score, route_scale=1.0):
+    return _orig_gate_weights(l, topk_idx, score, 1.0)
+
+
+def _scale_missing_in_backward(dgate, gates, w, route_scale=1.0):
+    return _orig_renorm_backward(dgate, gates, w, 1.0)
 
 
 def _run_all(fns):
@@ -96,6 +118,11 @@ PINS = [
     (L.test_hand_worked_golden, ()),
     (L.test_central_differences, ("swiglu", "sigmoid", 1)),
     (L.test_central_differences, ("gelu", "softmax", 2)),
+    (V.test_variant_topk_matches_brute_force, (8, 2, 4, 2, "ties", "top2")),
+    (V.test_golden_group_rules, ("top2",)),
+    (V.test_golden_bias_selects_and_gates_stay_unbiased, ()),
+    (V.test_route_scale_gates_sum_to_the_scale, (2.5,)),
+    (V.test_variant_central_differences, ()),
 ]
 
 
@@ -108,6 +135,10 @@ PINS = [
     ("silu_grad", _bad_silu_grad),
     ("routing_tables", _descending_slots),
     ("router_backward", _router_backward_wrong_sign),
+    ("selection_values", _bias_ignored),
+    ("select_topk", _group_rule_ignored),
+    ("gate_weights", _scale_dropped),
+    ("renorm_backward", _scale_missing_in_backward),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, repl):
     monkeypatch.setattr(O, name, repl)
