@@ -10,7 +10,12 @@
  *   select  group-limited top-k on the logits; groups are consecutive blocks
  *           of E/n_groups experts scored by their largest member; ties go to
  *           the smaller group / expert id                 (Infra Lab "Project status")
- *   gates   g = w_sel / sum(w_sel), w = the selected scores (outline Part 2)
+ *           Variants of the DeepSeek gate: an optional correction bias that
+ *           enters selection only, and a group score equal to the sum of the
+ *           group's two largest members; selection then ranks the fp32
+ *           scores plus the bias             (Infra Lab "Numerical contracts")
+ *   gates   g = c * w_sel / sum(w_sel), w = the selected unbiased scores,
+ *           c = route_scale (default 1)    (outline Part 2)
  *   dispatch per-expert histogram, exclusive scan, stable slots in ascending
  *           token order, gather into expert-major rows    (outline Part 4)
  *   experts ReLU/GELU MLP with biases, or SwiGLU W2(silu(W1 x) * W3 x)
@@ -66,6 +71,8 @@ extern "C" {
 #define MOE_EXPERT_SWIGLU   2     /* W2 (silu(W1 x) * W3 x), no biases */
 #define MOE_DTYPE_F32       0
 #define MOE_DTYPE_BF16      1     /* bf16 storage and MFMA inputs, fp32 accumulation */
+#define MOE_GROUP_MAX       0     /* group score = largest member logit */
+#define MOE_GROUP_TOP2_SUM  1     /* group score = sum of the two largest member values */
 
 #define MOE_MAX_EXPERTS   256
 #define MOE_MAX_K          16
@@ -74,7 +81,13 @@ extern "C" {
  * Layer shape.  Rules (MOE_ERR_INVALID_ARG when broken): T >= 0; d, E, ffn,
  * k, n_groups, topk_groups >= 1; k <= E; E % n_groups == 0;
  * topk_groups <= n_groups; k <= topk_groups * (E / n_groups);
- * T * k < 2^31.
+ * T * k < 2^31; group_score is MOE_GROUP_MAX or MOE_GROUP_TOP2_SUM, and
+ * MOE_GROUP_TOP2_SUM with n_groups > 1 needs E / n_groups >= 2; route_scale
+ * is finite and >= 0 (0 stands for 1, so that a zeroed struct is the plain
+ * layer).
+ * Selection values: the logits when group_score == MOE_GROUP_MAX and no
+ * correction bias is given (exact); otherwise the fp32 scores (softmax
+ * probabilities or sigmoid values) plus the correction bias, added in fp32.
  * Kernel limits (MOE_ERR_UNSUPPORTED): E <= 256, k <= 16; float32: d and ffn
  * multiples of 4; bfloat16: d and ffn multiples of 64 and E a multiple of 8.
  */
@@ -89,12 +102,18 @@ typedef struct moe_config {
     int32_t score;        /* MOE_SCORE_* */
     int32_t expert;       /* MOE_EXPERT_* */
     int32_t dtype;        /* MOE_DTYPE_* */
+    int32_t group_score;  /* MOE_GROUP_* */
+    float   route_scale;  /* gate multiplier after renormalisation; 0 = 1 */
 } moe_config;
 
 /*
  * Weights in the working dtype.  Wg [E,d]; W1 [E,ffn,d]; b1 [E,ffn];
  * W2 [E,d,ffn]; b2 [E,d]; W3 [E,ffn,d].  b1/b2 are required for the MLP
  * kinds and ignored (may be NULL) for SwiGLU; W3 is required for SwiGLU only.
+ * e_bias float [E] is the optional correction bias of the DeepSeek gate (NULL
+ * = none; only with MOE_SCORE_SIGMOID, else MOE_ERR_INVALID_ARG): it is added
+ * to the scores for selection only; gates and every gradient use the unbiased
+ * scores, and no gradient is computed for it.
  */
 typedef struct moe_weights {
     const void* Wg;
@@ -103,13 +122,14 @@ typedef struct moe_weights {
     const void* W2;
     const void* b2;
     const void* W3;
+    const float* e_bias;
 } moe_weights;
 
 /*
  * Routing outputs of the forward (all written by moe_forward / moe_route):
  *   logits   float [T,E]   router logits in fp32 (moe_route: ignored, may be NULL)
- *   topk_idx int32 [T,k]   selected experts, in (-logit, id) order
- *   gates    float [T,k]   renormalised gates, same order
+ *   topk_idx int32 [T,k]   selected experts, in (-selection value, id) order
+ *   gates    float [T,k]   renormalised gates times route_scale, same order
  *   counts   int32 [E]     rows per expert
  *   offsets  int32 [E+1]   exclusive scan of counts
  *   slot_of  int32 [T,k]   expert-major row of (t, i)
@@ -147,11 +167,13 @@ typedef struct moe_grads {
  * Parameters updated in place by moe_train_step: float32 masters and the
  * working copies (dtype).  For MOE_DTYPE_F32 a working pointer may equal its
  * master.  For bf16 the working copy is rewritten as the round-to-nearest-
- * even conversion of the updated master.
+ * even conversion of the updated master.  e_bias is the optional correction
+ * bias (as in moe_weights); it is read, never updated.
  */
 typedef struct moe_params {
     float* Wg;  float* W1;  float* b1;  float* W2;  float* b2;  float* W3;
     void*  Wg_w; void* W1_w; void* b1_w; void* W2_w; void* b2_w; void* W3_w;
+    const float* e_bias;
 } moe_params;
 
 /* Workspace buffers whose byte offsets moe_workspace_offset() reports.
@@ -179,10 +201,12 @@ int64_t moe_workspace_offset(const moe_config* cfg, int32_t which);
 /*
  * Routing only, from caller-supplied fp32 logits [T,E]: scores, group-limited
  * top-k, gates, histogram, scan and slot maps, and the aux value (steps of
- * outline Parts 2, 3, 4 and 6).  Writes every field of *r except r->logits.
+ * outline Parts 2, 3, 4 and 6).  e_bias: the optional correction bias
+ * (float [E] or NULL, as in moe_weights).  Writes every field of *r except
+ * r->logits.
  */
-int moe_route(const moe_config* cfg, const float* logits, moe_routing* r,
-              void* workspace, size_t workspace_bytes, void* stream);
+int moe_route(const moe_config* cfg, const float* logits, const float* e_bias,
+              moe_routing* r, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Forward of the layer: router GEMM, routing, gather, expert up and down

@@ -490,7 +490,7 @@ def train_step(X, Yt, P, shp: Shape, lr, aux_coef, topk_idx=None):
     m, dY = mse(fw["Y"], Yt)
     loss = m + aux_coef * fw["aux"]
     grads = layer_backward(X, P, shp, fw, dY, aux_coef)
-    newP = {}
+    newP = {"e_bias": P.get("e_bias")}          # the correction bias is not trained (R17)
     for n in ("Wg", "W1", "b1", "W2", "b2", "W3"):
         newP[n] = None if P.get(n) is None else sgd(P[n], grads["d" + n], lr)
     return {"fw": fw, "grads": grads, "mse": m, "loss": loss, "params": newP, "dY": dY}

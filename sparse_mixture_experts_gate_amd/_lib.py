@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 SCORE = {"softmax": 0, "sigmoid": 1}
 EXPERT = {"relu": 0, "gelu": 1, "swiglu": 2}
 DTYPE = {"f32": 0, "bf16": 1}
+GROUP = {"max": 0, "top2": 1}
 WS = {"XP": 0, "H": 1, "A": 2, "EO": 3}
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_NULL_PTR", -3: "MOE_ERR_MISALIGNED",
@@ -40,11 +41,16 @@ class MoeError(RuntimeError):
 
 class moe_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("T", "d", "E", "ffn", "k", "n_groups", "topk_groups", "score", "expert", "dtype")]
+                ("T", "d", "E", "ffn", "k", "n_groups", "topk_groups", "score", "expert", "dtype",
+                 "group_score")] + [("route_scale", ctypes.c_float)]
+
+
+WEIGHTS = ("Wg", "W1", "b1", "W2", "b2", "W3", "e_bias")
+PARAMS = ("Wg", "W1", "b1", "W2", "b2", "W3", "Wg_w", "W1_w", "b1_w", "W2_w", "b2_w", "W3_w", "e_bias")
 
 
 class moe_weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("Wg", "W1", "b1", "W2", "b2", "W3")]
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHTS]
 
 
 class moe_routing(ctypes.Structure):
@@ -57,8 +63,7 @@ class moe_grads(ctypes.Structure):
 
 
 class moe_params(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("Wg", "W1", "b1", "W2", "b2", "W3", "Wg_w", "W1_w", "b1_w", "W2_w", "b2_w", "W3_w")]
+    _fields_ = [(n, ctypes.c_void_p) for n in PARAMS]
 
 
 _lib = None
@@ -77,8 +82,8 @@ def load() -> ctypes.CDLL:
         lib.moe_workspace_bytes.restype = ctypes.c_size_t
         lib.moe_workspace_offset.argtypes = [P(moe_config), ctypes.c_int32]
         lib.moe_workspace_offset.restype = ctypes.c_int64
-        lib.moe_route.argtypes = [P(moe_config), ctypes.c_void_p, P(moe_routing), ctypes.c_void_p,
-                                  ctypes.c_size_t, ctypes.c_void_p]
+        lib.moe_route.argtypes = [P(moe_config), ctypes.c_void_p, ctypes.c_void_p, P(moe_routing),
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         lib.moe_forward.argtypes = [P(moe_config), ctypes.c_void_p, P(moe_weights), ctypes.c_void_p,
                                     P(moe_routing), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         lib.moe_backward.argtypes = [P(moe_config), ctypes.c_void_p, P(moe_weights), P(moe_routing),
@@ -102,12 +107,18 @@ def load() -> ctypes.CDLL:
 
 # ---- marshalling helpers ------------------------------------------------------------
 
-def config(w) -> moe_config:
-    """moe_config from a workloads.Workload (or anything with the same fields)."""
+def config(w, group_score=None, route_scale=None) -> moe_config:
+    """moe_config from a workloads.Workload (or anything with the same fields).
+
+    group_score ("max" / "top2" or the MOE_GROUP_* code) and route_scale default
+    to the workload's own fields when it has them, else to the plain gate.
+    """
     def code(table, v):
         return table[v] if isinstance(v, str) else int(v)
+    gs = group_score if group_score is not None else getattr(w, "group_score", "max")
+    rs = route_scale if route_scale is not None else getattr(w, "route_scale", 1.0)
     return moe_config(w.T, w.d, w.E, w.ffn, w.k, w.n_groups, w.topk_groups, code(SCORE, w.score),
-                      code(EXPERT, w.expert), code(DTYPE, w.dtype))
+                      code(EXPERT, w.expert), code(DTYPE, w.dtype), code(GROUP, gs), float(rs))
 
 
 def _p(t: Optional[torch.Tensor]):
@@ -147,7 +158,7 @@ def routing_struct(r: dict) -> moe_routing:
 
 
 def weights_struct(w: dict) -> moe_weights:
-    return moe_weights(*[_p(w.get(n)) for n in ("Wg", "W1", "b1", "W2", "b2", "W3")])
+    return moe_weights(*[_p(w.get(n)) for n in WEIGHTS])
 
 
 def grads_struct(g: dict) -> moe_grads:
@@ -155,16 +166,15 @@ def grads_struct(g: dict) -> moe_grads:
 
 
 def params_struct(p: dict) -> moe_params:
-    return moe_params(*[_p(p.get(n)) for n in
-                        ("Wg", "W1", "b1", "W2", "b2", "W3", "Wg_w", "W1_w", "b1_w", "W2_w", "b2_w", "W3_w")])
+    return moe_params(*[_p(p.get(n)) for n in PARAMS])
 
 
 # ---- entry points, same names as the C ABI -----------------------------------------
 
 def moe_route(cfg: moe_config, logits: torch.Tensor, routing: dict, workspace: torch.Tensor,
-              stream=None) -> None:
+              stream=None, e_bias: Optional[torch.Tensor] = None) -> None:
     r = routing_struct(routing)
-    _check(load().moe_route(ctypes.byref(cfg), _p(logits), ctypes.byref(r), _p(workspace),
+    _check(load().moe_route(ctypes.byref(cfg), _p(logits), _p(e_bias), ctypes.byref(r), _p(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream)), "moe_route")
 
 

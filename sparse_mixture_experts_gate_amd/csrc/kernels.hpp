@@ -16,6 +16,9 @@ struct RouteArgs {
     int32_t* hist;         // [E][nchunk]
     float* qpart;          // [nchunk][E]
     int T, E, k, n_groups, topk_groups, score, nchunk;
+    const float* bias;     // [E] correction bias (selection only) or NULL
+    int group_score;       // MOE_GROUP_*
+    float route_scale;     // gate multiplier after renormalisation
 };
 struct ScanArgs {
     const int32_t* hist;   // [E][nchunk]
@@ -54,6 +57,7 @@ struct RouterBwdArgs {
     void* dlogits;         // [T,E] dtype
     float aux_coef;
     int T, E, k, score;
+    float route_scale;     // the gates passed in already carry it
 };
 
 hipError_t launch_route_topk(const RouteArgs& a, hipStream_t s);

@@ -12,6 +12,7 @@
 // counts, offsets and the expert GEMM tile schedule never leave the device.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -35,6 +36,7 @@ struct Layout {
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+template <class P> inline bool aligned16(const P* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool shape_ok(const moe_config* c) {
     if (!c) return false;
@@ -47,7 +49,19 @@ bool shape_ok(const moe_config* c) {
     if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID) return false;
     if (c->expert < MOE_EXPERT_RELU || c->expert > MOE_EXPERT_SWIGLU) return false;
     if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16) return false;
+    if (c->group_score != MOE_GROUP_MAX && c->group_score != MOE_GROUP_TOP2_SUM) return false;
+    if (c->group_score == MOE_GROUP_TOP2_SUM && c->n_groups > 1 && c->E / c->n_groups < 2) return false;
+    if (!std::isfinite(c->route_scale) || c->route_scale < 0.f) return false;
     return true;
+}
+
+inline float route_scale(const moe_config* c) { return c->route_scale == 0.f ? 1.f : c->route_scale; }
+
+// The correction bias is optional, sigmoid scoring only, and read as fp32 [E].
+int check_bias(const moe_config* c, const float* e_bias) {
+    if (!e_bias) return MOE_OK;
+    if (c->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+    return aligned16(e_bias) ? MOE_OK : MOE_ERR_MISALIGNED;
 }
 
 int supported(const moe_config* c) {
@@ -95,7 +109,6 @@ Layout layout(const moe_config* c) {
     return L;
 }
 
-template <class P> inline bool aligned16(const P* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Device pointers of one call.  Token-sized tensors (tok = true) may be NULL
 // when T == 0, since they then hold no elements.
@@ -162,10 +175,11 @@ struct Ctx {
     } while (0)
 
 // Routing from logits: top-k, gates, histogram, scan, slots, aux.
-int run_routing(const Ctx& x, const float* logits, moe_routing* r) {
+int run_routing(const Ctx& x, const float* logits, const float* e_bias, moe_routing* r) {
     const moe_config* c = x.c;
     RouteArgs ra = {logits, r->topk_idx, r->gates, x.buf<int32_t>(B_HIST), x.buf<float>(B_QPART),
-                    c->T, c->E, c->k, c->n_groups, c->topk_groups, c->score, nchunk(c)};
+                    c->T, c->E, c->k, c->n_groups, c->topk_groups, c->score, nchunk(c),
+                    e_bias, c->group_score, route_scale(c)};
     TRY(launch_route_topk(ra, x.s));
     ScanArgs sa = {x.buf<int32_t>(B_HIST), x.buf<int32_t>(B_CBASE), r->counts, nchunk(c)};
     TRY(launch_expert_scan(sa, c->E, x.s));
@@ -204,7 +218,7 @@ int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_
     TRY(x.mark(MOE_STAGE_ROUTER_LOGITS));
     TRY(f32 ? simple_router_logits(rg, x.s) : mfma_router_logits(rg, x.s));
     TRY(x.mark(MOE_STAGE_ROUTE));
-    int st = run_routing(x, r->logits, r);
+    int st = run_routing(x, r->logits, w->e_bias, r);
     if (st != MOE_OK) return st;
     GatherArgs ga = {X, r->slot_of, x.buf<void>(B_XP), c->T, c->k, vec};
     TRY(x.mark(MOE_STAGE_GATHER));
@@ -255,7 +269,7 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
         TRY(launch_colsum(b1, c->dtype, x.s));
     }
     RouterBwdArgs rb = {r->logits, r->topk_idx, r->gates, x.buf<float>(B_DGATE), r->counts,
-                        x.buf<void>(B_DL), aux_coef, c->T, c->E, c->k, c->score};
+                        x.buf<void>(B_DL), aux_coef, c->T, c->E, c->k, c->score, route_scale(c)};
     TRY(x.mark(MOE_STAGE_ROUTER_BWD));
     TRY(launch_router_bwd(rb, c->dtype, x.s));
     RouterGemmArgs rg = {c->T, c->d, c->E, X, w->Wg, x.buf<void>(B_DL), nullptr,
@@ -274,7 +288,7 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 const char* moe_status_string(int st) {
     switch (st) {
@@ -306,17 +320,18 @@ int64_t moe_workspace_offset(const moe_config* cfg, int32_t which) {
     }
 }
 
-int moe_route(const moe_config* cfg, const float* logits, moe_routing* r, void* workspace,
-              size_t workspace_bytes, void* stream) {
+int moe_route(const moe_config* cfg, const float* logits, const float* e_bias, moe_routing* r,
+              void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_common(cfg, workspace, workspace_bytes);
     if (st != MOE_OK) return st;
+    if ((st = check_bias(cfg, e_bias)) != MOE_OK) return st;
     if (!r) return MOE_ERR_NULL_PTR;
     Ptrs P;
     P.add(logits, true);
     add_routing(P, r, false);
     if ((st = P.check(cfg->T)) != MOE_OK) return st;
     Ctx x{cfg, (char*)workspace, layout(cfg), (hipStream_t)stream};
-    return run_routing(x, logits, r);
+    return run_routing(x, logits, e_bias, r);
 }
 
 int moe_forward(const moe_config* cfg, const void* X, const moe_weights* w, void* Y,
@@ -324,6 +339,7 @@ int moe_forward(const moe_config* cfg, const void* X, const moe_weights* w, void
     int st = check_common(cfg, workspace, workspace_bytes);
     if (st != MOE_OK) return st;
     if (!w || !r) return MOE_ERR_NULL_PTR;
+    if ((st = check_bias(cfg, w->e_bias)) != MOE_OK) return st;
     Ptrs P;
     P.add(X, true); P.add(Y, true);
     add_weights(P, cfg, w);
@@ -356,6 +372,7 @@ static int train_step_impl(const moe_config* cfg, const void* X, const void* Y_t
     int st = check_common(cfg, workspace, workspace_bytes);
     if (st != MOE_OK) return st;
     if (!p || !r || !g) return MOE_ERR_NULL_PTR;
+    if ((st = check_bias(cfg, p->e_bias)) != MOE_OK) return st;
     const bool glu = cfg->expert == MOE_EXPERT_SWIGLU;
     Ptrs P;
     P.add(X, true); P.add(Y_target, true); P.add(Y, true); P.add(loss_out);
@@ -371,7 +388,7 @@ static int train_step_impl(const moe_config* cfg, const void* X, const void* Y_t
     }
     Ctx x{cfg, (char*)workspace, layout(cfg), (hipStream_t)stream, events};
     moe_weights w = {p->Wg_w, p->W1_w, glu ? nullptr : p->b1_w, p->W2_w, glu ? nullptr : p->b2_w,
-                     glu ? p->W3_w : nullptr};
+                     glu ? p->W3_w : nullptr, p->e_bias};
     st = run_forward(x, X, &w, Y, r, Y_target, aux_coef, loss_out);
     if (st != MOE_OK) return st;
     st = run_backward(x, X, &w, r, x.buf<void>(B_DY), aux_coef, g);

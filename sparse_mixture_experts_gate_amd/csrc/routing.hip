@@ -90,11 +90,14 @@ __device__ __forceinline__ float selected_score(float l, const TokenScores& ts, 
     return 1.0f / (1.0f + expf(-l));
 }
 
+// Selection ranks the logits (exact) for the plain gate, or the fp32 scores plus
+// the correction bias when a bias or the top-2-sum group score is in use.
 __global__ void __launch_bounds__(256)
 route_topk_kernel(RouteArgs a) {
     __shared__ int s_hist[MOE_MAX_EXPERTS];
     __shared__ float s_q[RT_WAVES][MOE_MAX_EXPERTS];
-    __shared__ float s_l[RT_WAVES][MOE_MAX_EXPERTS];
+    __shared__ float s_l[RT_WAVES][MOE_MAX_EXPERTS];   // logits (for the unbiased gates)
+    __shared__ float s_v[RT_WAVES][MOE_MAX_EXPERTS];   // selection values
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = a.E, k = a.k, G = a.n_groups;
     const int chunk = blockIdx.x;
@@ -114,24 +117,39 @@ route_topk_kernel(RouteArgs a) {
 #pragma unroll
         for (int m = 0; m < EPL; ++m) qacc[m] += ts.q[m];
 
-        // group limit: keep topk_groups groups by (-max member logit, group id)
+        // selection values
+        const bool on_scores = a.bias != nullptr || a.group_score == MOE_GROUP_TOP2_SUM;
+        float v[EPL];
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) {
+            int e = lane + 64 * m;
+            if (!on_scores) v[m] = ts.l[m];
+            else v[m] = (e < E) ? ts.s[m] + (a.bias ? a.bias[e] : 0.f) : -INFINITY;
+            if (e < E) { s_l[wave][e] = ts.l[m]; s_v[wave][e] = v[m]; }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // group limit: keep topk_groups groups by (-group score, group id); the
+        // group score is the largest member value, or the sum of the two largest
         uint64_t kept_lo = ~0ull, kept_hi = ~0ull;   // bit per group (G <= 128 supported)
         if (G > 1) {
+            const bool top2 = a.group_score == MOE_GROUP_TOP2_SUM;
+            float gv[2] = {-INFINITY, -INFINITY};    // lanes own groups lane, lane+64
 #pragma unroll
-            for (int m = 0; m < EPL; ++m) {
-                int e = lane + 64 * m;
-                if (e < E) s_l[wave][e] = ts.l[m];
+            for (int h = 0; h < 2; ++h) {
+                const int g = lane + 64 * h;
+                if (g < G) {
+                    float b1 = -INFINITY, b2 = -INFINITY;
+                    for (int j = 0; j < gsize; ++j) {
+                        const float x = s_v[wave][g * gsize + j];
+                        if (x > b1) { b2 = b1; b1 = x; } else if (x > b2) b2 = x;
+                    }
+                    gv[h] = top2 ? b1 + b2 : b1;
+                }
             }
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            float gv0 = -INFINITY, gv1 = -INFINITY;    // lanes own groups lane, lane+64
-            if (lane < G) {
-                for (int j = 0; j < gsize; ++j) gv0 = fmaxf(gv0, s_l[wave][lane * gsize + j]);
-            }
-            if (lane + 64 < G) {
-                for (int j = 0; j < gsize; ++j) gv1 = fmaxf(gv1, s_l[wave][(lane + 64) * gsize + j]);
-            }
+            const float gv0 = gv[0], gv1 = gv[1];
             kept_lo = kept_hi = 0;
             bool t0 = lane >= G, t1 = lane + 64 >= G;  // taken / absent
             for (int r = 0; r < a.topk_groups; ++r) {
@@ -145,7 +163,7 @@ route_topk_kernel(RouteArgs a) {
             }
         }
 
-        // top-k over eligible experts by (-logit, id)
+        // top-k over eligible experts by (-value, id)
         bool taken[EPL];
 #pragma unroll
         for (int m = 0; m < EPL; ++m) {
@@ -158,30 +176,32 @@ route_topk_kernel(RouteArgs a) {
             taken[m] = !elig;
         }
         int sel_e = -1;      // lane i < k keeps the i-th pick
-        float sel_l = 0.f;
         for (int i = 0; i < k; ++i) {
             float bv = -INFINITY; int bi = 0x7fffffff;
 #pragma unroll
             for (int m = 0; m < EPL; ++m) {
                 int e = lane + 64 * m;
-                if (!taken[m] && beats(ts.l[m], e, bv, bi)) { bv = ts.l[m]; bi = e; }
+                if (!taken[m] && beats(v[m], e, bv, bi)) { bv = v[m]; bi = e; }
             }
             wave_argmax(bv, bi);
 #pragma unroll
             for (int m = 0; m < EPL; ++m)
                 if (bi == lane + 64 * m) taken[m] = true;
-            if (lane == i) { sel_e = bi; sel_l = bv; }
+            if (lane == i) sel_e = bi;
         }
         // finite logits always leave k eligible experts; keep indices in range even
         // for malformed (NaN) input so that no later kernel indexes out of bounds
         if (lane < k && (sel_e < 0 || sel_e >= E)) sel_e = 0;
-        float w = (lane < k) ? selected_score(sel_l, ts, a.score) : 0.f;
+        // gates from the unbiased score of each pick
+        float w = (lane < k) ? selected_score(s_l[wave][sel_e], ts, a.score) : 0.f;
         float S = wave_sum(w);
         if (lane < k) {
             a.topk_idx[(size_t)t * k + lane] = sel_e;
-            a.gates[(size_t)t * k + lane] = w / S;
+            a.gates[(size_t)t * k + lane] = (w / S) * a.route_scale;
             atomicAdd(&s_hist[sel_e], 1);
         }
+        // s_l / s_v are rewritten for the next token only after every lane has read them
+        __builtin_amdgcn_wave_barrier();
     }
 
     // aux partial sums: waves' running sums (token order) added in wave order
@@ -366,7 +386,8 @@ router_bwd_kernel(RouterBwdArgs a) {
     }
     const float S = wave_sum(w_i);
     const float gdg = wave_sum(g_i * dg_i);
-    const float dw_i = (lane < k) ? (dg_i - gdg) / S : 0.f;
+    // g = c w / S: dL/dw_i = (c dg_i - sum_j g_j dg_j) / S
+    const float dw_i = (lane < k) ? (a.route_scale * dg_i - gdg) / S : 0.f;
     // aux gradient: dq_te = aux_coef * E * f_e / T, f_e = counts_e / (T k)
     const float c0 = a.aux_coef * (float)E / ((float)a.T * (float)a.T * (float)k);
     float sel[EPL], dq[EPL];

@@ -46,6 +46,10 @@ class Workload:
     steps: int
     init: str         # "fan_in" | "std0.02"
     gate: str         # "normal" | "zipf_tie"
+    # router variants (defaults: the plain gate)
+    group_score: str = "max"      # "max" | "top2"
+    route_scale: float = 1.0
+    e_bias: float = 0.0           # std of the seeded correction bias; 0 = no bias
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -88,7 +92,7 @@ WORKLOADS = [
 
 BY_NAME = {w.name: w for w in WORKLOADS}
 
-_TENSOR_ID = {"X": 1, "Yt": 2, "Wg": 3, "W1": 4, "W2": 5, "W3": 6, "dY": 7, "logits": 8}
+_TENSOR_ID = {"X": 1, "Yt": 2, "Wg": 3, "W1": 4, "W2": 5, "W3": 6, "dY": 7, "logits": 8, "e_bias": 9}
 
 
 def tensor_seed(base: int, tensor: str, expert: int = 0) -> int:
@@ -137,7 +141,9 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu",
     """All inputs of one layer step: activations, targets, master and working weights.
 
     Returned keys: X, Yt (working dtype); Wg, W1, b1, W2, b2, W3 (float32
-    masters); and the same names with a ``_w`` suffix for the working copies.
+    masters); and the same names with a ``_w`` suffix for the working copies;
+    e_bias, the float32 correction bias [E] ~ N(0, w.e_bias^2) (None when
+    w.e_bias == 0).
     Tensors that the expert kind does not use are None.  With masters=False
     the float32 masters are not kept (their keys hold None) and only the
     working copies are built, one expert at a time.
@@ -167,6 +173,8 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu",
             out[n], out[n + "_w"] = (z if masters else None), z.to(wd)
     else:
         out["b1"] = out["b2"] = out["b1_w"] = out["b2_w"] = None
+    out["e_bias"] = (_normal((w.E,), w.e_bias, tensor_seed(seed, "e_bias"), device)
+                     if w.e_bias > 0 else None)
     return out
 
 

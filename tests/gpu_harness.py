@@ -72,17 +72,22 @@ def assert_close(name, got, ref, rtol, atol, extra_abs=0.0):
 
 def shape_of(w) -> O.Shape:
     return O.Shape(E=w.E, k=w.k, n_groups=w.n_groups, topk_groups=w.topk_groups, score=w.score,
-                   expert=w.expert)
+                   expert=w.expert, group_score=w.group_score, route_scale=w.route_scale)
 
 
-def _sorted_eligible(l_row, n_groups, topk_groups):
-    """Eligible experts' logits in selection order, and the group scores in order."""
+def _group_scores(v_row, n_groups, group_score):
+    b = np.sort(v_row.reshape(n_groups, -1), axis=1)
+    return b[:, -1] if group_score == "max" else b[:, -1] + b[:, -2]
+
+
+def _sorted_eligible(l_row, n_groups, topk_groups, group_score="max"):
+    """Eligible experts' selection values in selection order, and the group scores in order."""
     E = l_row.shape[0]
     gs = E // n_groups
     elig = np.ones(E, dtype=bool)
     gvals = None
     if n_groups > 1:
-        g = l_row.reshape(n_groups, gs).max(axis=1)
+        g = _group_scores(l_row, n_groups, group_score)
         order = np.lexsort((np.arange(n_groups), -g))
         gvals = g[order]
         kept = np.zeros(n_groups, dtype=bool)
@@ -100,15 +105,22 @@ def _near(vals, upto, eps):
     return bool(np.any((d > 0) & (d < eps)))
 
 
-def resolve_routing(l64, gpu_idx, w, eps):
-    """Oracle selection with ambiguous tokens taken from the GPU after validation."""
-    ref = O.select_topk(l64, w.k, w.n_groups, w.topk_groups)
+def resolve_routing(l64, gpu_idx, w, eps, e_bias=None):
+    """Oracle selection with ambiguous tokens taken from the GPU after validation.
+
+    Works on the selection values: the logits for the plain gate, or the fp32
+    scores plus the correction bias for the router variants (the score is at
+    most as sensitive as the logit, so the same eps band applies).
+    """
+    v = O.selection_values(l64, w.score, e_bias, w.group_score)
+    ref = O.select_topk(v, w.k, w.n_groups, w.topk_groups, group_score=w.group_score)
+    l64 = np.asarray(v, dtype=np.float64)
     gpu_idx = np.asarray(gpu_idx, dtype=np.int64)
     diff = np.where(np.any(ref != gpu_idx, axis=1))[0]
     resolved = ref.copy()
     n_amb = 0
     for t in diff:
-        vals, ids, gvals = _sorted_eligible(l64[t], w.n_groups, w.topk_groups)
+        vals, ids, gvals = _sorted_eligible(l64[t], w.n_groups, w.topk_groups, w.group_score)
         amb = _near(vals, w.k, eps) or (gvals is not None and _near(gvals, w.topk_groups, eps))
         assert amb, f"token {t}: GPU top-k {gpu_idx[t]} differs from oracle {ref[t]} at a clear margin"
         # the GPU's pick must be a valid top-k within eps: no expert left out of the
@@ -123,7 +135,7 @@ def resolve_routing(l64, gpu_idx, w, eps):
             if e not in chosen and (e // gs) in chosen_groups:
                 assert l64[t, e] <= lo + eps, f"token {t}: left-out expert {e} clearly larger"
         if w.n_groups > 1:
-            gsc = l64[t].reshape(w.n_groups, gs).max(axis=1)
+            gsc = _group_scores(l64[t], w.n_groups, w.group_score)
             cut = np.sort(gsc)[::-1][w.topk_groups - 1]
             assert len(chosen_groups) <= w.topk_groups
             assert all(gsc[g] >= cut - eps for g in chosen_groups), f"token {t}: group clearly dropped"
@@ -146,6 +158,7 @@ class GpuRun:
         self.X = inp["X"].to(device)
         self.weights = {n: (None if inp.get(n + "_w") is None else inp[n + "_w"].to(device))
                         for n in ("Wg", "W1", "b1", "W2", "b2", "W3")}
+        self.weights["e_bias"] = None if inp.get("e_bias") is None else inp["e_bias"].to(device)
 
     def forward(self):
         L.moe_forward(self.cfg, self.X, self.weights, self.Y, self.routing, self.ws)
@@ -161,7 +174,9 @@ class GpuRun:
 
 
 def oracle_params(inp):
-    return {n: to64(inp.get(n + "_w")) for n in ("Wg", "W1", "b1", "W2", "b2", "W3")}
+    P = {n: to64(inp.get(n + "_w")) for n in ("Wg", "W1", "b1", "W2", "b2", "W3")}
+    P["e_bias"] = None if inp.get("e_bias") is None else inp["e_bias"].cpu().numpy().astype(np.float32)
+    return P
 
 
 def check_routing_tables(r_gpu, resolved, w):
@@ -191,7 +206,8 @@ def full_parity(w, inp, dY, aux_coef, check_saved=True, label=""):
     shp = shape_of(w)
     l64 = X64 @ P["Wg"].T
     assert_close("logits", to64(run.routing["logits"]), l64, rtol, atol)
-    resolved, n_amb = resolve_routing(l64, run.routing["topk_idx"].cpu().numpy(), w, EPS[w.dtype])
+    resolved, n_amb = resolve_routing(l64, run.routing["topk_idx"].cpu().numpy(), w, EPS[w.dtype],
+                                      P["e_bias"])
     check_routing_tables(run.routing, resolved, w)
     fw = O.layer_forward(X64, P, shp, topk_idx=resolved)
     gr = O.layer_backward(X64, P, shp, fw, to64(dY), aux_coef)

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert L.abi_version() == 1
+    assert L.abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert L.status_string(code) and L.status_string(code) != "unknown status"
     assert L.status_string(12345) == "unknown status"
@@ -65,9 +65,20 @@ def test_workspace_bytes(lib):
     assert L.workspace_offset(L.config(bad), "H") == -1
 
 
-def _call_forward(cfg, ws_bytes=1 << 30, ptr=4096, ws_ptr=4096):
+def test_binding_structs_match_the_header():
+    """Every ctypes struct lists the members of its C struct, in order."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name, cls in (("moe_config", L.moe_config), ("moe_weights", L.moe_weights),
+                      ("moe_routing", L.moe_routing), ("moe_grads", L.moe_grads),
+                      ("moe_params", L.moe_params)):
+        body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (name, name), text, re.S).group(1)
+        members = re.findall(r"\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*[;,]", body)
+        assert members == [f[0] for f in cls._fields_], (name, members)
+
+
+def _call_forward(cfg, ws_bytes=1 << 30, ptr=4096, ws_ptr=4096, e_bias=None):
     lib = L.load()
-    w = L.moe_weights(ptr, ptr, ptr, ptr, ptr, ptr)
+    w = L.moe_weights(ptr, ptr, ptr, ptr, ptr, ptr, e_bias)
     r = L.moe_routing(ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr)
     return lib.moe_forward(ctypes.byref(cfg), ctypes.c_void_p(ptr), ctypes.byref(w), ctypes.c_void_p(ptr),
                            ctypes.byref(r), ctypes.c_void_p(ws_ptr), ws_bytes, None)
@@ -87,6 +98,37 @@ def _call_forward(cfg, ws_bytes=1 << 30, ptr=4096, ws_ptr=4096):
 def test_invalid_configs_are_rejected_before_launch(lib, change, code):
     cfg = L.config(W.WORKLOADS[0].replace(**change))
     assert _call_forward(cfg) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(group_score=7), -1),
+    (dict(route_scale=-1.0), -1),
+    (dict(route_scale=float("nan")), -1),
+    (dict(route_scale=float("inf")), -1),
+    (dict(route_scale=2.5), 0),
+    (dict(group_score="top2"), 0),
+])
+def test_router_variant_rules(lib, kw, code):
+    cfg = L.config(W.WORKLOADS[0], **kw)
+    if code == 0:
+        # valid: accepted by validation (no launch here: the pointers are fake)
+        assert L.workspace_bytes(cfg) > 0
+    else:
+        assert L.workspace_bytes(cfg) == 0
+        assert _call_forward(cfg) == code
+
+
+def test_top2_group_score_needs_two_members_per_group(lib):
+    w = W.WORKLOADS[0].replace(n_groups=4, topk_groups=2, k=2)     # E = 4: one expert per group
+    assert _call_forward(L.config(w, group_score="top2")) == -1
+    assert L.workspace_bytes(L.config(w, group_score="top2")) == 0
+
+
+def test_correction_bias_rules(lib):
+    w = W.WORKLOADS[0]                                   # softmax scoring
+    assert _call_forward(L.config(w), e_bias=4096) == -1     # bias needs sigmoid scoring
+    ws = W.WORKLOADS[0].replace(score="sigmoid")
+    assert _call_forward(L.config(ws), e_bias=4100) == -3    # misaligned bias
 
 
 def test_bf16_shape_rules(lib):

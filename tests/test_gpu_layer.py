@@ -47,11 +47,23 @@ BF16_CASES = [
 ]
 
 
+# router variants: correction bias (selection only), top-2-sum group score, route scale
+VARIANT_CASES = [
+    wl("f32_swiglu_bias_top2_scale", expert="swiglu", score="sigmoid", n_groups=4, topk_groups=2,
+       e_bias=0.1, group_score="top2", route_scale=2.5),
+    wl("f32_relu_softmax_top2_half", n_groups=2, topk_groups=1, group_score="top2", route_scale=0.5),
+    wl("bf16_swiglu_bias_top2_scale", T=700, d=384, E=16, ffn=192, k=3, n_groups=4, topk_groups=2,
+       dtype="bf16", expert="swiglu", score="sigmoid", e_bias=0.1, group_score="top2", route_scale=2.5),
+    wl("bf16_gelu_bias_max", T=500, d=256, E=16, ffn=320, k=2, n_groups=4, topk_groups=2,
+       dtype="bf16", expert="gelu", score="sigmoid", e_bias=0.2),
+]
+
+
 def _inputs(w, seed=0):
     return W.make_inputs(w, seed=seed, masters=True)
 
 
-@pytest.mark.parametrize("w", F32_CASES + BF16_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("w", F32_CASES + BF16_CASES + VARIANT_CASES, ids=lambda w: w.name)
 def test_forward_backward_parity(w):
     say(f"layer parity {w}")
     inp = _inputs(w)
@@ -138,6 +150,8 @@ def train_step_parity(w, inp, label):
         if inp.get(n) is not None:
             params[n] = inp[n].clone().to(dev)
             params[n + "_w"] = inp[n + "_w"].clone().to(dev)
+    if inp.get("e_bias") is not None:
+        params["e_bias"] = inp["e_bias"].to(dev)
     X, Yt = inp["X"].to(dev), inp["Yt"].to(dev)
     L.moe_train_step(cfg, X, Yt, params, w.lr, w.aux_coef, Y, r, g, loss, ws)
     torch.cuda.synchronize()
@@ -145,7 +159,7 @@ def train_step_parity(w, inp, label):
     X64 = to64(inp["X"])
     P = oracle_params(inp)
     l64 = X64 @ P["Wg"].T
-    resolved, n_amb = resolve_routing(l64, r["topk_idx"].cpu().numpy(), w, EPS[w.dtype])
+    resolved, n_amb = resolve_routing(l64, r["topk_idx"].cpu().numpy(), w, EPS[w.dtype], P["e_bias"])
     check_routing_tables(r, resolved, w)
     st = O.train_step(X64, to64(inp["Yt"]), P, shape_of(w), w.lr, w.aux_coef, topk_idx=resolved)
     say(f"[{label}] loss gpu {loss.tolist()} oracle {[st['mse'], st['fw']['aux'], st['loss']]}")
@@ -153,6 +167,8 @@ def train_step_parity(w, inp, label):
     assert_close("Y", to64(Y), st["fw"]["Y"], rtol, atol)
     for n in g:
         assert_close(n, to64(g[n]), st["grads"][n], rtol, atol)
+    if "e_bias" in params:
+        assert torch.equal(params["e_bias"].cpu(), inp["e_bias"]), "the correction bias was written"
     for n in ("Wg", "W1", "b1", "W2", "b2", "W3"):
         if n not in params:
             continue
@@ -168,8 +184,8 @@ def train_step_parity(w, inp, label):
     return params, loss
 
 
-@pytest.mark.parametrize("w", [F32_CASES[0], F32_CASES[2], BF16_CASES[1], BF16_CASES[3]],
-                         ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [F32_CASES[0], F32_CASES[2], BF16_CASES[1], BF16_CASES[3],
+                               VARIANT_CASES[0], VARIANT_CASES[2]], ids=lambda w: w.name)
 def test_train_step_parity(w):
     train_step_parity(w, _inputs(w), w.name)
 

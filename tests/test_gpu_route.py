@@ -11,7 +11,7 @@ import torch
 from oracle import moe_oracle as O
 from sparse_mixture_experts_gate_amd import _lib as L
 from sparse_mixture_experts_gate_amd import workloads as W
-from tests.gpu_harness import assert_close, say
+from tests.gpu_harness import assert_close, resolve_routing, say
 
 pytestmark = pytest.mark.gpu
 
@@ -34,17 +34,17 @@ CASES = [
 ]
 
 
-def _workload(T, E, k, G, TG, score):
+def _workload(T, E, k, G, TG, score, **kw):
     return W.Workload("route", T=T, d=4, E=E, ffn=4, k=k, n_groups=G, topk_groups=TG, score=score,
                       expert="relu", dtype="f32", lr=0.0, aux_coef=0.0, steps=1, init="fan_in",
-                      gate="normal")
+                      gate="normal", **kw)
 
 
-def _route(w, logits):
+def _route(w, logits, e_bias=None):
     cfg = L.config(w)
     ws = L.alloc_workspace(cfg, "cuda")
     r = L.alloc_routing(w, "cuda")
-    L.moe_route(cfg, logits.cuda(), r, ws)
+    L.moe_route(cfg, logits.cuda(), r, ws, e_bias=None if e_bias is None else e_bias.cuda())
     torch.cuda.synchronize()
     return {n: v.cpu() for n, v in r.items()}
 
@@ -86,3 +86,53 @@ def test_route_is_deterministic():
     a, b = _route(w, logits), _route(w, logits)
     for n in a:
         assert torch.equal(a[n], b[n]), n
+
+
+# router variants: (T, E, k, G, TG, score, kind, bias std, group score, route scale)
+VARIANTS = [
+    (777, 64, 6, 8, 4, "sigmoid", "normal", 0.1, "top2", 2.5),
+    (300, 256, 8, 8, 4, "sigmoid", "ties", 0.25, "top2", 1.0),
+    (500, 32, 4, 4, 2, "softmax", "normal", 0.0, "top2", 1.0),
+    (400, 64, 6, 8, 4, "sigmoid", "normal", 0.1, "max", 1.0),
+    (256, 256, 8, 128, 16, "sigmoid", "normal", 0.05, "top2", 0.5),   # 128 groups of two
+    (0, 8, 2, 2, 1, "sigmoid", "normal", 0.1, "top2", 2.0),           # no tokens
+]
+EPS_V = 1e-6   # fp32 selection values: the device sigmoid/softmax may differ by an ulp
+
+
+@pytest.mark.parametrize("T,E,k,G,TG,score,kind,bstd,gs,rs", VARIANTS)
+def test_route_variants(T, E, k, G, TG, score, kind, bstd, gs, rs):
+    say(f"route variant T={T} E={E} k={k} G={G}/{TG} {score} {kind} bias={bstd} {gs} scale={rs}")
+    w = _workload(T, E, k, G, TG, score, group_score=gs, route_scale=rs, e_bias=bstd)
+    logits = W.make_router_logits(T, E, kind, seed=T + E + 1)
+    bias = W.make_inputs(w.replace(T=1, d=8, ffn=8), seed=T)["e_bias"]
+    r = _route(w, logits, bias)
+    l64 = logits.double().numpy()
+    b32 = None if bias is None else bias.numpy().astype(np.float32)
+    if T == 0:
+        assert float(r["aux"][0]) == 0.0
+        return
+    resolved, n_amb = resolve_routing(l64, r["topk_idx"].numpy(), w, EPS_V, b32)
+    say(f"  ambiguous tokens {n_amb} of {T}")
+    assert n_amb <= max(2, T // 50)
+    rt = O.routing_tables(resolved, E)
+    assert np.array_equal(r["counts"].numpy(), rt.counts)
+    assert np.array_equal(r["offsets"].numpy(), rt.offsets)
+    assert np.array_equal(r["slot_of"].numpy(), rt.slot_of)
+    assert np.array_equal(r["token_of"].numpy(), rt.token_of)
+    g, _ = O.gate_weights(l64, resolved, score, rs)
+    assert_close("gates", r["gates"].double().numpy(), g, 1e-5, 1e-5)
+    aux, _, _ = O.aux_loss(rt.counts, O.aux_probs(l64, score), k)
+    assert_close("aux", r["aux"].double().numpy(), [aux], 1e-5, 1e-5)
+
+
+def test_bias_changes_picks_but_not_the_gates_of_unchanged_picks():
+    w0 = _workload(2000, 64, 6, 8, 4, "sigmoid")
+    wb = w0.replace(e_bias=0.01)          # small enough to leave about a quarter of the picks
+    logits = W.make_router_logits(2000, 64, "normal", seed=9)
+    bias = W.make_inputs(wb.replace(T=1, d=8, ffn=8), seed=4)["e_bias"]
+    a = _route(w0, logits)
+    b = _route(wb, logits, bias)
+    same = np.all(a["topk_idx"].numpy() == b["topk_idx"].numpy(), axis=1)
+    assert 0 < same.sum() < 2000, "the bias should change some picks and leave others"
+    assert torch.equal(a["gates"][same], b["gates"][same])
