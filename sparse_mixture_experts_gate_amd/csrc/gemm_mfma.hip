@@ -29,8 +29,11 @@
 //     barrier per k-tile publishes the next stage, with the first fragments of
 //     that stage read under the last MFMAs of the current one;
 //   * the MFMA is issued with the N operand first, so each lane's
-//     accumulators hold 4 consecutive output columns: epilogue stores are
-//     8-byte (bf16) or 16-byte (fp32) vectors;
+//     accumulators hold 4 consecutive output columns; plain stores (bf16 or
+//     fp32) and the SwiGLU forward outputs go out through LDS, so that every
+//     store instruction writes whole rows with 16-byte vectors; the
+//     activation-backward epilogues read H and write directly from the
+//     accumulator layout;
 //   * tiles are scheduled on the device from the expert offsets: ROWS mode
 //     walks the m-tiles of every expert's row segment (prefix of per-expert
 //     tile counts, binary search per workgroup); KSEG mode gives each expert
@@ -391,6 +394,153 @@ gemm_bf16_kernel(GemmParams p) {
     }
 
     // ---- epilogue ----------------------------------------------------------------------
+    if constexpr (EPI == EPI_STORE && OUT_F32) {
+        // fp32 tile written out through LDS in two passes of 128 rows: each pass the two
+        // wavefronts that own those rows put their accumulators in LDS as 1 KB rows (16-byte
+        // chunk q of row r at chunk q ^ (r & 63)), then all 256 threads store whole rows
+        float* stage = reinterpret_cast<float*>(&lds[0][0][0]);
+        __syncthreads();                                   // every wave is past its last LDS read
+        const int rr = lane & 31, hk = lane >> 5;
+        const int qt = tid & 63;
+        for (int pass = 0; pass < 2; ++pass) {
+            if (wm == pass) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = i * 32 + rr;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int q = wn * 32 + j * 8 + g * 2 + hk;
+                            *reinterpret_cast<float4*>(stage + r * 256 + ((q ^ (r & 63)) << 2)) =
+                                make_float4(acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                                            acc[i][j][g * 4 + 3]);
+                        }
+                }
+            }
+            __syncthreads();
+            const int n = n0 + qt * 4;
+            float b[4] = {0.f, 0.f, 0.f, 0.f};
+            if (p.bias && n < p.N) load4(p.bias + (long)e * p.bias_es + n, b);
+#pragma unroll 4
+            for (int it = 0; it < 32; ++it) {
+                const int r = it * 4 + (tid >> 6);
+                const int ml = pass * 128 + r;
+                const float4 x = *reinterpret_cast<const float4*>(stage + r * 256 + ((qt ^ (r & 63)) << 2));
+                if (ml < rows_valid && n < p.N) {
+                    const float v[4] = {x.x + b[0], x.y + b[1], x.z + b[2], x.w + b[3]};
+                    const long row = (MODE == MODE_ROWS) ? row_base + m0 + ml : (long)(m0 + ml);
+                    if (MODE == MODE_KSEG) {
+                        void* base = p.C;
+                        long m = row;
+                        if (p.C2 && m >= p.c2_mstart) { base = p.C2; m -= p.c2_mstart; }
+                        store4(reinterpret_cast<float*>(base) + (long)e * p.ces + m * p.ldc + n, v);
+                    } else {
+                        store4(reinterpret_cast<float*>(p.C) + row * p.ldc + n, v);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        return;
+    }
+    if constexpr ((EPI == EPI_STORE || EPI == EPI_UP_SWIGLU) && !OUT_F32) {
+        // bf16 tile written out through LDS: 512-byte rows of 32 chunks, chunk q of row r at
+        // q ^ (r & 31); each lane puts its 4 consecutive columns (8 bytes) in place, then the
+        // 256 threads store whole rows with 16-byte vectors
+        bf16* stage = &lds[0][0][0];
+        __syncthreads();
+        const int rr = lane & 31, hk = lane >> 5;
+        auto put = [&](int r, int c, const float* v) {      // c: first of 4 columns
+            const int q = c >> 3;
+            store4(stage + r * 256 + ((q ^ (r & 31)) << 3) + (c & 7), v);
+        };
+        // stage columns [c_lo, c_lo + ncols) of rows 0..255, store row r's columns to dst(r, c)
+        auto drain = [&](int ncols, auto dst) {
+            const int cpr = ncols / 8;                       // 16-byte chunks per row
+            const int rows_per_it = 256 / cpr;
+            const int q = tid % cpr;
+            for (int r = tid / cpr; r < 256; r += rows_per_it) {
+                const uint4 x = *reinterpret_cast<const uint4*>(stage + r * 256 + ((q ^ (r & 31)) << 3));
+                if (r < rows_valid) dst(r, q * 8, x);
+            }
+        };
+        if constexpr (EPI == EPI_STORE) {
+            float bias[4][4][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * 128 + j * 32 + g * 8 + hk * 4;
+                    if (p.bias && n < p.N) load4(p.bias + (long)e * p.bias_es + n, bias[j][g]);
+                    else bias[j][g][0] = bias[j][g][1] = bias[j][g][2] = bias[j][g][3] = 0.f;
+                }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float v[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][g * 4 + q] + bias[j][g][q];
+                        put(wm * 128 + i * 32 + rr, wn * 128 + j * 32 + g * 8 + hk * 4, v);
+                    }
+            __syncthreads();
+            drain(256, [&](int r, int c, uint4 x) {
+                const int n = n0 + c;
+                if (n < p.N) {
+                    const long row = (MODE == MODE_ROWS) ? row_base + m0 + r : (long)(m0 + r);
+                    *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(p.C) + row * p.ldc + n) = x;
+                }
+            });
+        } else {
+            // pass 1: [H1 | H3] as columns 0-127 | 128-255; pass 2: A in columns 0-127
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float h1[4], h3[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) { h1[q] = acc[i][j][g * 4 + q]; h3[q] = acc[i][j + 2][g * 4 + q]; }
+                        const int c = wn * 64 + j * 32 + g * 8 + hk * 4;
+                        put(wm * 128 + i * 32 + rr, c, h1);
+                        put(wm * 128 + i * 32 + rr, 128 + c, h3);
+                    }
+            __syncthreads();
+            bf16* H = reinterpret_cast<bf16*>(p.C2);
+            drain(256, [&](int r, int c, uint4 x) {
+                const int hc = c & 127, hid = hid0 + hc;
+                if (hid < p.ffn) {
+                    const long row = row_base + m0 + r;
+                    *reinterpret_cast<uint4*>(H + row * (2L * p.ffn) + (c >= 128 ? p.ffn : 0) + hid) = x;
+                }
+            });
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float a[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) a[q] = siluf_(acc[i][j][g * 4 + q]) * acc[i][j + 2][g * 4 + q];
+                        put(wm * 128 + i * 32 + rr, wn * 64 + j * 32 + g * 8 + hk * 4, a);
+                    }
+            __syncthreads();
+            drain(128, [&](int r, int c, uint4 x) {
+                const int hid = hid0 + c;
+                if (hid < p.ffn) {
+                    const long row = row_base + m0 + r;
+                    *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(p.C) + row * (long)p.ffn + hid) = x;
+                }
+            });
+        }
+        return;
+    }
     const int rr = lane & 31, hk = lane >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
