@@ -75,6 +75,7 @@ struct GemmParams {
     const int32_t* offsets;
     const int32_t* tile_prefix;
     int mtiles_ub;
+    int kchunk;                   // KSEG without offsets: segment e is rows [e kchunk, (e+1) kchunk) of K
     int xcd_balance;              // deal each XCD a contiguous, equal share of the tiles
     void* C; void* C2; void* C3; long ldc; long ces;
     int c2_mstart;
@@ -261,6 +262,9 @@ gemm_bf16_kernel(GemmParams p) {
         if (p.offsets) {
             row_base = p.offsets[e];
             K = p.offsets[e + 1] - p.offsets[e];
+        } else if (p.kchunk > 0) {
+            row_base = (long)e * p.kchunk;
+            K = min(p.kchunk, p.K - (int)row_base);
         }
     } else {
         const int MT = (p.M + BM - 1) / BM;
@@ -759,16 +763,47 @@ hipError_t mfma_router_dx(const RouterGemmArgs& a, hipStream_t s) {
     return run<MODE_DENSE, false, true, EPI_STORE, true>(p, grid, s);
 }
 
+// dWg (E x d) = dl^T X over K = T tokens.  With a partial buffer the T rows are
+// split into nsplit chunks (KSEG segments without offsets) whose fp32 partial
+// products are then summed in chunk order; without one, a single segment.
+__global__ void __launch_bounds__(256) sum_partials_kernel(const float* part, float* out, long n4, int nsplit) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    float4 acc = reinterpret_cast<const float4*>(part)[i];
+    for (int s = 1; s < nsplit; ++s) {
+        const float4 v = reinterpret_cast<const float4*>(part)[(long)s * n4 + i];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    reinterpret_cast<float4*>(out)[i] = acc;
+}
+
+int router_dwg_splits(int T) {
+    int s = T / 2048;                     // each chunk keeps at least 2048 rows
+    return s < 1 ? 1 : (s > 16 ? 16 : s);
+}
+
 hipError_t mfma_router_dwg(const RouterGemmArgs& a, hipStream_t s) {
-    // dWg (E x d) = dl^T X: one K segment [0, T)
+    const int nsplit = a.dwg_part ? router_dwg_splits(a.T) : 1;
     GemmParams p = {};
-    p.E = 1; p.offsets = nullptr; p.K = a.T; p.b2_kstart = -1;
+    p.b2_kstart = -1;
     p.A = (const bf16*)a.dl; p.lda = a.E;
     p.B = (const bf16*)a.X; p.ldb = a.d;
-    p.M = a.E; p.N = a.d;
-    p.C = a.dWg; p.ldc = a.d; p.ces = 0;
-    const int grid = ((a.E + BM - 1) / BM) * ((a.d + BN - 1) / BN);
-    return run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
+    p.M = a.E; p.N = a.d; p.K = a.T;
+    p.ldc = a.d;
+    p.E = nsplit;
+    if (nsplit > 1) {
+        p.kchunk = ((a.T + nsplit - 1) / nsplit + BK - 1) / BK * BK;
+        p.C = a.dwg_part; p.ces = (long)a.E * a.d;
+    } else {
+        p.C = a.dWg; p.ces = 0;
+    }
+    const int grid = nsplit * ((a.E + BM - 1) / BM) * ((a.d + BN - 1) / BN);
+    hipError_t st = run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
+    if (st != hipSuccess || nsplit == 1) return st;
+    const long n4 = (long)a.E * a.d / 4;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       (const float*)a.dwg_part, a.dWg, n4, nsplit);
+    return hipGetLastError();
 }
 
 }  // namespace moe

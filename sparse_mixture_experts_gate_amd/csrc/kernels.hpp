@@ -155,7 +155,9 @@ struct RouterGemmArgs {
     int T, d, E;
     const void* X; const void* Wg; const void* dl;
     float* logits; float* dXr; float* dWg;
+    float* dwg_part;       // bf16 path: router_dwg_splits(T) x [E,d] fp32 partials, or NULL
 };
+int router_dwg_splits(int T);
 hipError_t simple_router_logits(const RouterGemmArgs& a, hipStream_t s);
 hipError_t simple_router_dx(const RouterGemmArgs& a, hipStream_t s);
 hipError_t simple_router_dwg(const RouterGemmArgs& a, hipStream_t s);

@@ -27,7 +27,7 @@ constexpr int kChunk = 64;
 
 enum WsBuf {
     B_XP = 0, B_H, B_A, B_EO, B_DEO, B_DH, B_DXP, B_DY, B_DXR, B_DL, B_DGATE, B_GATEOF,
-    B_HIST, B_CBASE, B_QPART, B_LPART, B_TPREFIX, B_COUNT
+    B_HIST, B_CBASE, B_QPART, B_LPART, B_TPREFIX, B_DWGPART, B_COUNT
 };
 
 struct Layout {
@@ -100,6 +100,9 @@ Layout layout(const moe_config* c) {
     sz[B_QPART] = nc * E * 4;
     sz[B_LPART] = (size_t)combine_loss_blocks(c->T) * 4;
     sz[B_TPREFIX] = 3 * (MOE_MAX_EXPERTS + 1) * 4;
+    // split-K partials of the router weight gradient (bf16 path only)
+    const int nsplit = c->dtype == MOE_DTYPE_F32 ? 0 : router_dwg_splits(c->T);
+    sz[B_DWGPART] = nsplit > 1 ? (size_t)nsplit * E * d * 4 : 0;
     size_t o = 0;
     for (int b = 0; b < B_COUNT; ++b) {
         L.off[b] = o;
@@ -214,7 +217,7 @@ int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_
     const moe_config* c = x.c;
     const bool f32 = c->dtype == MOE_DTYPE_F32;
     const int vec = c->d * esize(c) / 16;
-    RouterGemmArgs rg = {c->T, c->d, c->E, X, w->Wg, nullptr, r->logits, nullptr, nullptr};
+    RouterGemmArgs rg = {c->T, c->d, c->E, X, w->Wg, nullptr, r->logits, nullptr, nullptr, nullptr};
     TRY(x.mark(MOE_STAGE_ROUTER_LOGITS));
     TRY(f32 ? simple_router_logits(rg, x.s) : mfma_router_logits(rg, x.s));
     TRY(x.mark(MOE_STAGE_ROUTE));
@@ -273,7 +276,8 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
     TRY(x.mark(MOE_STAGE_ROUTER_BWD));
     TRY(launch_router_bwd(rb, c->dtype, x.s));
     RouterGemmArgs rg = {c->T, c->d, c->E, X, w->Wg, x.buf<void>(B_DL), nullptr,
-                         x.buf<float>(B_DXR), g->dWg};
+                         x.buf<float>(B_DXR), g->dWg,
+                         router_dwg_splits(c->T) > 1 ? x.buf<float>(B_DWGPART) : nullptr};
     TRY(x.mark(MOE_STAGE_ROUTER_DWG));
     TRY(f32 ? simple_router_dwg(rg, x.s) : mfma_router_dwg(rg, x.s));
     TRY(x.mark(MOE_STAGE_ROUTER_DX));
