@@ -11,7 +11,10 @@
 // One kernel template covers every contraction:
 //   * workgroup tile 256 x 256, k-tiles of 32, 256 threads = 4 wavefronts in a
 //     2 x 2 grid, each wavefront a 128 x 128 block of 4 x 4 MFMA 32x32x16 tiles
-//     with fp32 accumulators;
+//     with fp32 accumulators; the last m-tile of an expert with at most 128
+//     (64) valid rows puts the 4 wavefronts side by side on 64 columns each,
+//     4 x 2 (2 x 2) MFMA tiles, so that it costs a fraction of a full tile's
+//     MFMA work;
 //   * every operand goes straight from global memory into LDS (buffer loads
 //     with an LDS destination, bounds checked by the buffer descriptor so
 //     ragged rows and k tails read as zero) through a ring of 4 LDS stages,
@@ -158,9 +161,9 @@ __device__ __forceinline__ void dma_one(const OpPlan& o, int i, uint32_t t, int 
         const int row0 = DIRECT_ROWS * j;
         int rowbase = row0;
         rsrc_t r = o.r0;
-        if (o.paired) {
-            rowbase = ((row0 >> 7) << 6) + (row0 & 63);
-            if ((row0 >> 6) & 1) r = o.r1;
+        if (o.paired) {      // tile rows alternate 32 W1 rows and the 32 W3 rows of the same units
+            rowbase = ((row0 >> 6) << 5) + (row0 & 31);
+            if ((row0 >> 5) & 1) r = o.r1;
         }
         dma16(r, t + j * 1024, o.vo[i & 1], (uint32_t)rowbase * o.ld_bytes + (uint32_t)k0 * 2u);
     }
@@ -183,6 +186,7 @@ __device__ __forceinline__ bf16x8 read_strided(const bf16* T, int colbase, int k
     return __builtin_bit_cast(bf16x8, v);
 }
 struct Frags { bf16x8 a[4], b[4]; };
+template <int I, int J> struct Layout { static constexpr int NI = I, NJ = J; };
 __device__ __forceinline__ bf16x8 read_contig(const bf16* T, int rowbase, int ks) {
     const int lane = threadIdx.x & 63;
     const int rr = lane & 31, hk = lane >> 5;
@@ -336,296 +340,290 @@ gemm_bf16_kernel(GemmParams p) {
         if (q < IPW_A) dma_one<AT>(pa, q, lds_base + st, kt * BK, wave);
         else dma_one<BT>(pb, q - IPW_A, lds_base + st + TILE_ELEMS * 2, kt * BK, wave);
     };
-    auto read_one = [&](const bf16* As, const bf16* Bs, int ks, Frags& f, int idx) {
-        if (idx < 4) f.a[idx] = AT ? read_strided(As, wm * 128 + idx * 32, ks) : read_contig(As, wm * 128 + idx * 32, ks);
-        else f.b[idx - 4] = BT ? read_strided(Bs, wn * 128 + (idx - 4) * 32, ks) : read_contig(Bs, wn * 128 + (idx - 4) * 32, ks);
-    };
-    auto mfma_one = [&](const Frags& f, int i) {
-        acc[i >> 2][i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[i & 3], f.a[i >> 2], acc[i >> 2][i & 3], 0, 0, 0);
-    };
+    const int rr = lane & 31, hk = lane >> 5;
 
-    if (nk > 0) {
+    // The main loop and epilogue for one wave layout (NI x NJ MFMA blocks per wave):
+    // 4 x 4 with the waves in a 2 x 2 grid of 128 x 128; for row tiles with at most 128
+    // (64) valid rows, 4 x 2 (2 x 2) with the waves side by side on 64 columns each, so
+    // that a short tail tile costs a fraction of the MFMA work of a full one.
+    auto tile = [&](auto lay) {
+        constexpr int NI = decltype(lay)::NI, NJ = decltype(lay)::NJ;
+        constexpr int NMF = NI * NJ;                   // MFMA slots per k-step
+        constexpr int NR = NI + NJ;                    // fragment reads per k-step
+        const int rb = (NJ == 4) ? wm * 128 : 0;       // first row / column of the wave
+        const int cb = (NJ == 4) ? wn * 128 : wave * 64;
+        auto read_one = [&](const bf16* As, const bf16* Bs, int ks, Frags& f, int idx) {
+            if (idx < NI) f.a[idx] = AT ? read_strided(As, rb + idx * 32, ks) : read_contig(As, rb + idx * 32, ks);
+            else f.b[idx - NI] = BT ? read_strided(Bs, cb + (idx - NI) * 32, ks) : read_contig(Bs, cb + (idx - NI) * 32, ks);
+        };
+        auto mfma_one = [&](const Frags& f, int i) {
+            const int ii = i / NJ, jj = i % NJ;
+            acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[jj], f.a[ii], acc[ii][jj], 0, 0, 0);
+        };
+
+        if (nk > 0) {
 #pragma unroll
-        for (int t = 0; t < DIST; ++t)
+            for (int t = 0; t < DIST; ++t)
 #pragma unroll
-            for (int q = 0; q < LPW; ++q) dma(q, t);
-        wait_vm<LPW * (DIST - 1)>();
-        __syncthreads();
-        Frags fa, fb;
+                for (int q = 0; q < LPW; ++q) dma(q, t);
+            wait_vm<LPW * (DIST - 1)>();
+            __syncthreads();
+            Frags fa, fb;
 #pragma unroll
-        for (int idx = 0; idx < 8; ++idx) read_one(lds[0][0], lds[0][1], 0, fa, idx);
-        for (int kt = 0; kt < nk; ++kt) {
-            const int st = kt % NS;
-            const bf16* As = lds[st][0];
-            const bf16* Bs = lds[st][1];
-            const int pf = kt + DIST;
+            for (int idx = 0; idx < NR; ++idx) read_one(lds[0][0], lds[0][1], 0, fa, idx);
+            for (int kt = 0; kt < nk; ++kt) {
+                const int st = kt % NS;
+                const bf16* As = lds[st][0];
+                const bf16* Bs = lds[st][1];
+                const int pf = kt + DIST;
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                Frags& cur = (s & 1) ? fb : fa;
-                Frags& nxt = (s & 1) ? fa : fb;
-                if (s + 1 < KSTEPS) {
-                    // 16 slots: MFMA i, then fragment i of step s+1 (slots 0-7) or a load (8-15)
+                for (int s = 0; s < KSTEPS; ++s) {
+                    Frags& cur = (s & 1) ? fb : fa;
+                    Frags& nxt = (s & 1) ? fa : fb;
+                    if (s + 1 < KSTEPS) {
+                        // slot i: MFMA i, then fragment i of step s+1 and/or one load of k-tile pf
+                        constexpr int lo = (NMF >= NR + PART) ? NR : NMF - PART;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        mfma_one(cur, i);
-                        if (i < 8) read_one(As, Bs, s + 1, nxt, i);
-                        else if (i - 8 < PART) dma(s * PART + i - 8, pf);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                } else {
-                    // last step: loads under the first half, then publish tile kt+1 and read
-                    // its first fragments under the second half
+                        for (int i = 0; i < NMF; ++i) {
+                            mfma_one(cur, i);
+                            if (i < NR) read_one(As, Bs, s + 1, nxt, i);
+                            if (i >= lo && i - lo < PART) dma(s * PART + i - lo, pf);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    } else {
+                        // last step: loads under the first half, then publish tile kt+1 and
+                        // read its first fragments under the second half
+                        constexpr int h1 = NMF / 2;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        mfma_one(cur, i);
-                        if (i < PART) dma(s * PART + i, pf);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                    wait_vm<LPW * (DIST - 1)>();
-                    wait_lgkm0();
-                    __syncthreads();
-                    const int sn = (kt + 1) % NS;
+                        for (int i = 0; i < h1; ++i) {
+                            mfma_one(cur, i);
 #pragma unroll
-                    for (int i = 8; i < 16; ++i) {
-                        mfma_one(cur, i);
-                        read_one(lds[sn][0], lds[sn][1], 0, nxt, i - 8);
-                        __builtin_amdgcn_sched_barrier(0);
+                            for (int q = i * PART / h1; q < (i + 1) * PART / h1; ++q) dma(s * PART + q, pf);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        wait_vm<LPW * (DIST - 1)>();
+                        wait_lgkm0();
+                        __syncthreads();
+                        const int sn = (kt + 1) % NS;
+#pragma unroll
+                        for (int i = h1; i < NMF; ++i) {
+                            mfma_one(cur, i);
+#pragma unroll
+                            for (int idx = (i - h1) * NR / (NMF - h1); idx < (i - h1 + 1) * NR / (NMF - h1); ++idx)
+                                read_one(lds[sn][0], lds[sn][1], 0, nxt, idx);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
                     }
                 }
             }
+            wait_vm<0>();
         }
-        wait_vm<0>();
-    }
 
-    // ---- epilogue ----------------------------------------------------------------------
-    if constexpr (EPI == EPI_STORE && OUT_F32) {
-        // fp32 tile written out through LDS in two passes of 128 rows: each pass the two
-        // wavefronts that own those rows put their accumulators in LDS as 1 KB rows (16-byte
-        // chunk q of row r at chunk q ^ (r & 63)), then all 256 threads store whole rows
-        float* stage = reinterpret_cast<float*>(&lds[0][0][0]);
-        __syncthreads();                                   // every wave is past its last LDS read
-        const int rr = lane & 31, hk = lane >> 5;
-        const int qt = tid & 63;
-        for (int pass = 0; pass < 2; ++pass) {
-            if (wm == pass) {
+        // ---- epilogue ------------------------------------------------------------------
+        if constexpr (EPI == EPI_STORE && OUT_F32) {
+            // fp32 tile written out through LDS in two passes of 128 rows: each pass the
+            // wavefronts that own those rows put their accumulators in LDS as 1 KB rows
+            // (16-byte chunk q of row r at chunk q ^ (r & 63)), then all 256 threads store
+            // whole rows
+            float* stage = reinterpret_cast<float*>(&lds[0][0][0]);
+            __syncthreads();                                   // every wave is past its last LDS read
+            const int qt = tid & 63;
+            const int npass = rows_valid > 128 ? 2 : 1;
+            for (int pass = 0; pass < npass; ++pass) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = i * 32 + rr;
+                for (int i = 0; i < NI; ++i) {
+                    const int r = rb + i * 32 + rr - pass * 128;
+                    if ((rb + i * 32) / 128 != pass) continue;   // wave-uniform
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < NJ; ++j)
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
-                            const int q = wn * 32 + j * 8 + g * 2 + hk;
+                            const int q = (cb + j * 32 + g * 8 + hk * 4) >> 2;
                             *reinterpret_cast<float4*>(stage + r * 256 + ((q ^ (r & 63)) << 2)) =
                                 make_float4(acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
                                             acc[i][j][g * 4 + 3]);
                         }
                 }
-            }
-            __syncthreads();
-            const int n = n0 + qt * 4;
-            float b[4] = {0.f, 0.f, 0.f, 0.f};
-            if (p.bias && n < p.N) load4(p.bias + (long)e * p.bias_es + n, b);
+                __syncthreads();
+                const int n = n0 + qt * 4;
+                float b[4] = {0.f, 0.f, 0.f, 0.f};
+                if (p.bias && n < p.N) load4(p.bias + (long)e * p.bias_es + n, b);
 #pragma unroll 4
-            for (int it = 0; it < 32; ++it) {
-                const int r = it * 4 + (tid >> 6);
-                const int ml = pass * 128 + r;
-                const float4 x = *reinterpret_cast<const float4*>(stage + r * 256 + ((qt ^ (r & 63)) << 2));
-                if (ml < rows_valid && n < p.N) {
-                    const float v[4] = {x.x + b[0], x.y + b[1], x.z + b[2], x.w + b[3]};
-                    const long row = (MODE == MODE_ROWS) ? row_base + m0 + ml : (long)(m0 + ml);
-                    if (MODE == MODE_KSEG) {
-                        void* base = p.C;
-                        long m = row;
-                        if (p.C2 && m >= p.c2_mstart) { base = p.C2; m -= p.c2_mstart; }
-                        store4(reinterpret_cast<float*>(base) + (long)e * p.ces + m * p.ldc + n, v);
-                    } else {
-                        store4(reinterpret_cast<float*>(p.C) + row * p.ldc + n, v);
+                for (int it = 0; it < 32; ++it) {
+                    const int r = it * 4 + (tid >> 6);
+                    const int ml = pass * 128 + r;
+                    const float4 x = *reinterpret_cast<const float4*>(stage + r * 256 + ((qt ^ (r & 63)) << 2));
+                    if (ml < rows_valid && n < p.N) {
+                        const float v[4] = {x.x + b[0], x.y + b[1], x.z + b[2], x.w + b[3]};
+                        const long row = (MODE == MODE_ROWS) ? row_base + m0 + ml : (long)(m0 + ml);
+                        if (MODE == MODE_KSEG) {
+                            void* base = p.C;
+                            long m = row;
+                            if (p.C2 && m >= p.c2_mstart) { base = p.C2; m -= p.c2_mstart; }
+                            store4(reinterpret_cast<float*>(base) + (long)e * p.ces + m * p.ldc + n, v);
+                        } else {
+                            store4(reinterpret_cast<float*>(p.C) + row * p.ldc + n, v);
+                        }
                     }
                 }
+                __syncthreads();
             }
-            __syncthreads();
+            return;
         }
-        return;
-    }
-    if constexpr ((EPI == EPI_STORE || EPI == EPI_UP_SWIGLU) && !OUT_F32) {
-        // bf16 tile written out through LDS: 512-byte rows of 32 chunks, chunk q of row r at
-        // q ^ (r & 31); each lane puts its 4 consecutive columns (8 bytes) in place, then the
-        // 256 threads store whole rows with 16-byte vectors
-        bf16* stage = &lds[0][0][0];
-        __syncthreads();
-        const int rr = lane & 31, hk = lane >> 5;
-        auto put = [&](int r, int c, const float* v) {      // c: first of 4 columns
-            const int q = c >> 3;
-            store4(stage + r * 256 + ((q ^ (r & 31)) << 3) + (c & 7), v);
-        };
-        // stage columns [c_lo, c_lo + ncols) of rows 0..255, store row r's columns to dst(r, c)
-        auto drain = [&](int ncols, auto dst) {
-            const int cpr = ncols / 8;                       // 16-byte chunks per row
-            const int rows_per_it = 256 / cpr;
-            const int q = tid % cpr;
-            for (int r = tid / cpr; r < 256; r += rows_per_it) {
-                const uint4 x = *reinterpret_cast<const uint4*>(stage + r * 256 + ((q ^ (r & 31)) << 3));
-                if (r < rows_valid) dst(r, q * 8, x);
-            }
-        };
-        if constexpr (EPI == EPI_STORE) {
-            float bias[4][4][4];
+        if constexpr ((EPI == EPI_STORE || EPI == EPI_UP_SWIGLU) && !OUT_F32) {
+            // bf16 tile written out through LDS: 512-byte rows of 32 chunks, chunk q of row r
+            // at q ^ (r & 31); each lane puts its 4 consecutive columns (8 bytes) in place,
+            // then the 256 threads store whole rows with 16-byte vectors
+            bf16* stage = &lds[0][0][0];
+            __syncthreads();
+            auto put = [&](int r, int c, const float* v) {      // c: first of 4 columns
+                const int q = c >> 3;
+                store4(stage + r * 256 + ((q ^ (r & 31)) << 3) + (c & 7), v);
+            };
+            // store the first ncols staged columns of every valid row to dst(r, c, 16 bytes)
+            auto drain = [&](int ncols, auto dst) {
+                const int cpr = ncols / 8;                       // 16-byte chunks per row
+                const int rows_per_it = 256 / cpr;
+                const int q = tid % cpr;
+                for (int r = tid / cpr; r < rows_valid; r += rows_per_it) {
+                    const uint4 x = *reinterpret_cast<const uint4*>(stage + r * 256 + ((q ^ (r & 31)) << 3));
+                    dst(r, q * 8, x);
+                }
+            };
+            if constexpr (EPI == EPI_STORE) {
+                float bias[NJ][4][4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int n = n0 + cb + j * 32 + g * 8 + hk * 4;
+                        if (p.bias && n < p.N) load4(p.bias + (long)e * p.bias_es + n, bias[j][g]);
+                        else bias[j][g][0] = bias[j][g][1] = bias[j][g][2] = bias[j][g][3] = 0.f;
+                    }
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            float v[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) v[q] = acc[i][j][g * 4 + q] + bias[j][g][q];
+                            put(rb + i * 32 + rr, cb + j * 32 + g * 8 + hk * 4, v);
+                        }
+                __syncthreads();
+                drain(256, [&](int r, int c, uint4 x) {
+                    const int n = n0 + c;
+                    if (n < p.N) {
+                        const long row = (MODE == MODE_ROWS) ? row_base + m0 + r : (long)(m0 + r);
+                        *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(p.C) + row * p.ldc + n) = x;
+                    }
+                });
+            } else {
+                // tile columns (B rows) alternate 32 W1 rows and the 32 W3 rows of the same
+                // hidden units, so MFMA blocks j and j+1 (j even) pair H1 with H3.
+                // Pass 1: [H1 | H3] staged as columns 0-127 | 128-255; pass 2: A in 0-127.
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; j += 2)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            float h1[4], h3[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) { h1[q] = acc[i][j][g * 4 + q]; h3[q] = acc[i][j + 1][g * 4 + q]; }
+                            const int c = ((cb + j * 32) >> 6) * 32 + g * 8 + hk * 4;
+                            put(rb + i * 32 + rr, c, h1);
+                            put(rb + i * 32 + rr, 128 + c, h3);
+                        }
+                __syncthreads();
+                bf16* H = reinterpret_cast<bf16*>(p.C2);
+                drain(256, [&](int r, int c, uint4 x) {
+                    const int hc = c & 127, hid = hid0 + hc;
+                    if (hid < p.ffn) {
+                        const long row = row_base + m0 + r;
+                        *reinterpret_cast<uint4*>(H + row * (2L * p.ffn) + (c >= 128 ? p.ffn : 0) + hid) = x;
+                    }
+                });
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; j += 2)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            float a[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) a[q] = siluf_(acc[i][j][g * 4 + q]) * acc[i][j + 1][g * 4 + q];
+                            put(rb + i * 32 + rr, ((cb + j * 32) >> 6) * 32 + g * 8 + hk * 4, a);
+                        }
+                __syncthreads();
+                drain(128, [&](int r, int c, uint4 x) {
+                    const int hid = hid0 + c;
+                    if (hid < p.ffn) {
+                        const long row = row_base + m0 + r;
+                        *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(p.C) + row * (long)p.ffn + hid) = x;
+                    }
+                });
+            }
+            return;
+        }
+        // MLP forward and the activation backward: straight from the accumulator layout
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int ml = rb + i * 32 + rr;               // local row
+            if (ml >= rows_valid) continue;
+            const long row = (MODE == MODE_ROWS) ? row_base + m0 + ml : (long)(m0 + ml);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wn * 128 + j * 32 + g * 8 + hk * 4;
-                    if (p.bias && n < p.N) load4(p.bias + (long)e * p.bias_es + n, bias[j][g]);
-                    else bias[j][g][0] = bias[j][g][1] = bias[j][g][2] = bias[j][g][3] = 0.f;
-                }
+                    float v[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        float v[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][g * 4 + q] + bias[j][g][q];
-                        put(wm * 128 + i * 32 + rr, wn * 128 + j * 32 + g * 8 + hk * 4, v);
-                    }
-            __syncthreads();
-            drain(256, [&](int r, int c, uint4 x) {
-                const int n = n0 + c;
-                if (n < p.N) {
-                    const long row = (MODE == MODE_ROWS) ? row_base + m0 + r : (long)(m0 + r);
-                    *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(p.C) + row * p.ldc + n) = x;
-                }
-            });
-        } else {
-            // pass 1: [H1 | H3] as columns 0-127 | 128-255; pass 2: A in columns 0-127
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        float h1[4], h3[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) { h1[q] = acc[i][j][g * 4 + q]; h3[q] = acc[i][j + 2][g * 4 + q]; }
-                        const int c = wn * 64 + j * 32 + g * 8 + hk * 4;
-                        put(wm * 128 + i * 32 + rr, c, h1);
-                        put(wm * 128 + i * 32 + rr, 128 + c, h3);
-                    }
-            __syncthreads();
-            bf16* H = reinterpret_cast<bf16*>(p.C2);
-            drain(256, [&](int r, int c, uint4 x) {
-                const int hc = c & 127, hid = hid0 + hc;
-                if (hid < p.ffn) {
-                    const long row = row_base + m0 + r;
-                    *reinterpret_cast<uint4*>(H + row * (2L * p.ffn) + (c >= 128 ? p.ffn : 0) + hid) = x;
-                }
-            });
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        float a[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) a[q] = siluf_(acc[i][j][g * 4 + q]) * acc[i][j + 2][g * 4 + q];
-                        put(wm * 128 + i * 32 + rr, wn * 64 + j * 32 + g * 8 + hk * 4, a);
-                    }
-            __syncthreads();
-            drain(128, [&](int r, int c, uint4 x) {
-                const int hid = hid0 + c;
-                if (hid < p.ffn) {
-                    const long row = row_base + m0 + r;
-                    *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(p.C) + row * (long)p.ffn + hid) = x;
-                }
-            });
-        }
-        return;
-    }
-    const int rr = lane & 31, hk = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ml = wm * 128 + i * 32 + rr;       // local row
-        if (ml >= rows_valid) continue;
-        const long row = (MODE == MODE_ROWS) ? row_base + m0 + ml : (long)(m0 + ml);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float v[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] = acc[i][j][g * 4 + q];
-                const int nl = wn * 128 + j * 32 + g * 8 + hk * 4;    // first of 4 local cols
-                if (EPI == EPI_UP_SWIGLU) {
-                    if (j >= 2) continue;
-                    const int hid = hid0 + wn * 64 + j * 32 + g * 8 + hk * 4;
-                    if (hid >= p.ffn) continue;
-                    float h3[4], a[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        h3[q] = acc[i][j + 2][g * 4 + q];
-                        a[q] = siluf_(v[q]) * h3[q];
-                    }
-                    bf16* H = reinterpret_cast<bf16*>(p.C2);
-                    store4(H + row * (2L * p.ffn) + hid, v);
-                    store4(H + row * (2L * p.ffn) + p.ffn + hid, h3);
-                    store4(reinterpret_cast<bf16*>(p.C) + row * (long)p.ffn + hid, a);
-                    continue;
-                }
-                const int n = n0 + nl;
-                if (n >= p.N) continue;
-                if (EPI == EPI_UP_RELU || EPI == EPI_UP_GELU) {
-                    float b[4], a[4];
-                    load4(p.bias + (long)e * p.bias_es + n, b);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        v[q] += b[q];
-                        a[q] = (EPI == EPI_UP_RELU) ? fmaxf(v[q], 0.f) : geluf_(v[q]);
-                    }
-                    store4(reinterpret_cast<bf16*>(p.C2) + row * p.ldc + n, v);
-                    store4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + n, a);
-                } else if (EPI == EPI_DN_SWIGLU) {
-                    float h1[4], h3[4], d1[4], d3[4];
-                    load4(p.H + row * p.ldh + n, h1);
-                    load4(p.H + row * p.ldh + p.ffn + n, h3);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        d1[q] = v[q] * h3[q] * silu_gradf_(h1[q]);
-                        d3[q] = v[q] * siluf_(h1[q]);
-                    }
-                    bf16* dH = reinterpret_cast<bf16*>(p.C);
-                    store4(dH + row * p.ldc + n, d1);
-                    store4(dH + row * p.ldc + p.ffn + n, d3);
-                } else if (EPI == EPI_DN_RELU || EPI == EPI_DN_GELU) {
-                    float h[4];
-                    load4(p.H + row * p.ldh + n, h);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        v[q] *= (EPI == EPI_DN_RELU) ? (h[q] > 0.f ? 1.f : 0.f) : gelu_gradf_(h[q]);
-                    store4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + n, v);
-                } else {   // EPI_STORE
-                    if (p.bias) {
-                        float b[4];
+                    for (int q = 0; q < 4; ++q) v[q] = acc[i][j][g * 4 + q];
+                    const int n = n0 + cb + j * 32 + g * 8 + hk * 4;    // first of 4 columns
+                    if (n >= p.N) continue;
+                    if (EPI == EPI_UP_RELU || EPI == EPI_UP_GELU) {
+                        float b[4], a[4];
                         load4(p.bias + (long)e * p.bias_es + n, b);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) v[q] += b[q];
-                    }
-                    if (MODE == MODE_KSEG) {
-                        void* base = p.C;
-                        long m = row;
-                        if (p.C2 && m >= p.c2_mstart) { base = p.C2; m -= p.c2_mstart; }
-                        store4(reinterpret_cast<float*>(base) + (long)e * p.ces + m * p.ldc + n, v);
-                    } else if (OUT_F32) {
-                        store4(reinterpret_cast<float*>(p.C) + row * p.ldc + n, v);
-                    } else {
+                        for (int q = 0; q < 4; ++q) {
+                            v[q] += b[q];
+                            a[q] = (EPI == EPI_UP_RELU) ? fmaxf(v[q], 0.f) : geluf_(v[q]);
+                        }
+                        store4(reinterpret_cast<bf16*>(p.C2) + row * p.ldc + n, v);
+                        store4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + n, a);
+                    } else if (EPI == EPI_DN_SWIGLU) {
+                        float h1[4], h3[4], d1[4], d3[4];
+                        load4(p.H + row * p.ldh + n, h1);
+                        load4(p.H + row * p.ldh + p.ffn + n, h3);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            d1[q] = v[q] * h3[q] * silu_gradf_(h1[q]);
+                            d3[q] = v[q] * siluf_(h1[q]);
+                        }
+                        bf16* dH = reinterpret_cast<bf16*>(p.C);
+                        store4(dH + row * p.ldc + n, d1);
+                        store4(dH + row * p.ldc + p.ffn + n, d3);
+                    } else if (EPI == EPI_DN_RELU || EPI == EPI_DN_GELU) {
+                        float h[4];
+                        load4(p.H + row * p.ldh + n, h);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            v[q] *= (EPI == EPI_DN_RELU) ? (h[q] > 0.f ? 1.f : 0.f) : gelu_gradf_(h[q]);
                         store4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + n, v);
                     }
                 }
             }
         }
+    };
+
+    if constexpr (MODE == MODE_ROWS) {
+        if (rows_valid <= 64) tile(Layout<2, 2>{});
+        else if (rows_valid <= 128) tile(Layout<4, 2>{});
+        else tile(Layout<4, 4>{});
+    } else {
+        tile(Layout<4, 4>{});
     }
 }
 
