@@ -23,26 +23,29 @@ __device__ __forceinline__ void load_slots(const int32_t* slot_of, int t, int k,
     for (int i = 0; i < MOE_MAX_K; ++i) sl[i] = (i < k) ? slot_of[(size_t)t * k + i] : 0;
 }
 
-template <class T>
+// KT > 0: k known at compile time, so the loops over the k expert rows unroll and
+// all k loads of a vector are in flight together; KT == 0: any k.
+template <class T, int KT>
 __global__ void __launch_bounds__(256) gather_kernel(GatherArgs a) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * TOK_WAVES + (threadIdx.x >> 6);
     if (t >= a.T) return;
-    int sl[MOE_MAX_K];
-    load_slots(a.slot_of, t, a.k, sl);
+    const int k = KT > 0 ? KT : a.k;
+        int sl[MOE_MAX_K];
+    load_slots(a.slot_of, t, k, sl);
     const uint4* src = reinterpret_cast<const uint4*>(a.X) + (size_t)t * a.vec;
     uint4* dst = reinterpret_cast<uint4*>(a.Xp);
     for (int v = lane; v < a.vec; v += 64) {
         uint4 x = src[v];
 #pragma unroll
         for (int i = 0; i < MOE_MAX_K; ++i) {
-            if (i >= a.k) break;
+            if (i >= k) break;
             dst[(size_t)sl[i] * a.vec + v] = x;
         }
     }
 }
 
-template <class T, bool LOSS>
+template <class T, bool LOSS, int KT>
 __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     __shared__ float s_part[TOK_WAVES];
     constexpr int N = Vec16<T>::N;
@@ -50,11 +53,12 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     const int t = blockIdx.x * TOK_WAVES + wave;
     float sq = 0.f;
     if (t < a.T) {
+        const int k = KT > 0 ? KT : a.k;
         int sl[MOE_MAX_K];
         float g[MOE_MAX_K];
-        load_slots(a.slot_of, t, a.k, sl);
+        load_slots(a.slot_of, t, k, sl);
 #pragma unroll
-        for (int i = 0; i < MOE_MAX_K; ++i) g[i] = (i < a.k) ? a.gates[(size_t)t * a.k + i] : 0.f;
+        for (int i = 0; i < MOE_MAX_K; ++i) g[i] = (i < k) ? a.gates[(size_t)t * k + i] : 0.f;
         const uint4* eo = reinterpret_cast<const uint4*>(a.EO);
         for (int v = lane; v < a.vec; v += 64) {
             float acc[N];
@@ -62,7 +66,7 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
             for (int j = 0; j < N; ++j) acc[j] = 0.f;
 #pragma unroll
             for (int i = 0; i < MOE_MAX_K; ++i) {
-                if (i >= a.k) break;
+                if (i >= k) break;
                 float x[N];
                 Vec16<T>::unpack(eo[(size_t)sl[i] * a.vec + v], x);
 #pragma unroll
@@ -95,18 +99,19 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     }
 }
 
-template <class T>
+template <class T, int KT>
 __global__ void __launch_bounds__(256) combine_bwd_kernel(CombineBwdArgs a) {
     constexpr int N = Vec16<T>::N;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * TOK_WAVES + (threadIdx.x >> 6);
     if (t >= a.T) return;
-    int sl[MOE_MAX_K];
+    const int k = KT > 0 ? KT : a.k;
+        int sl[MOE_MAX_K];
     float g[MOE_MAX_K], dg[MOE_MAX_K];
-    load_slots(a.slot_of, t, a.k, sl);
+    load_slots(a.slot_of, t, k, sl);
 #pragma unroll
     for (int i = 0; i < MOE_MAX_K; ++i) {
-        g[i] = (i < a.k) ? a.gates[(size_t)t * a.k + i] : 0.f;
+        g[i] = (i < k) ? a.gates[(size_t)t * k + i] : 0.f;
         dg[i] = 0.f;
     }
     const uint4* dy4 = reinterpret_cast<const uint4*>(a.dY) + (size_t)t * a.vec;
@@ -117,7 +122,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(CombineBwdArgs a) {
         Vec16<T>::unpack(dy4[v], dy);
 #pragma unroll
         for (int i = 0; i < MOE_MAX_K; ++i) {
-            if (i >= a.k) break;
+            if (i >= k) break;
             float x[N], o[N];
             const size_t r = (size_t)sl[i] * a.vec + v;
             Vec16<T>::unpack(eo[r], x);
@@ -131,20 +136,21 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(CombineBwdArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < MOE_MAX_K; ++i) {
-        if (i >= a.k) break;
+        if (i >= k) break;
         float s = wave_sum(dg[i]);
-        if (lane == 0) a.dgate[(size_t)t * a.k + i] = s;
+        if (lane == 0) a.dgate[(size_t)t * k + i] = s;
     }
 }
 
-template <class T>
+template <class T, int KT>
 __global__ void __launch_bounds__(256) scatter_kernel(ScatterArgs a) {
     constexpr int N = Vec16<T>::N;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * TOK_WAVES + (threadIdx.x >> 6);
     if (t >= a.T) return;
-    int sl[MOE_MAX_K];
-    load_slots(a.slot_of, t, a.k, sl);
+    const int k = KT > 0 ? KT : a.k;
+        int sl[MOE_MAX_K];
+    load_slots(a.slot_of, t, k, sl);
     const uint4* dxp = reinterpret_cast<const uint4*>(a.dXp);
     // router-path gradient is fp32 [T, d]: N floats per vector of T
     const float* dxr = a.dXr + (size_t)t * a.vec * N;
@@ -154,7 +160,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(ScatterArgs a) {
         for (int j = 0; j < N; ++j) acc[j] = 0.f;
 #pragma unroll
         for (int i = 0; i < MOE_MAX_K; ++i) {
-            if (i >= a.k) break;
+            if (i >= k) break;
             float x[N];
             Vec16<T>::unpack(dxp[(size_t)sl[i] * a.vec + v], x);
 #pragma unroll
@@ -238,34 +244,46 @@ __global__ void __launch_bounds__(256) sgd_kernel(SgdArgs a) {
 static inline dim3 tok_grid(int T) { return dim3((T + TOK_WAVES - 1) / TOK_WAVES); }
 int combine_loss_blocks(int T) { return (T + TOK_WAVES - 1) / TOK_WAVES; }
 
+// Launch KERNEL<..., KT> with KT = k for the common k, else KT = 0 (any k).
+#define MOE_LAUNCH_K(KERNEL, k, grid, s, a, ...)                                                  \
+    do {                                                                                          \
+        switch (k) {                                                                              \
+            case 2: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 2>), grid, dim3(256), 0, s, a); break; \
+            case 4: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 4>), grid, dim3(256), 0, s, a); break; \
+            case 6: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 6>), grid, dim3(256), 0, s, a); break; \
+            case 8: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 8>), grid, dim3(256), 0, s, a); break; \
+            default: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, 0>), grid, dim3(256), 0, s, a);        \
+        }                                                                                         \
+    } while (0)
+
 hipError_t launch_gather(const GatherArgs& a, int dtype, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
-    if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(gather_kernel<float>, tok_grid(a.T), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(gather_kernel<bf16>, tok_grid(a.T), dim3(256), 0, s, a);
+    if (dtype == MOE_DTYPE_F32) MOE_LAUNCH_K(gather_kernel, a.k, tok_grid(a.T), s, a, float);
+    else MOE_LAUNCH_K(gather_kernel, a.k, tok_grid(a.T), s, a, bf16);
     return hipGetLastError();
 }
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
     const bool loss = a.Yt != nullptr;
     if (dtype == MOE_DTYPE_F32) {
-        if (loss) hipLaunchKernelGGL((combine_kernel<float, true>), tok_grid(a.T), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((combine_kernel<float, false>), tok_grid(a.T), dim3(256), 0, s, a);
+        if (loss) MOE_LAUNCH_K(combine_kernel, a.k, tok_grid(a.T), s, a, float, true);
+        else MOE_LAUNCH_K(combine_kernel, a.k, tok_grid(a.T), s, a, float, false);
     } else {
-        if (loss) hipLaunchKernelGGL((combine_kernel<bf16, true>), tok_grid(a.T), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((combine_kernel<bf16, false>), tok_grid(a.T), dim3(256), 0, s, a);
+        if (loss) MOE_LAUNCH_K(combine_kernel, a.k, tok_grid(a.T), s, a, bf16, true);
+        else MOE_LAUNCH_K(combine_kernel, a.k, tok_grid(a.T), s, a, bf16, false);
     }
     return hipGetLastError();
 }
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, int dtype, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
-    if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(combine_bwd_kernel<float>, tok_grid(a.T), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(combine_bwd_kernel<bf16>, tok_grid(a.T), dim3(256), 0, s, a);
+    if (dtype == MOE_DTYPE_F32) MOE_LAUNCH_K(combine_bwd_kernel, a.k, tok_grid(a.T), s, a, float);
+    else MOE_LAUNCH_K(combine_bwd_kernel, a.k, tok_grid(a.T), s, a, bf16);
     return hipGetLastError();
 }
 hipError_t launch_scatter(const ScatterArgs& a, int dtype, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
-    if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(scatter_kernel<float>, tok_grid(a.T), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(scatter_kernel<bf16>, tok_grid(a.T), dim3(256), 0, s, a);
+    if (dtype == MOE_DTYPE_F32) MOE_LAUNCH_K(scatter_kernel, a.k, tok_grid(a.T), s, a, float);
+    else MOE_LAUNCH_K(scatter_kernel, a.k, tok_grid(a.T), s, a, bf16);
     return hipGetLastError();
 }
 hipError_t launch_colsum(const ColSumArgs& a, int dtype, hipStream_t s) {
