@@ -65,6 +65,29 @@ def stage_work(w):
 
 
 GEMM_STAGES = ("up_fwd", "down_fwd", "down_dgrad", "down_wgrad", "up_dgrad", "up_wgrad")
+PEAK_CLOCK_GHZ = 2.4           # the clock the published dense peak is quoted at
+
+
+def executed_gemm_flops(w, counts):
+    """MFMA work the expert GEMMs execute for these per-expert row counts.
+
+    Row-mode GEMMs (forward and dgrad) run 256-row tiles, and the last tile of an
+    expert runs 64, 128 or 256 rows (its narrower wave layouts); the weight
+    gradients run K = the expert's rows rounded up to the 32-row k-tile.  Returns
+    the executed flops per stage; ideal / executed is the tail-lane utilisation.
+    """
+    hc = 2 * w.ffn if w.expert == "swiglu" else w.ffn
+    d, ffn = w.d, w.ffn
+    rows_tile, rows_k = 0, 0
+    for c in counts:
+        c = int(c)
+        full, rem = divmod(c, 256)
+        tail = 0 if rem == 0 else (64 if rem <= 64 else 128 if rem <= 128 else 256)
+        rows_tile += full * 256 + tail
+        rows_k += -(-c // 32) * 32
+    return {"up_fwd": 2.0 * rows_tile * d * hc, "down_fwd": 2.0 * rows_tile * ffn * d,
+            "down_dgrad": 2.0 * rows_tile * d * ffn, "up_dgrad": 2.0 * rows_tile * hc * d,
+            "down_wgrad": 2.0 * rows_k * d * ffn, "up_wgrad": 2.0 * rows_k * hc * d}
 
 # source file of the kernels behind each stage (the HBM byte counts measured with
 # rocprofv3 hold only while that file is unchanged)
@@ -144,8 +167,8 @@ def cpu_baseline(w, inp, budget_s: float):
     return {"value": w.T / full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"float64 oracle: routing of all {w.T} tokens ({t_route:.1f} s) + expert "
                        f"forward/backward of {n_exp} whole expert segments ({rows} of {w.T * w.k} "
-                       f"rows, {t_exp:.1f} s), expert part scaled by rows; "
-                       f"estimated {full:.0f} s per step"),
+                       f"rows, {t_exp:.1f} s), expert part extrapolated to all rows by row count: "
+                       f"{full:.0f} s per step, extrapolated"),
             "seconds_measured": round(t_route + t_exp, 2)}
 
 
@@ -219,6 +242,12 @@ def main(argv=None) -> int:
         for s in L.STAGES:
             stage_ms[s].extend(ev.ms[s])
     avg = {s: sum(v) / len(v) for s, v in stage_ms.items()}
+    # GPU time of each whole step (first mark to last) and of its forward + backward
+    step_gpu = sorted(sum(stage_ms[s][i] for s in L.STAGES) for i in range(a.steps))
+    fb_gpu = sorted(sum(stage_ms[s][i] for s in L.STAGES if s != "sgd") for i in range(a.steps))
+
+    def pct(v, q):
+        return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
     work = stage_work(w)
     stages = {}
     for s in L.STAGES:
@@ -248,6 +277,8 @@ def main(argv=None) -> int:
                 "work_per_launch": n}
     gemm_ms = sum(avg[s] for s in GEMM_STAGES)
     gemm_flop = sum(work[s][1] for s in GEMM_STAGES)
+    counts = r["counts"].cpu().tolist()
+    exec_flop = executed_gemm_flops(w, counts) if w.dtype == "bf16" else None
     fwd_bwd_ms = sum(avg[s] for s in L.STAGES if s != "sgd")
     ms_per_step = elapsed / a.steps * 1e3
     out = {
@@ -270,6 +301,13 @@ def main(argv=None) -> int:
         "fwd_bwd_tokens_per_s": round(w.T / (fwd_bwd_ms * 1e-3), 1),
         "expert_gemm_tflops": round(gemm_flop / (gemm_ms * 1e-3) / 1e12, 2),
         "expert_gemm_frac_peak": round(gemm_flop / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "expert_gemm_peak": {"tflops": PEAK_BF16_TFLOPS, "clock_ghz": PEAK_CLOCK_GHZ},
+        "expert_gemm_executed_frac_peak": (None if exec_flop is None else round(
+            sum(exec_flop.values()) / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)),
+        "expert_gemm_tail_utilisation": (None if exec_flop is None else round(
+            gemm_flop / sum(exec_flop.values()), 4)),
+        "step_gpu_ms": {"median": round(pct(step_gpu, 0.5), 3), "p90": round(pct(step_gpu, 0.9), 3)},
+        "fwd_bwd_gpu_ms": {"median": round(pct(fb_gpu, 0.5), 3), "p90": round(pct(fb_gpu, 0.9), 3)},
         "dispatch_gbps": stages["gather"].get("gbs"),
         "combine_gbps": stages["combine_loss"].get("gbs"),
         "stages": stages,
