@@ -16,6 +16,14 @@ Kernel time per kernel, from one kernel-trace run:
     python -m sparse_mixture_experts_gate_amd.profile_summary --stats OUT/trace/kt_kernel_stats.csv \\
         --steps 7 --markdown M --command "..."
 
+MFMA utilisation and clock per GEMM stage, from one counter run:
+
+    rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 \\
+        SQ_INSTS_MFMA SQ_CYCLES GRBM_GUI_ACTIVE -d OUT/mfma -o mfma --output-format csv -- \\
+        python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline
+    python -m sparse_mixture_experts_gate_amd.profile_summary --mfma OUT/mfma/mfma_counter_collection.csv \\
+        --markdown M --command "..."
+
 FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch.  Each is scaled by
 the factor that makes the known-size device copy (--copy-calibration-mib)
 read and write exactly its size.  The library's kernels of the one timed
@@ -185,9 +193,70 @@ def stats_markdown(path, steps, title, command):
     return "\n".join(lines) + "\n"
 
 
+N_XCD, N_CU, SIMD_PER_CU = 8, 256, 4
+PEAK_BF16_TFLOPS, PEAK_CLOCK_GHZ = 2500.0, 2.4
+
+
+def mfma_markdown(path, title, command):
+    """Per GEMM stage of the first traced step: executed MFMA flops (MOPS x 512), the
+    fraction of SIMD-cycles the MFMA pipe is busy, and the clock the chip held.
+
+    SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of every SIMD (it equals the number
+    of 32x32x16 MFMAs times their 32 cycles); SQ_BUSY_CU_CYCLES sums the busy cycles of
+    every CU; GRBM_GUI_ACTIVE sums the active cycles of the 8 XCDs, so GRBM / 8 over the
+    kernel's duration is the mean clock (SQ_CYCLES / 32 shader engines agrees).
+    """
+    per = {}
+    for r in csv.DictReader(open(path)):
+        d = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                   "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    state = {"stage": None, "wgrad": 0}
+    rows, started = [], False
+    for did in sorted(per):
+        d = per[did]
+        st = _stage_of(d["name"], state)
+        if st == "router_logits":
+            if started:
+                break
+            started = True
+        if not started or st is None:
+            continue
+        state["stage"] = st
+        if "gemm_bf16_kernel" not in d["name"]:
+            continue
+        secs = d["ns"] * 1e-9
+        flops = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        ghz = d.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD / d["ns"]
+        busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (SIMD_PER_CU * max(d.get("SQ_BUSY_CU_CYCLES", 1.0), 1.0))
+        tf = flops / secs / 1e12
+        rows.append((st, d["ns"] / 1e6, flops / 1e12, tf, tf / PEAK_BF16_TFLOPS, ghz,
+                     tf / (PEAK_BF16_TFLOPS * ghz / PEAK_CLOCK_GHZ), busy))
+    lines = [f"# {title}", "", "Command (repository root, one MI355X):", "", "```", command, "```", "",
+             "Executed flops count every MFMA issued (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), tail-tile",
+             "padding included.  The clock is GRBM_GUI_ACTIVE / 8 XCDs over the kernel's duration.",
+             "\"of peak\" divides by 2.5 PF (quoted at 2.4 GHz); \"of peak at clock\" by 2.5 PF x clock / 2.4 GHz.",
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES).", "",
+             "| stage | ms | executed TFLOP | TFLOP/s | of peak | clock (GHz) | of peak at clock | MFMA busy |",
+             "|---|---|---|---|---|---|---|---|"]
+    for st, ms, tfl, tf, fr, ghz, frc, busy in rows:
+        lines.append(f"| {st} | {ms:.3f} | {tfl:.3f} | {tf:.1f} | {fr:.3f} | {ghz:.2f} | {frc:.3f} | {busy:.3f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     if argv is None:
         argv = sys.argv[1:]
+    if argv and argv[0] == "--mfma":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("--mfma", required=True)
+        ap.add_argument("--workload", default="grouped_sigmoid_t32768_d7168_e256")
+        ap.add_argument("--markdown", required=True)
+        ap.add_argument("--command", default="")
+        a = ap.parse_args(argv)
+        open(a.markdown, "w").write(mfma_markdown(a.mfma, f"MFMA utilisation, training step, {a.workload}",
+                                                  a.command))
+        return 0
     if argv and argv[0] == "--stats":
         ap = argparse.ArgumentParser()
         ap.add_argument("--stats", required=True)
