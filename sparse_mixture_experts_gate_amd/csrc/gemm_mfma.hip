@@ -79,7 +79,7 @@ struct GemmParams {
     const int32_t* tile_prefix;
     int mtiles_ub;
     int kchunk;                   // KSEG without offsets: segment e is rows [e kchunk, (e+1) kchunk) of K
-    int xcd_balance;              // deal each XCD a contiguous, equal share of the tiles
+    int xcd_group;                // XCDs per tile group: 1, 2, 4 or 8 (see the tile deal)
     void* C; void* C2; void* C3; long ldc; long ces;
     int c2_mstart;
     const bf16* bias; long bias_es;
@@ -231,11 +231,19 @@ gemm_bf16_kernel(GemmParams p) {
     else nreal = ((p.M + BM - 1) / BM) * NT;
     nreal = uni(nreal);
     int L = blockIdx.x;
-    if (p.xcd_balance) {   // XCD x (= blockIdx % 8) takes a contiguous, equal share of the tiles
-        const int x = L & 7, i = L >> 3, q = nreal >> 3, r = nreal & 7;
-        if (i >= q + (x < r ? 1 : 0)) return;
-        L = x * q + min(x, r) + i;
-    } else if (L >= nreal) return;
+    {
+        // Workgroups are dealt to the 8 XCDs round-robin by blockIdx. The XCDs form 8/G groups
+        // of G; each group takes a contiguous, equal share of the tiles and deals it round-robin
+        // to its members. G = 8 spreads neighbouring tiles over every L2 (each operand row is
+        // fetched into all of them); G = 1 keeps them on one XCD (least fabric traffic, but the
+        // requests of the co-resident tiles crowd one L2).
+        const int G = p.xcd_group;
+        const int x = L & 7, i = L >> 3, g = x / G, u = x - g * G, ng = 8 / G;
+        const int q = nreal / ng, r = nreal - q * ng;
+        const int li = i * G + u;
+        if (li >= q + (g < r ? 1 : 0)) return;
+        L = g * q + min(g, r) + li;
+    }
 
     int e = 0, m0 = 0, n_t = 0;
     long row_base = 0;
@@ -629,9 +637,13 @@ gemm_bf16_kernel(GemmParams p) {
 
 // ---- host side -------------------------------------------------------------------------------
 template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32>
-static hipError_t run(const GemmParams& p, int grid, hipStream_t s) {
+static hipError_t run(GemmParams p, int grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
-    grid = (grid + 7) & ~7;   // whole XCD rounds; surplus workgroups exit at once
+    // Whole XCD rounds; surplus workgroups exit at once. A multiple of 8 is a multiple of
+    // every group count, so each group's slots cover its share of the tiles.
+    grid = (grid + 7) & ~7;
+    if (p.xcd_group == 0) p.xcd_group = 8;
+    if (p.xcd_group != 1 && p.xcd_group != 2 && p.xcd_group != 4 && p.xcd_group != 8) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_bf16_kernel<MODE, AT, BT, EPI, OUT_F32>), dim3(grid), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
@@ -644,6 +656,7 @@ static GemmParams base_rows(const ExpertGemmArgs& a) {
     p.mtiles_ub = (a.rows + BM - 1) / BM + a.E;
     p.b2_kstart = -1;
     p.ffn = a.ffn;
+    p.xcd_group = 4;     // measured: less fabric traffic than 8, steadier clock than 1 or 2
     return p;
 }
 
@@ -717,7 +730,7 @@ hipError_t mfma_down_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     p.M = a.d; p.N = a.ffn;
     p.C = a.dW2; p.ldc = a.ffn; p.ces = (long)a.d * a.ffn;
     const int grid = a.E * ((a.d + BM - 1) / BM) * ((a.ffn + BN - 1) / BN);
-    p.xcd_balance = 1;
+    p.xcd_group = 2;
     return run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
 }
 
@@ -733,7 +746,7 @@ hipError_t mfma_up_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     p.C = a.dW1; p.ldc = a.d; p.ces = (long)a.ffn * a.d;
     if (glu) { p.C2 = a.dW3; p.c2_mstart = a.ffn; }
     const int grid = a.E * ((hcols + BM - 1) / BM) * ((a.d + BN - 1) / BN);
-    p.xcd_balance = 1;
+    p.xcd_group = 2;
     return run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
 }
 
