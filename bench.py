@@ -29,39 +29,72 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
-def stage_work(w):
-    """Algorithmic work of each stage: ("flop", n) or ("byte", n)."""
+def stage_work(w, fused=False):
+    """Algorithmic work of each stage: {"flop": n, "byte": n} (either may be 0).
+
+    Bytes count each operand read once and each output written once.  fused: the
+    weight-gradient stages apply the SGD step to the expert weights (read and write
+    the fp32 master, write the working copy) instead of writing the fp32 gradient,
+    and the SGD stage covers the router weight and the biases only."""
     s = 2 if w.dtype == "bf16" else 4
     T, d, E, k, ffn = w.T, w.d, w.E, w.k, w.ffn
     R = T * k
-    hid = 2 * ffn if w.expert == "swiglu" else ffn     # up-projection output columns
-    nparam = E * d + E * ffn * d * (3 if w.expert == "swiglu" else 2)
-    if w.expert != "swiglu":
-        nparam += E * ffn + E * d
+    glu = w.expert == "swiglu"
+    hid = 2 * ffn if glu else ffn       # up-projection output columns
+    n_up, n_dn = E * hid * d, E * d * ffn              # expert parameters of each projection
+    n_small = E * d + (0 if glu else E * ffn + E * d)  # router weight and biases
+    wg_out = 8 + s if fused else 4                     # per weight-gradient element
+    sgd_params = n_small if fused else n_small + n_up + n_dn
+
+    def fl(n):
+        return {"flop": n, "byte": 0}
+
+    def by(n):
+        return {"flop": 0, "byte": n}
     return {
-        "router_logits": ("flop", 2.0 * T * d * E),
-        "route": ("byte", T * E * 4 + T * k * 8 + R * 12),
+        "router_logits": {"flop": 2.0 * T * d * E, "byte": T * d * s + E * d * s + T * E * 4},
+        "route": by(T * E * 4 + T * k * 8 + R * 12),
         # read X once, write k rows, read the slot indices
-        "gather": ("byte", (T * d + R * d) * s + R * 4),
-        "up_fwd": ("flop", 2.0 * R * d * hid),
-        "down_fwd": ("flop", 2.0 * R * ffn * d),
+        "gather": by((T * d + R * d) * s + R * 4),
+        # Xp, W1|W3 in; H and A out
+        "up_fwd": {"flop": 2.0 * R * d * hid, "byte": (R * d + n_up + R * hid + R * ffn) * s},
+        # A, W2 in; EO out
+        "down_fwd": {"flop": 2.0 * R * ffn * d, "byte": (R * ffn + n_dn + R * d) * s},
         # read k rows, gates, slots; write Y; read Y_target; write dY
-        "combine_loss": ("byte", (R * d + 3 * T * d) * s + R * 8),
+        "combine_loss": by((R * d + 3 * T * d) * s + R * 8),
         # read dY and k rows of EO, write k rows of dEO; slots, gates, dgate
-        "combine_bwd": ("byte", (T * d + 2 * R * d) * s + R * 12),
-        "down_dgrad": ("flop", 2.0 * R * d * ffn),
-        "down_wgrad": ("flop", 2.0 * R * d * ffn),
-        "up_dgrad": ("flop", 2.0 * R * hid * d),
-        "up_wgrad": ("flop", 2.0 * R * hid * d),
-        "bias_grads": ("byte", (R * d + R * ffn) * s if w.expert != "swiglu" else 0),
-        "router_bwd": ("byte", T * E * (4 + s) + T * k * 16),
-        "router_dwg": ("flop", 2.0 * T * E * d),
-        "router_dx": ("flop", 2.0 * T * E * d),
+        "combine_bwd": by((T * d + 2 * R * d) * s + R * 12),
+        # dEO, W2, H in; dH out
+        "down_dgrad": {"flop": 2.0 * R * d * ffn, "byte": (R * d + n_dn + 2 * R * hid) * s},
+        # dEO, A in; dW2 out (or the SGD step on W2)
+        "down_wgrad": {"flop": 2.0 * R * d * ffn, "byte": (R * d + R * ffn) * s + n_dn * wg_out},
+        # dH, W1|W3 in; dXp out
+        "up_dgrad": {"flop": 2.0 * R * hid * d, "byte": (R * hid + n_up + R * d) * s},
+        # dH, Xp in; dW1|dW3 out (or the SGD step on W1|W3)
+        "up_wgrad": {"flop": 2.0 * R * hid * d, "byte": (R * hid + R * d) * s + n_up * wg_out},
+        "bias_grads": by((R * d + R * ffn) * s if not glu else 0),
+        "router_bwd": by(T * E * (4 + s) + T * k * 16),
+        "router_dwg": {"flop": 2.0 * T * E * d, "byte": (T * E + T * d) * s + E * d * 4},
+        "router_dx": {"flop": 2.0 * T * E * d, "byte": (T * E + E * d) * s + T * d * 4},
         # read k rows of dXp and the fp32 router part, write dX, read slots
-        "scatter": ("byte", R * d * s + T * d * (4 + s) + R * 4),
+        "scatter": by(R * d * s + T * d * (4 + s) + R * 4),
         # master read + write, gradient read, working copy write
-        "sgd": ("byte", nparam * (4 + 4 + 4 + s)),
+        "sgd": by(sgd_params * (4 + 4 + 4 + s)),
     }
+
+
+def roof_of(work, ms, peak_flops_tf):
+    """The roof that bounds a stage (the one with the longer ideal time) and the
+    stage's achieved rate against it."""
+    t_flop = work["flop"] / (peak_flops_tf * 1e12) if work["flop"] else 0.0
+    t_byte = work["byte"] / (PEAK_HBM_GBS * 1e9) if work["byte"] else 0.0
+    if t_flop >= t_byte:
+        ach = work["flop"] / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_flops_tf, "unit": "TFLOP/s",
+                "frac": round(ach / peak_flops_tf, 4), "work_per_launch": work["flop"]}
+    ach = work["byte"] / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4), "work_per_launch": work["byte"]}
 
 
 GEMM_STAGES = ("up_fwd", "down_fwd", "down_dgrad", "down_wgrad", "up_dgrad", "up_wgrad")
@@ -98,15 +131,18 @@ STAGE_SOURCE.update({s: "routing.hip" for s in ("route", "router_bwd")})
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_train_step_t32768_d7168_e256.json")
 
 
-def measured_traffic(stage: str, workload: str):
+def measured_traffic(stage: str, workload: str, sgd: str):
     """HBM bytes per step of a stage from the committed counter summary, or None when
-    there is none or the kernel source has changed since the counters were taken."""
+    there is none, it was taken in the other SGD mode, or the kernel source has
+    changed since the counters were taken."""
     import hashlib
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     if rec.get("workload") != workload or stage not in rec.get("stages", {}):
+        return None
+    if rec.get("sgd", "stored") != sgd:
         return None
     src = os.path.join(ROOT, "sparse_mixture_experts_gate_amd", "csrc", STAGE_SOURCE[stage])
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -180,6 +216,12 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="grouped_sigmoid_t32768_d7168_e256")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sgd", choices=("fused", "stored"), default="fused",
+                    help="fused: the expert weight-gradient GEMMs apply the SGD step themselves "
+                         "(no expert gradients stored); stored: gradients written, then one SGD pass")
+    ap.add_argument("--gemm-steps", type=int, default=3,
+                    help="with --sgd fused: profiled steps that store the expert gradients, run "
+                         "after the timed region, for the GEMM-only stage times")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps (outside "
                          "the timed region), a known-size reference for hardware byte counters")
@@ -202,7 +244,11 @@ def main(argv=None) -> int:
     cfg = L.config(w)
     ws = L.alloc_workspace(cfg, dev)
     r = L.alloc_routing(w, dev)
+    fused = a.sgd == "fused"
     g = L.alloc_grads(w, dev)
+    if fused:
+        for n in ("dW1", "dW2", "dW3"):
+            g.pop(n, None)
     Y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
     loss = torch.empty(3, dtype=torch.float32, device=dev)
     params = {}
@@ -236,50 +282,68 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     elapsed = t1 - t0
-    stage_ms = {s: [] for s in L.STAGES}
-    for ev in events:
-        ev.collect()
-        for s in L.STAGES:
-            stage_ms[s].extend(ev.ms[s])
-    avg = {s: sum(v) / len(v) for s, v in stage_ms.items()}
+
+    def collect(evs):
+        per = {s: [] for s in L.STAGES}
+        for ev in evs:
+            ev.collect()
+            for s in L.STAGES:
+                per[s].extend(ev.ms[s])
+        return per, {s: sum(v) / len(v) for s, v in per.items()}
+    stage_ms, avg = collect(events)
     # GPU time of each whole step (first mark to last) and of its forward + backward
     step_gpu = sorted(sum(stage_ms[s][i] for s in L.STAGES) for i in range(a.steps))
-    fb_gpu = sorted(sum(stage_ms[s][i] for s in L.STAGES if s != "sgd") for i in range(a.steps))
 
     def pct(v, q):
         return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
-    work = stage_work(w)
-    stages = {}
-    for s in L.STAGES:
-        kind, n = work[s]
-        ms = avg[s]
-        ent = {"ms": round(ms, 4)}
-        if ms > 0 and n > 0:
-            if kind == "flop":
-                tf = n / (ms * 1e-3) / 1e12
-                ent.update(tflops=round(tf, 2), frac=round(tf / PEAK_BF16_TFLOPS, 4))
-            else:
-                gbs = n / (ms * 1e-3) / 1e9
-                ent.update(gbs=round(gbs, 1), frac=round(gbs / PEAK_HBM_GBS, 4))
-        stages[s] = ent
+    peak_tf = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    def stage_table(avg_ms, work):
+        out = {}
+        for s in L.STAGES:
+            ms = avg_ms[s]
+            ent = {"ms": round(ms, 4)}
+            if ms > 0 and (work[s]["flop"] or work[s]["byte"]):
+                ro = roof_of(work[s], ms, peak_tf)
+                ent.update(bound=ro["bound"], frac=ro["frac"])
+                if work[s]["flop"]:
+                    ent["tflops"] = round(work[s]["flop"] / (ms * 1e-3) / 1e12, 2)
+                if work[s]["byte"]:
+                    ent["gbs"] = round(work[s]["byte"] / (ms * 1e-3) / 1e9, 1)
+            out[s] = ent
+        return out
+    work = stage_work(w, fused)
+    stages = stage_table(avg, work)
     dom = max(L.STAGES, key=lambda s: avg[s])
-    kind, n = work[dom]
-    traffic = measured_traffic(dom, w.name)
-    if kind == "flop":
-        ach = n / (avg[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": dom, "work_per_launch": n}
-    else:
-        ach = n / (avg[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom,
-                "work_per_launch": n}
-    gemm_ms = sum(avg[s] for s in GEMM_STAGES)
-    gemm_flop = sum(work[s][1] for s in GEMM_STAGES)
+    roof = roof_of(work[dom], avg[dom], peak_tf)
+    roof["traffic"] = measured_traffic(dom, w.name, a.sgd)
+    roof["kernel"] = dom
+
+    # GEMM-only times: with the fused step, a few more profiled steps (outside the
+    # timed region) that store the expert weight gradients
+    gemm_avg, gemm_mode, gemm_ms_steps = avg, a.sgd, stage_ms
+    stages_stored = None
+    if fused and a.gemm_steps > 0:
+        gs = L.alloc_grads(w, dev)
+        ev2 = [L.StageEvents() for _ in range(a.gemm_steps)]
+        with torch.cuda.stream(stream):
+            for i in range(a.gemm_steps):
+                L.moe_train_step_profiled(cfg, X, Yt, params, w.lr, w.aux_coef, Y, r, gs, loss, ws,
+                                          ev2[i], stream=stream)
+            stream.synchronize()
+        gemm_ms_steps, gemm_avg = collect(ev2)
+        gemm_mode = "stored"
+        stages_stored = stage_table(gemm_avg, stage_work(w, False))
+        del gs
+    gemm_ms = sum(gemm_avg[s] for s in GEMM_STAGES)
+    gemm_flop = sum(work[s]["flop"] for s in GEMM_STAGES)
     counts = r["counts"].cpu().tolist()
     exec_flop = executed_gemm_flops(w, counts) if w.dtype == "bf16" else None
-    fwd_bwd_ms = sum(avg[s] for s in L.STAGES if s != "sgd")
+    # forward + backward alone: from steps that store the gradients (with the fused
+    # step the weight-gradient stages also carry the expert weights' SGD)
+    fwd_bwd_ms = sum(gemm_avg[s] for s in L.STAGES if s != "sgd")
+    n_fb = len(gemm_ms_steps["sgd"])
+    fb_gpu = sorted(sum(gemm_ms_steps[s][i] for s in L.STAGES if s != "sgd") for i in range(n_fb))
     ms_per_step = elapsed / a.steps * 1e3
     out = {
         "metric": METRIC,
@@ -296,9 +360,14 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "ffn": w.ffn, "k": w.k,
                    "n_groups": w.n_groups, "topk_groups": w.topk_groups, "score": w.score,
-                   "expert": w.expert, "step": "forward+loss+backward+sgd"},
+                   "expert": w.expert, "step": "forward+loss+backward+sgd",
+                   "sgd": "fused into the expert weight-gradient GEMMs" if fused
+                   else "one pass over stored gradients"},
         "roofline": roof,
         "fwd_bwd_tokens_per_s": round(w.T / (fwd_bwd_ms * 1e-3), 1),
+        "sgd": a.sgd,
+        "expert_gemm_from": f"{gemm_mode} gradients" + (f", {a.gemm_steps} extra profiled steps"
+                                                        if gemm_mode != a.sgd else ""),
         "expert_gemm_tflops": round(gemm_flop / (gemm_ms * 1e-3) / 1e12, 2),
         "expert_gemm_frac_peak": round(gemm_flop / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "expert_gemm_peak": {"tflops": PEAK_BF16_TFLOPS, "clock_ghz": PEAK_CLOCK_GHZ},
@@ -311,6 +380,7 @@ def main(argv=None) -> int:
         "dispatch_gbps": stages["gather"].get("gbs"),
         "combine_gbps": stages["combine_loss"].get("gbs"),
         "stages": stages,
+        "stages_stored_gradients": stages_stored,
         "loss": [round(x, 6) for x in loss.tolist()],
         "counts_min_max": [int(r["counts"].min()), int(r["counts"].max())],
         "empty_experts": int((r["counts"] == 0).sum()),

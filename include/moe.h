@@ -233,6 +233,15 @@ int moe_backward(const moe_config* cfg, const void* X, const moe_weights* w,
  * aux_coef * aux, backward, then SGD with learning rate lr on every
  * parameter (masters, then working copies).  Y_target dtype [T,d].
  * Writes Y, *r, *g and loss_out (device float[3] = {mse, aux, loss}).
+ *
+ * The expert weight gradients g->dW1, g->dW2 (and g->dW3 for SwiGLU) are
+ * either all given or all NULL; a mix fails with MOE_ERR_NULL_PTR.  When
+ * they are NULL, nothing is stored for them: the weight-gradient
+ * contractions apply the SGD step to W1, W2 (W3) and their working copies
+ * directly, which saves writing and re-reading those gradients (about 8
+ * bytes per expert parameter).  Each updated value is the same in both
+ * modes: master = fma(-lr, grad, master) in float32, with grad the same
+ * float32 sum.  The other gradients (dX, dWg, db1, db2) are always written.
  */
 int moe_train_step(const moe_config* cfg, const void* X, const void* Y_target,
                    moe_params* p, float lr, float aux_coef,
@@ -248,15 +257,16 @@ int moe_train_step(const moe_config* cfg, const void* X, const void* Y_target,
 #define MOE_STAGE_COMBINE_LOSS    5   /* F7-F8 Y, MSE, dY, loss scalars           */
 #define MOE_STAGE_COMBINE_BWD     6   /* B1  dgate, dEO                           */
 #define MOE_STAGE_DOWN_DGRAD      7   /* B2  dA = dEO W2, activation backward     */
-#define MOE_STAGE_DOWN_WGRAD      8   /* B3  dW2 = dEO^T A                        */
+#define MOE_STAGE_DOWN_WGRAD      8   /* B3  dW2 = dEO^T A (fused: + SGD on W2)    */
 #define MOE_STAGE_UP_DGRAD        9   /* B4  dXp = dH W1 (+ dH3 W3)               */
-#define MOE_STAGE_UP_WGRAD       10   /* B5  dW1 (| dW3) = dH^T Xp                */
+#define MOE_STAGE_UP_WGRAD       10   /* B5  dW1 (| dW3) = dH^T Xp (fused: + SGD)  */
 #define MOE_STAGE_BIAS_GRADS     11   /*     db1, db2 (MLP kinds)                 */
 #define MOE_STAGE_ROUTER_BWD     12   /* B7  dlogits                              */
 #define MOE_STAGE_ROUTER_DWG     13   /* B8  dWg = dl^T X                         */
 #define MOE_STAGE_ROUTER_DX      14   /* B8  router part of dX = dl Wg            */
 #define MOE_STAGE_SCATTER        15   /* B6  dX = sum of dXp rows + router part   */
-#define MOE_STAGE_SGD            16   /* S1  masters and working copies           */
+#define MOE_STAGE_SGD            16   /* S1  masters and working copies (fused:
+                                           Wg and the biases only)                  */
 #define MOE_NUM_STAGES           17
 
 /*

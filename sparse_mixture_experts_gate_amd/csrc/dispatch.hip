@@ -199,8 +199,11 @@ __device__ __forceinline__ void sgd8(float* master, const float* grad, void* wor
     const nf4* g4 = reinterpret_cast<const nf4*>(grad) + 2 * i;
     nf4 m0 = m4[0], m1 = m4[1];
     const nf4 g0 = __builtin_nontemporal_load(g4), g1 = __builtin_nontemporal_load(g4 + 1);
-    m0 -= lr * g0;
-    m1 -= lr * g1;
+    // one rounding per element, as in the SGD epilogue of the weight-gradient GEMMs
+    m0.x = __builtin_fmaf(-lr, g0.x, m0.x); m0.y = __builtin_fmaf(-lr, g0.y, m0.y);
+    m0.z = __builtin_fmaf(-lr, g0.z, m0.z); m0.w = __builtin_fmaf(-lr, g0.w, m0.w);
+    m1.x = __builtin_fmaf(-lr, g1.x, m1.x); m1.y = __builtin_fmaf(-lr, g1.y, m1.y);
+    m1.z = __builtin_fmaf(-lr, g1.z, m1.z); m1.w = __builtin_fmaf(-lr, g1.w, m1.w);
     m4[0] = m0;
     m4[1] = m1;
     if constexpr (sizeof(TW) == 2) {
@@ -234,7 +237,7 @@ __global__ void __launch_bounds__(256) sgd_kernel(SgdArgs a) {
     if (i < n8) sgd8<TW>(master, grad, work, i, a.lr);
     // tail (n not a multiple of 8)
     for (long t = 8 * n8 + i0; t < n; t += stride) {
-        float m = master[t] - a.lr * grad[t];
+        float m = __builtin_fmaf(-a.lr, grad[t], master[t]);
         master[t] = m;
         reinterpret_cast<TW*>(work)[t] = from_f<TW>(m);
     }

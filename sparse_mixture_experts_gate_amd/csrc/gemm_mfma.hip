@@ -80,8 +80,9 @@ struct GemmParams {
     int mtiles_ub;
     int kchunk;                   // KSEG without offsets: segment e is rows [e kchunk, (e+1) kchunk) of K
     int xcd_group;                // XCDs per tile group: 1, 2, 4 or 8 (see the tile deal)
-    void* C; void* C2; void* C3; long ldc; long ces;
+    void* C; void* C2; long ldc; long ces;
     int c2_mstart;
+    void* W; void* W2; float lr;  // EPI_SGD: C/C2 are fp32 masters, W/W2 their bf16 copies
     const bf16* bias; long bias_es;
     const bf16* H; long ldh; int ffn;
 };
@@ -194,6 +195,9 @@ __device__ __forceinline__ bf16x8 read_contig(const bf16* T, int rowbase, int ks
     const int ch = ((2 * ks + hk) ^ key) << 3;
     return *reinterpret_cast<const bf16x8*>(T + (rowbase + rr) * BK + ch);
 }
+typedef float nf4 __attribute__((ext_vector_type(4)));
+typedef unsigned int nu2 __attribute__((ext_vector_type(2)));
+typedef unsigned int nu4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store4(bf16* p, const float* v) {
     uint2 u;
     bf16* b = reinterpret_cast<bf16*>(&u);
@@ -428,6 +432,102 @@ gemm_bf16_kernel(GemmParams p) {
         }
 
         // ---- epilogue ------------------------------------------------------------------
+        if constexpr (EPI == EPI_SGD) {
+            // SGD step on the fp32 masters in place of storing the weight gradient.  The
+            // tile goes out in 8 passes of 32 rows: the two wavefronts that own a pass's
+            // rows put their accumulators in LDS (1 KB rows, 16-byte chunk c of row r at
+            // c ^ r; two buffers, so one barrier per pass), then all 256 threads update
+            // whole rows.  Each thread loads its masters two passes ahead into registers:
+            // vector memory operations retire in issue order, so a wait for those loads
+            // never covers the stores of the two passes before.
+            static_assert(MODE == MODE_KSEG && OUT_F32 && NI == 4 && NJ == 4,
+                          "SGD epilogue: weight gradients, full wave layout");
+            {
+                float* stage = reinterpret_cast<float*>(&lds[0][0][0]);   // 2 x 32 rows x 1 KB
+                const int qt = tid & 63, rs = wave;            // a wavefront updates whole rows
+                const int n = n0 + qt * 4;
+                const bool col_ok = n < p.N;
+                const float nlr = -p.lr;
+                float* const M1 = reinterpret_cast<float*>(p.C);
+                float* const M2 = reinterpret_cast<float*>(p.C2);
+                bf16* const W1 = reinterpret_cast<bf16*>(p.W);
+                bf16* const W2 = reinterpret_cast<bf16*>(p.W2);
+                const int c2 = M2 ? p.c2_mstart : 0x7fffffff;
+                const long ldc = p.ldc, eoff = (long)e * p.ces;
+                // Tile rows [0, n1) are rows m0.. of C (W), rows [n1, rows_valid) rows of C2 (W2).
+                // One buffer descriptor per half bounds the tile's rows up to column N, so that
+                // every load and store is issued unconditionally (exact wait counts) and a lane
+                // outside the tile gets an offset past the bound: its store is dropped and its
+                // load returns zeros.
+                const int n1 = max(0, min(rows_valid, c2 - m0));
+                const int n2 = rows_valid - n1;
+                const long b1 = eoff + (long)m0 * ldc, b2 = eoff + (long)max(m0 - c2, 0) * ldc;
+                const rsrc_t rm1 = make_rsrc(M1 + b1, n1 > 0 ? ((long)(n1 - 1) * ldc + p.N) * 4 : 0);
+                const rsrc_t rw1 = make_rsrc(W1 + b1, n1 > 0 ? ((long)(n1 - 1) * ldc + p.N) * 2 : 0);
+                const rsrc_t rm2 = n2 > 0 ? make_rsrc(M2 + b2, ((long)(n2 - 1) * ldc + p.N) * 4) : rm1;
+                const rsrc_t rw2 = n2 > 0 ? make_rsrc(W2 + b2, ((long)(n2 - 1) * ldc + p.N) * 2) : rw1;
+                constexpr uint32_t OUT = 0x80000000u;          // past every bound
+                // element offset of tile row ml (wave-uniform) at this thread's columns in its
+                // half, or OUT
+                auto elem = [&](int ml, bool& sec) -> uint32_t {
+                    sec = ml >= n1;
+                    const int r = sec ? ml - n1 : ml;
+                    return (ml < rows_valid && col_ok) ? (uint32_t)((long)r * ldc + n) : OUT;
+                };
+                nf4 mb[3][8];
+                auto prefetch = [&](int q, nf4* dst) {
+#pragma unroll
+                    for (int it = 0; it < 8; ++it) {
+                        bool sec;
+                        const uint32_t o = elem(q * 32 + it * 4 + rs, sec);
+                        dst[it] = __builtin_bit_cast(nf4, __builtin_amdgcn_raw_buffer_load_b128(
+                            sec ? rm2 : rm1, o == OUT ? OUT : o * 4, 0, 2));
+                    }
+                };
+                prefetch(0, mb[0]);
+                prefetch(1, mb[1]);
+                __syncthreads();                               // every wave is past its last LDS read
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    if (q * 32 >= rows_valid) break;           // uniform
+                    if (q + 2 < 8) prefetch(q + 2, mb[(q + 2) % 3]);
+                    float* S = stage + (q & 1) * (32 * 256);
+                    if (rb == (q >> 2) * 128) {                // the waves that own rows q*32 ..
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                const int c = (cb + j * 32 + g * 8 + hk * 4) >> 2;
+                                *reinterpret_cast<nf4*>(S + rr * 256 + ((c ^ rr) << 2)) =
+                                    nf4{acc[q & 3][j][g * 4], acc[q & 3][j][g * 4 + 1],
+                                        acc[q & 3][j][g * 4 + 2], acc[q & 3][j][g * 4 + 3]};
+                            }
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int it = 0; it < 8; ++it) {
+                        const int r = it * 4 + rs;
+                        const nf4 gr = *reinterpret_cast<const nf4*>(S + r * 256 + ((qt ^ r) << 2));
+                        bool sec;
+                        const uint32_t o = elem(q * 32 + r, sec);
+                        const nf4 mv = mb[q % 3][it];
+                        nf4 w;
+                        w.x = __builtin_fmaf(nlr, gr.x, mv.x);
+                        w.y = __builtin_fmaf(nlr, gr.y, mv.y);
+                        w.z = __builtin_fmaf(nlr, gr.z, mv.z);
+                        w.w = __builtin_fmaf(nlr, gr.w, mv.w);
+                        uint2 u;
+                        bf16* h = reinterpret_cast<bf16*>(&u);
+                        h[0] = (bf16)w.x; h[1] = (bf16)w.y; h[2] = (bf16)w.z; h[3] = (bf16)w.w;
+                        const nu2 uv = {u.x, u.y};
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(nu4, w), sec ? rm2 : rm1,
+                                                               o == OUT ? OUT : o * 4, 0, 2);
+                        __builtin_amdgcn_raw_buffer_store_b64(uv, sec ? rw2 : rw1, o == OUT ? OUT : o * 2, 0, 2);
+                    }
+                }
+            }
+            return;
+        }
         if constexpr (EPI == EPI_STORE && OUT_F32) {
             // fp32 tile written out through LDS in two passes of 128 rows: each pass the
             // wavefronts that own those rows put their accumulators in LDS as 1 KB rows
@@ -456,21 +556,24 @@ gemm_bf16_kernel(GemmParams p) {
                 const int n = n0 + qt * 4;
                 float b[4] = {0.f, 0.f, 0.f, 0.f};
                 if (p.bias && n < p.N) load4(p.bias + (long)e * p.bias_es + n, b);
+                // the output halves as locals: a per-lane choice between two kernel-argument
+                // fields compiles to a load of the chosen field and a full wait before the store
+                float* const C1 = reinterpret_cast<float*>(p.C);
+                float* const C2 = reinterpret_cast<float*>(p.C2);
+                const int c2 = C2 ? p.c2_mstart : 0x7fffffff;
 #pragma unroll 4
                 for (int it = 0; it < 32; ++it) {
-                    const int r = it * 4 + (tid >> 6);
+                    const int r = it * 4 + wave;                   // a wavefront stores whole rows
                     const int ml = pass * 128 + r;
                     const float4 x = *reinterpret_cast<const float4*>(stage + r * 256 + ((qt ^ (r & 63)) << 2));
                     if (ml < rows_valid && n < p.N) {
                         const float v[4] = {x.x + b[0], x.y + b[1], x.z + b[2], x.w + b[3]};
                         const long row = (MODE == MODE_ROWS) ? row_base + m0 + ml : (long)(m0 + ml);
                         if (MODE == MODE_KSEG) {
-                            void* base = p.C;
-                            long m = row;
-                            if (p.C2 && m >= p.c2_mstart) { base = p.C2; m -= p.c2_mstart; }
-                            store4(reinterpret_cast<float*>(base) + (long)e * p.ces + m * p.ldc + n, v);
+                            const bool sec = row >= c2;
+                            store4((sec ? C2 : C1) + (long)e * p.ces + (sec ? row - c2 : row) * p.ldc + n, v);
                         } else {
-                            store4(reinterpret_cast<float*>(p.C) + row * p.ldc + n, v);
+                            store4(C1 + row * p.ldc + n, v);
                         }
                     }
                 }
@@ -731,6 +834,10 @@ hipError_t mfma_down_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     p.C = a.dW2; p.ldc = a.ffn; p.ces = (long)a.d * a.ffn;
     const int grid = a.E * ((a.d + BM - 1) / BM) * ((a.ffn + BN - 1) / BN);
     p.xcd_group = 2;
+    if (a.W2m) {    // SGD step on W2 in place of storing dW2
+        p.C = a.W2m; p.W = a.W2w; p.lr = a.lr;
+        return run<MODE_KSEG, true, true, EPI_SGD, true>(p, grid, s);
+    }
     return run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
 }
 
@@ -747,6 +854,11 @@ hipError_t mfma_up_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     if (glu) { p.C2 = a.dW3; p.c2_mstart = a.ffn; }
     const int grid = a.E * ((hcols + BM - 1) / BM) * ((a.d + BN - 1) / BN);
     p.xcd_group = 2;
+    if (a.W1m) {    // SGD step on W1 (and W3) in place of storing dW1 (dW3)
+        p.C = a.W1m; p.W = a.W1w; p.lr = a.lr;
+        if (glu) { p.C2 = a.W3m; p.W2 = a.W3w; }
+        return run<MODE_KSEG, true, true, EPI_SGD, true>(p, grid, s);
+    }
     return run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
 }
 

@@ -109,14 +109,21 @@ __global__ void __launch_bounds__(256) s_up_dgrad(ExpertGemmArgs a) {
 template <class T>
 __global__ void __launch_bounds__(256)
 s_wgrad(const int32_t* offsets, const T* P, int ldp, int pcol0, const T* Q, int ldq,
-        float* out, int M, int N) {
+        float* out, int M, int N, float* master, T* work, float lr) {
     const int e = blockIdx.z, m = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
     if (n >= N) return;
     const int lo = offsets[e], hi = offsets[e + 1];
     float acc = 0.f;
     for (int r = lo; r < hi; ++r)
         acc = fmaf(to_f<T>(P[(size_t)r * ldp + pcol0 + m]), to_f<T>(Q[(size_t)r * ldq + n]), acc);
-    out[((size_t)e * M + m) * N + n] = acc;
+    const size_t o = ((size_t)e * M + m) * N + n;
+    if (master) {           // SGD step in place of storing the gradient
+        const float w = fmaf(-lr, acc, master[o]);
+        master[o] = w;
+        work[o] = from_f<T>(w);
+    } else {
+        out[o] = acc;
+    }
 }
 
 // Router: logits = X Wg^T (fp32 out).
@@ -186,7 +193,8 @@ hipError_t simple_up_dgrad(const ExpertGemmArgs& a, hipStream_t s) {
 hipError_t simple_down_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     // dW2[e][c][j] = sum_r dEO[r][c] * A[r][j]
     hipLaunchKernelGGL(s_wgrad<float>, dim3((a.ffn + 255) / 256, a.d, a.E), dim3(256), 0, s,
-                       a.offsets, (const float*)a.dEO, a.d, 0, (const float*)a.A, a.ffn, a.dW2, a.d, a.ffn);
+                       a.offsets, (const float*)a.dEO, a.d, 0, (const float*)a.A, a.ffn, a.dW2, a.d, a.ffn,
+                       a.W2m, (float*)a.W2w, a.lr);
     return hipGetLastError();
 }
 hipError_t simple_up_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
@@ -194,10 +202,10 @@ hipError_t simple_up_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     const int hcols = glu ? 2 * a.ffn : a.ffn;
     dim3 g((a.d + 255) / 256, a.ffn, a.E);
     hipLaunchKernelGGL(s_wgrad<float>, g, dim3(256), 0, s, a.offsets, (const float*)a.dH, hcols, 0,
-                       (const float*)a.Xp, a.d, a.dW1, a.ffn, a.d);
+                       (const float*)a.Xp, a.d, a.dW1, a.ffn, a.d, a.W1m, (float*)a.W1w, a.lr);
     if (glu)
         hipLaunchKernelGGL(s_wgrad<float>, g, dim3(256), 0, s, a.offsets, (const float*)a.dH, hcols, a.ffn,
-                           (const float*)a.Xp, a.d, a.dW3, a.ffn, a.d);
+                           (const float*)a.Xp, a.d, a.dW3, a.ffn, a.d, a.W3m, (float*)a.W3w, a.lr);
     return hipGetLastError();
 }
 hipError_t simple_router_logits(const RouterGemmArgs& a, hipStream_t s) {

@@ -122,6 +122,8 @@ enum GemmEpi {
     EPI_DN_SWIGLU = 4,     // dH1 = dA*H3*silu'(H1), dH3 = dA*silu(H1)
     EPI_DN_RELU = 5,       // dH = dA * relu'(H)
     EPI_DN_GELU = 6,       // dH = dA * gelu'(H)
+    EPI_SGD = 7,           // weight gradient applied as an SGD step instead of stored:
+                           // master = fma(-lr, acc, master), working copy = bf16(master)
 };
 
 // Expert contractions of the layer.  All row-major; see each field.
@@ -135,6 +137,13 @@ struct ExpertGemmArgs {
     const void* dEO; void* dH; void* dXp;  // backward
     float* dW1; float* dW3; float* dW2;
     int expert;                      // MOE_EXPERT_*
+    // SGD fused into the weight-gradient contractions (training step without stored
+    // expert gradients): when W1m is set, the up-projection wgrad updates W1m/W1w (and
+    // W3m/W3w) in place of writing dW1 (dW3); when W2m is set, the down-projection wgrad
+    // updates W2m/W2w in place of writing dW2.  m = fp32 masters, w = working copies.
+    float* W1m; float* W3m; float* W2m;
+    void* W1w; void* W3w; void* W2w;
+    float lr;
 };
 // float32 layer (gemm_simple.hip): one thread per output element, fp32 accumulate.
 hipError_t simple_up_fwd(const ExpertGemmArgs& a, hipStream_t s);

@@ -12,6 +12,7 @@
 // counts, offsets and the expert GEMM tile schedule never leave the device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -70,6 +71,10 @@ int supported(const moe_config* c) {
         if (c->d % 4 || c->ffn % 4) return MOE_ERR_UNSUPPORTED;
     } else {
         if (c->d % 64 || c->ffn % 64 || c->E % 8) return MOE_ERR_UNSUPPORTED;
+        // The grouped GEMMs address an expert's rows of a k-strided operand (up to T rows of
+        // up to max(d, hcols) bf16) through one buffer descriptor with 32-bit offsets.
+        const int64_t widest = std::max<int64_t>(c->d, c->expert == MOE_EXPERT_SWIGLU ? 2 * (int64_t)c->ffn : c->ffn);
+        if ((int64_t)c->T * widest * 2 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
     }
     return MOE_OK;
 }
@@ -153,10 +158,14 @@ void add_routing(Ptrs& P, const moe_routing* r, bool logits) {
     P.add(r->slot_of, true); P.add(r->token_of, true); P.add(r->aux);
 }
 
-void add_grads(Ptrs& P, const moe_config* c, const moe_grads* g) {
-    P.add(g->dX, true); P.add(g->dWg); P.add(g->dW1); P.add(g->dW2);
-    if (c->expert == MOE_EXPERT_SWIGLU) P.add(g->dW3);
-    else { P.add(g->db1); P.add(g->db2); }
+// experts = false: the expert weight gradients (dW1, dW2, dW3) are not stored.
+void add_grads(Ptrs& P, const moe_config* c, const moe_grads* g, bool experts = true) {
+    P.add(g->dX, true); P.add(g->dWg);
+    if (experts) {
+        P.add(g->dW1); P.add(g->dW2);
+        if (c->expert == MOE_EXPERT_SWIGLU) P.add(g->dW3);
+    }
+    if (c->expert != MOE_EXPERT_SWIGLU) { P.add(g->db1); P.add(g->db2); }
 }
 
 struct Ctx {
@@ -245,8 +254,11 @@ int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_
     return MOE_OK;
 }
 
+// sgd != NULL: the expert weight gradients are not stored; the weight-gradient
+// contractions apply the SGD step (rate lr) to sgd's masters and working copies.
 int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_routing* r,
-                 const void* dY, float aux_coef, moe_grads* g) {
+                 const void* dY, float aux_coef, moe_grads* g,
+                 const moe_params* sgd = nullptr, float lr = 0.f) {
     const moe_config* c = x.c;
     const bool f32 = c->dtype == MOE_DTYPE_F32;
     const int vec = c->d * esize(c) / 16;
@@ -256,6 +268,14 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
     TRY(launch_combine_bwd(cb, c->dtype, x.s));
     ExpertGemmArgs ea = expert_args(x, w, r);
     ea.dW1 = g->dW1; ea.dW2 = g->dW2; ea.dW3 = g->dW3;
+    if (sgd) {
+        const bool glu = c->expert == MOE_EXPERT_SWIGLU;
+        ea.dW1 = ea.dW2 = ea.dW3 = nullptr;
+        ea.W1m = sgd->W1; ea.W1w = sgd->W1_w;
+        ea.W2m = sgd->W2; ea.W2w = sgd->W2_w;
+        ea.W3m = glu ? sgd->W3 : nullptr; ea.W3w = glu ? sgd->W3_w : nullptr;
+        ea.lr = lr;
+    }
     TRY(x.mark(MOE_STAGE_DOWN_DGRAD));
     TRY(f32 ? simple_down_dgrad(ea, x.s) : mfma_down_dgrad(ea, x.s));
     TRY(x.mark(MOE_STAGE_DOWN_WGRAD));
@@ -378,13 +398,18 @@ static int train_step_impl(const moe_config* cfg, const void* X, const void* Y_t
     if (!p || !r || !g) return MOE_ERR_NULL_PTR;
     if ((st = check_bias(cfg, p->e_bias)) != MOE_OK) return st;
     const bool glu = cfg->expert == MOE_EXPERT_SWIGLU;
+    // expert weight gradients: all given (stored, then SGD over every parameter) or all
+    // NULL (SGD fused into the weight-gradient contractions, nothing stored)
+    const int n_null = !g->dW1 + !g->dW2 + (glu ? !g->dW3 : 0);
+    const bool fused = n_null == (glu ? 3 : 2);
+    if (n_null && !fused) return MOE_ERR_NULL_PTR;
     Ptrs P;
     P.add(X, true); P.add(Y_target, true); P.add(Y, true); P.add(loss_out);
     P.add(p->Wg); P.add(p->W1); P.add(p->W2); P.add(p->Wg_w); P.add(p->W1_w); P.add(p->W2_w);
     if (glu) { P.add(p->W3); P.add(p->W3_w); }
     else { P.add(p->b1); P.add(p->b2); P.add(p->b1_w); P.add(p->b2_w); }
     add_routing(P, r, true);
-    add_grads(P, cfg, g);
+    add_grads(P, cfg, g, !fused);
     if ((st = P.check(cfg->T)) != MOE_OK) return st;
     if (events) {
         for (int i = 0; i <= MOE_NUM_STAGES; ++i)
@@ -395,14 +420,15 @@ static int train_step_impl(const moe_config* cfg, const void* X, const void* Y_t
                      glu ? p->W3_w : nullptr, p->e_bias};
     st = run_forward(x, X, &w, Y, r, Y_target, aux_coef, loss_out);
     if (st != MOE_OK) return st;
-    st = run_backward(x, X, &w, r, x.buf<void>(B_DY), aux_coef, g);
+    st = run_backward(x, X, &w, r, x.buf<void>(B_DY), aux_coef, g, fused ? p : nullptr, lr);
     if (st != MOE_OK) return st;
     const long E = cfg->E, d = cfg->d, ffn = cfg->ffn;
+    // (the expert weights W1, W2, W3 were already updated when the step is fused)
     struct { float* m; const float* g; void* w; long n; } upd[6] = {
         {p->Wg, g->dWg, p->Wg_w, E * d},
-        {p->W1, g->dW1, p->W1_w, E * ffn * d},
-        {p->W2, g->dW2, p->W2_w, E * d * ffn},
-        {glu ? p->W3 : nullptr, g->dW3, p->W3_w, E * ffn * d},
+        {fused ? nullptr : p->W1, g->dW1, p->W1_w, E * ffn * d},
+        {fused ? nullptr : p->W2, g->dW2, p->W2_w, E * d * ffn},
+        {glu && !fused ? p->W3 : nullptr, g->dW3, p->W3_w, E * ffn * d},
         {glu ? nullptr : p->b1, g->db1, p->b1_w, E * ffn},
         {glu ? nullptr : p->b2, g->db2, p->b2_w, E * d},
     };

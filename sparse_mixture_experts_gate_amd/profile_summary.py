@@ -3,9 +3,9 @@
 HBM traffic per stage, from two counter runs:
 
     rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o fetch --output-format csv -- \\
-        python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration-mib 1024
+        python3 bench.py --steps 1 --warmup 0 --gemm-steps 0 --no-cpu-baseline --copy-calibration-mib 1024
     rocprofv3 --pmc WRITE_SIZE -d OUT/write -o write --output-format csv -- \\
-        python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration-mib 1024
+        python3 bench.py --steps 1 --warmup 0 --gemm-steps 0 --no-cpu-baseline --copy-calibration-mib 1024
     python -m sparse_mixture_experts_gate_amd.profile_summary OUT/fetch/fetch_counter_collection.csv \\
         OUT/write/write_counter_collection.csv --calibration-mib 1024 --json J --markdown M
 
@@ -160,7 +160,9 @@ def markdown(rec, title, command):
              f"{rec['calibration']['copy_write_kib'] / 1024:.1f} MiB by WRITE_SIZE, so FETCH_SIZE is "
              f"scaled by {rec['calibration']['fetch_scale']} and WRITE_SIZE by "
              f"{rec['calibration']['write_scale']}.", "",
-             "FETCH_SIZE counts L2 misses (served by the MALL or HBM), WRITE_SIZE the L2 write-back traffic.", "",
+             "FETCH_SIZE counts L2 misses (served by the MALL or HBM), WRITE_SIZE the L2 write-back traffic.",
+             f"SGD mode of the step: {rec.get('sgd', 'stored')} (fused: the expert weight-gradient GEMMs apply "
+             "the SGD step to the expert weights; the sgd stage covers the router weight and biases).", "",
              "| stage | launches | fabric read (GB) | fabric write (GB) | total (GB) | ms (under counters) |",
              "|---|---|---|---|---|---|"]
     for st, e in rec["stages"].items():
@@ -276,9 +278,12 @@ def main(argv=None):
     ap.add_argument("--json")
     ap.add_argument("--markdown")
     ap.add_argument("--command", default="")
+    ap.add_argument("--sgd", choices=("fused", "stored"), default="fused",
+                    help="the bench.py --sgd mode the counters were taken in")
     a = ap.parse_args(argv)
     rec = summarize(a.fetch_csv, a.write_csv, a.calibration_mib)
     rec["workload"] = a.workload
+    rec["sgd"] = a.sgd
     rec["command"] = a.command
     if a.json:
         json.dump(rec, open(a.json, "w"), indent=1)

@@ -136,6 +136,11 @@ def test_bf16_shape_rules(lib):
     assert _call_forward(L.config(w.replace(d=1000))) == -5
     assert _call_forward(L.config(w.replace(ffn=4000))) == -5
     assert _call_forward(L.config(w.replace(E=12, k=2))) == -5
+    # an expert's rows of the widest k-strided operand must span less than 2 GiB
+    widest = max(w.d, 2 * w.ffn if w.expert == "swiglu" else w.ffn)
+    assert _call_forward(L.config(w.replace(T=(1 << 31) // (2 * widest) + 1))) == -5
+    wg = w.replace(expert="swiglu", ffn=2048)                    # hcols 4096 > d
+    assert _call_forward(L.config(wg.replace(T=(1 << 30) // 4096 + 1))) == -5
 
 
 def test_pointer_and_workspace_errors(lib):

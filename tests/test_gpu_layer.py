@@ -138,13 +138,21 @@ def test_inputs_unchanged_and_calls_repeatable():
         assert torch.equal(run.grads[n], g1[n]), n
 
 
-def train_step_parity(w, inp, label):
-    """moe_train_step against the oracle's forward, loss, backward and SGD."""
+EXPERT_GRADS = ("dW1", "dW2", "dW3")
+
+
+def train_step_parity(w, inp, label, fused=False):
+    """moe_train_step against the oracle's forward, loss, backward and SGD.
+    fused: the expert weight gradients are not passed, so the weight-gradient
+    contractions apply the SGD step to W1, W2 (W3) themselves."""
     dev = "cuda"
     cfg = L.config(w)
     ws = L.alloc_workspace(cfg, dev)
     r = L.alloc_routing(w, dev)
     g = L.alloc_grads(w, dev)
+    if fused:
+        for n in EXPERT_GRADS:
+            g.pop(n, None)
     Y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
     loss = torch.empty(3, dtype=torch.float32, device=dev)
     params = {}
@@ -190,6 +198,101 @@ def train_step_parity(w, inp, label):
                                VARIANT_CASES[0], VARIANT_CASES[2]], ids=lambda w: w.name)
 def test_train_step_parity(w):
     train_step_parity(w, _inputs(w), w.name)
+
+
+FUSED_CASES = [F32_CASES[0], F32_CASES[2], BF16_CASES[0], BF16_CASES[1], BF16_CASES[2], BF16_CASES[5],
+               VARIANT_CASES[2]]
+
+
+@pytest.mark.parametrize("w", FUSED_CASES, ids=lambda w: w.name)
+def test_train_step_fused_sgd_parity(w):
+    train_step_parity(w, _inputs(w), w.name + "/fused", fused=True)
+
+
+def _one_step(w, inp, fused, Wg_override=None):
+    dev = "cuda"
+    cfg = L.config(w)
+    ws = L.alloc_workspace(cfg, dev)
+    r = L.alloc_routing(w, dev)
+    g = L.alloc_grads(w, dev)
+    if fused:
+        for n in EXPERT_GRADS:
+            g.pop(n, None)
+    Y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
+    loss = torch.empty(3, dtype=torch.float32, device=dev)
+    params = {}
+    for n in ("Wg", "W1", "b1", "W2", "b2", "W3"):
+        if inp.get(n) is not None:
+            params[n] = inp[n].clone().to(dev)
+            params[n + "_w"] = inp[n + "_w"].clone().to(dev)
+    L.moe_train_step(cfg, inp["X"].to(dev), inp["Yt"].to(dev), params, w.lr, w.aux_coef, Y, r, g,
+                     loss, ws)
+    torch.cuda.synchronize()
+    out = {"Y": Y.cpu(), "loss": loss.cpu(), **{n: v.cpu() for n, v in params.items()},
+           **{"grad " + n: v.cpu() for n, v in g.items() if n not in EXPERT_GRADS},
+           **{"routing " + n: v.cpu() for n, v in r.items()}}
+    return out
+
+
+@pytest.mark.parametrize("w", [F32_CASES[2], BF16_CASES[0], BF16_CASES[1], BF16_CASES[5]],
+                         ids=lambda w: w.name)
+def test_fused_sgd_equals_stored_gradient_step(w):
+    """The fused step and the step through stored gradients give bitwise the same
+    parameters, outputs and remaining gradients: the gradient is the same float32
+    sum and each element takes the same fused multiply-add."""
+    inp = _inputs(w)
+    a = _one_step(w, inp, fused=False)
+    b = _one_step(w, inp, fused=True)
+    assert a.keys() == b.keys()
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_fused_sgd_with_empty_experts():
+    """Experts that receive no rows keep their weights (their gradient is zero) in the
+    fused step too, and their working copies are rewritten from the masters."""
+    w = wl("bf16_empty_fused", T=512, d=256, E=8, ffn=256, k=2, dtype="bf16", expert="swiglu")
+    inp = _inputs(w)
+    g = inp["Wg"].clone()
+    g[4:] = g[3]
+    inp["Wg"] = g
+    inp["Wg_w"] = g.to(torch.bfloat16)
+    out = _one_step(w, inp, fused=True)
+    assert out["routing counts"][5:].tolist() == [0, 0, 0]
+    for n in ("W1", "W2", "W3"):
+        assert torch.equal(out[n][5:], inp[n][5:]), n
+        assert torch.equal(out[n + "_w"][5:], inp[n][5:].to(torch.bfloat16)), n
+    ref = _one_step(w, inp, fused=False)
+    for n in ref:
+        assert torch.equal(ref[n], out[n]), n
+
+
+def test_train_step_rejects_partial_expert_gradients():
+    """dW1, dW2 (dW3) are given together or not at all."""
+    w = BF16_CASES[4]
+    dev = "cuda"
+    cfg = L.config(w)
+    ws = L.alloc_workspace(cfg, dev)
+    r = L.alloc_routing(w, dev)
+    inp = _inputs(w)
+    params = {}
+    for n in ("Wg", "W1", "W2", "W3"):
+        params[n] = inp[n].clone().to(dev)
+        params[n + "_w"] = inp[n + "_w"].clone().to(dev)
+    keep = {n: v.clone() for n, v in params.items()}
+    Y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
+    loss = torch.empty(3, dtype=torch.float32, device=dev)
+    for drop in (("dW1",), ("dW3",), ("dW1", "dW2")):
+        g = L.alloc_grads(w, dev)
+        for n in drop:
+            g.pop(n)
+        with pytest.raises(L.MoeError) as ei:
+            L.moe_train_step(cfg, inp["X"].to(dev), inp["Yt"].to(dev), params, w.lr, w.aux_coef, Y, r,
+                             g, loss, ws)
+        assert L.STATUS[ei.value.status] == "MOE_ERR_NULL_PTR"
+    torch.cuda.synchronize()
+    for n, v in keep.items():
+        assert torch.equal(params[n], v), n
 
 
 @pytest.mark.parametrize("w", [F32_CASES[0], BF16_CASES[3]], ids=lambda w: w.name)
