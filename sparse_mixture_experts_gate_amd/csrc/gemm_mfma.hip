@@ -198,6 +198,21 @@ __device__ __forceinline__ bf16x8 read_contig(const bf16* T, int rowbase, int ks
 typedef float nf4 __attribute__((ext_vector_type(4)));
 typedef unsigned int nu2 __attribute__((ext_vector_type(2)));
 typedef unsigned int nu4 __attribute__((ext_vector_type(4)));
+// 8 bf16 of a 16-byte vector to float, and back (round to nearest even)
+__device__ __forceinline__ void unpack8(nu4 u, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        f[2 * k] = __uint_as_float(u[k] << 16);
+        f[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ nu4 pack8(const float* f) {
+    nu4 u;
+    bf16* b = reinterpret_cast<bf16*>(&u);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) b[k] = (bf16)f[k];
+    return u;
+}
 __device__ __forceinline__ void store4(bf16* p, const float* v) {
     uint2 u;
     bf16* b = reinterpret_cast<bf16*>(&u);
@@ -679,7 +694,92 @@ gemm_bf16_kernel(GemmParams p) {
             }
             return;
         }
-        // MLP forward and the activation backward: straight from the accumulator layout
+        if constexpr (EPI == EPI_DN_SWIGLU || EPI == EPI_DN_RELU || EPI == EPI_DN_GELU) {
+            // Activation backward.  dA (the fp32 accumulators) goes out in passes of 32 rows
+            // through LDS (1 KB rows, 16-byte chunk c of row r at c ^ r, two buffers, one
+            // barrier per pass); each thread then takes 8 consecutive columns of a row, reads
+            // H (H1 and H3 for SwiGLU) as 16-byte vectors loaded two passes ahead, and writes
+            // dH.  H and dH go through buffer descriptors bounded to the tile's rows, and every
+            // load and store is issued unconditionally (a lane outside the tile gets an offset
+            // past the bound: its store is dropped, its load reads zeros), so the waits for H
+            // count exactly and never cover the stores of the two passes before.
+            constexpr bool GLU = EPI == EPI_DN_SWIGLU;
+            constexpr int NH = GLU ? 2 : 1;                    // H vectors per 8 columns
+            constexpr uint32_t OUT = 0x80000000u;              // past every bound
+            float* stage = reinterpret_cast<float*>(&lds[0][0][0]);   // 2 x 32 rows x 1 KB
+            const int c8 = tid & 31, rs = tid >> 5;            // 8-column chunk; row of an 8-row step
+            const int n = n0 + c8 * 8;
+            const bool col_ok = n < p.N;
+            const long rowg = row_base + m0;                   // first row of the tile
+            const int ldh = (int)p.ldh, ldc = (int)p.ldc, ffn = p.ffn;
+            const rsrc_t rh = make_rsrc(p.H + rowg * ldh, (long)rows_valid * ldh * 2);
+            const rsrc_t rd = make_rsrc(reinterpret_cast<bf16*>(p.C) + rowg * ldc, (long)rows_valid * ldc * 2);
+            const int npass = (rows_valid + 31) >> 5;
+            nu4 hb[3][4][NH];
+            auto prefetch = [&](int q, nu4 (*dst)[NH]) {
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int r = q * 32 + it * 8 + rs;
+                    const bool ok = r < rows_valid && col_ok;
+#pragma unroll
+                    for (int h = 0; h < NH; ++h)
+                        dst[it][h] = __builtin_bit_cast(nu4, __builtin_amdgcn_raw_buffer_load_b128(
+                            rh, ok ? (uint32_t)(r * ldh + n + h * ffn) * 2 : OUT, 0, 0));
+                }
+            };
+            prefetch(0, hb[0]);
+            if (npass > 1) prefetch(1, hb[1]);
+            __syncthreads();                                   // every wave is past its last LDS read
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if (q >= npass) break;                         // uniform
+                if (q + 2 < npass) prefetch(q + 2, hb[(q + 2) % 3]);
+                float* S = stage + (q & 1) * (32 * 256);
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    if (rb + i * 32 != q * 32) continue;       // the waves that own rows q*32 ..
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int c = (cb + j * 32 + g * 8 + hk * 4) >> 2;
+                            *reinterpret_cast<nf4*>(S + rr * 256 + ((c ^ rr) << 2)) =
+                                nf4{acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                                    acc[i][j][g * 4 + 3]};
+                        }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int r = it * 8 + rs;                 // row within the pass
+                    const int rt = q * 32 + r;                 // row within the tile
+                    const bool ok = rt < rows_valid && col_ok;
+                    const nf4 x0 = *reinterpret_cast<const nf4*>(S + r * 256 + (((2 * c8) ^ r) << 2));
+                    const nf4 x1 = *reinterpret_cast<const nf4*>(S + r * 256 + (((2 * c8 + 1) ^ r) << 2));
+                    const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    float h1[8], o1[8];
+                    unpack8(hb[q % 3][it][0], h1);
+                    if constexpr (GLU) {
+                        float h3[8], o3[8];
+                        unpack8(hb[q % 3][it][NH - 1], h3);
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) {
+                            o1[k] = v[k] * h3[k] * silu_gradf_(h1[k]);
+                            o3[k] = v[k] * siluf_(h1[k]);
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b128(pack8(o3), rd,
+                            ok ? (uint32_t)(rt * ldc + n + ffn) * 2 : OUT, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+                            o1[k] = v[k] * ((EPI == EPI_DN_RELU) ? (h1[k] > 0.f ? 1.f : 0.f) : gelu_gradf_(h1[k]));
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(pack8(o1), rd, ok ? (uint32_t)(rt * ldc + n) * 2 : OUT, 0, 0);
+                }
+            }
+            return;
+        }
+        // MLP forward: straight from the accumulator layout
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int ml = rb + i * 32 + rr;               // local row
@@ -704,25 +804,6 @@ gemm_bf16_kernel(GemmParams p) {
                         }
                         store4(reinterpret_cast<bf16*>(p.C2) + row * p.ldc + n, v);
                         store4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + n, a);
-                    } else if (EPI == EPI_DN_SWIGLU) {
-                        float h1[4], h3[4], d1[4], d3[4];
-                        load4(p.H + row * p.ldh + n, h1);
-                        load4(p.H + row * p.ldh + p.ffn + n, h3);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            d1[q] = v[q] * h3[q] * silu_gradf_(h1[q]);
-                            d3[q] = v[q] * siluf_(h1[q]);
-                        }
-                        bf16* dH = reinterpret_cast<bf16*>(p.C);
-                        store4(dH + row * p.ldc + n, d1);
-                        store4(dH + row * p.ldc + p.ffn + n, d3);
-                    } else if (EPI == EPI_DN_RELU || EPI == EPI_DN_GELU) {
-                        float h[4];
-                        load4(p.H + row * p.ldh + n, h);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            v[q] *= (EPI == EPI_DN_RELU) ? (h[q] > 0.f ? 1.f : 0.f) : gelu_gradf_(h[q]);
-                        store4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + n, v);
                     }
                 }
             }
