@@ -388,6 +388,53 @@ gemm_bf16_kernel(GemmParams p) {
             acc[ii][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[jj], f.a[ii], acc[ii][jj], 0, 0, 0);
         };
 
+        // EPI_SGD: the tile's fp32 masters (and bf16 copies), and its first two passes of
+        // masters loaded before the main loop (they arrive with the first k-tile's loads)
+        const int qt = tid & 63, rs = wave;            // a wavefront updates whole rows
+        const int n = n0 + qt * 4;
+        const bool col_ok = n < p.N;
+        const float nlr = -p.lr;
+        float* const M1 = reinterpret_cast<float*>(p.C);
+        float* const M2 = reinterpret_cast<float*>(p.C2);
+        bf16* const W1 = reinterpret_cast<bf16*>(p.W);
+        bf16* const W2 = reinterpret_cast<bf16*>(p.W2);
+        const int c2 = M2 ? p.c2_mstart : 0x7fffffff;
+        const long ldc = p.ldc, eoff = (long)e * p.ces;
+        // Tile rows [0, n1) are rows m0.. of C (W), rows [n1, rows_valid) rows of C2 (W2).
+        // One buffer descriptor per half bounds the tile's rows up to column N, so that
+        // every load and store is issued unconditionally (exact wait counts) and a lane
+        // outside the tile gets an offset past the bound: its store is dropped and its
+        // load returns zeros.
+        const int n1 = max(0, min(rows_valid, c2 - m0));
+        const int n2 = rows_valid - n1;
+        const long b1 = eoff + (long)m0 * ldc, b2 = eoff + (long)max(m0 - c2, 0) * ldc;
+        const rsrc_t rm1 = make_rsrc(M1 + b1, n1 > 0 ? ((long)(n1 - 1) * ldc + p.N) * 4 : 0);
+        const rsrc_t rw1 = make_rsrc(W1 + b1, n1 > 0 ? ((long)(n1 - 1) * ldc + p.N) * 2 : 0);
+        const rsrc_t rm2 = n2 > 0 ? make_rsrc(M2 + b2, ((long)(n2 - 1) * ldc + p.N) * 4) : rm1;
+        const rsrc_t rw2 = n2 > 0 ? make_rsrc(W2 + b2, ((long)(n2 - 1) * ldc + p.N) * 2) : rw1;
+        constexpr uint32_t OUT = 0x80000000u;          // past every bound
+        // element offset of tile row ml (wave-uniform) at this thread's columns in its
+        // half, or OUT
+        auto elem = [&](int ml, bool& sec) -> uint32_t {
+            sec = ml >= n1;
+            const int r = sec ? ml - n1 : ml;
+            return (ml < rows_valid && col_ok) ? (uint32_t)((long)r * ldc + n) : OUT;
+        };
+        nf4 mb[3][8];
+        auto prefetch = [&](int q, nf4* dst) {
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                bool sec;
+                const uint32_t o = elem(q * 32 + it * 4 + rs, sec);
+                dst[it] = __builtin_bit_cast(nf4, __builtin_amdgcn_raw_buffer_load_b128(
+                    sec ? rm2 : rm1, o == OUT ? OUT : o * 4, 0, 2));
+            }
+        };
+        if constexpr (EPI == EPI_SGD) {
+            prefetch(0, mb[0]);
+            prefetch(1, mb[1]);
+        }
+
         if (nk > 0) {
 #pragma unroll
             for (int t = 0; t < DIST; ++t)
@@ -459,48 +506,6 @@ gemm_bf16_kernel(GemmParams p) {
                           "SGD epilogue: weight gradients, full wave layout");
             {
                 float* stage = reinterpret_cast<float*>(&lds[0][0][0]);   // 2 x 32 rows x 1 KB
-                const int qt = tid & 63, rs = wave;            // a wavefront updates whole rows
-                const int n = n0 + qt * 4;
-                const bool col_ok = n < p.N;
-                const float nlr = -p.lr;
-                float* const M1 = reinterpret_cast<float*>(p.C);
-                float* const M2 = reinterpret_cast<float*>(p.C2);
-                bf16* const W1 = reinterpret_cast<bf16*>(p.W);
-                bf16* const W2 = reinterpret_cast<bf16*>(p.W2);
-                const int c2 = M2 ? p.c2_mstart : 0x7fffffff;
-                const long ldc = p.ldc, eoff = (long)e * p.ces;
-                // Tile rows [0, n1) are rows m0.. of C (W), rows [n1, rows_valid) rows of C2 (W2).
-                // One buffer descriptor per half bounds the tile's rows up to column N, so that
-                // every load and store is issued unconditionally (exact wait counts) and a lane
-                // outside the tile gets an offset past the bound: its store is dropped and its
-                // load returns zeros.
-                const int n1 = max(0, min(rows_valid, c2 - m0));
-                const int n2 = rows_valid - n1;
-                const long b1 = eoff + (long)m0 * ldc, b2 = eoff + (long)max(m0 - c2, 0) * ldc;
-                const rsrc_t rm1 = make_rsrc(M1 + b1, n1 > 0 ? ((long)(n1 - 1) * ldc + p.N) * 4 : 0);
-                const rsrc_t rw1 = make_rsrc(W1 + b1, n1 > 0 ? ((long)(n1 - 1) * ldc + p.N) * 2 : 0);
-                const rsrc_t rm2 = n2 > 0 ? make_rsrc(M2 + b2, ((long)(n2 - 1) * ldc + p.N) * 4) : rm1;
-                const rsrc_t rw2 = n2 > 0 ? make_rsrc(W2 + b2, ((long)(n2 - 1) * ldc + p.N) * 2) : rw1;
-                constexpr uint32_t OUT = 0x80000000u;          // past every bound
-                // element offset of tile row ml (wave-uniform) at this thread's columns in its
-                // half, or OUT
-                auto elem = [&](int ml, bool& sec) -> uint32_t {
-                    sec = ml >= n1;
-                    const int r = sec ? ml - n1 : ml;
-                    return (ml < rows_valid && col_ok) ? (uint32_t)((long)r * ldc + n) : OUT;
-                };
-                nf4 mb[3][8];
-                auto prefetch = [&](int q, nf4* dst) {
-#pragma unroll
-                    for (int it = 0; it < 8; ++it) {
-                        bool sec;
-                        const uint32_t o = elem(q * 32 + it * 4 + rs, sec);
-                        dst[it] = __builtin_bit_cast(nf4, __builtin_amdgcn_raw_buffer_load_b128(
-                            sec ? rm2 : rm1, o == OUT ? OUT : o * 4, 0, 2));
-                    }
-                };
-                prefetch(0, mb[0]);
-                prefetch(1, mb[1]);
                 __syncthreads();                               // every wave is past its last LDS read
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
