@@ -12,15 +12,15 @@ HBM traffic per stage, from two counter runs:
 Kernel time per kernel, from one kernel-trace run:
 
     rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o kt -- \\
-        python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline
+        python3 bench.py --steps 5 --warmup 2 --gemm-steps 0 --no-cpu-baseline
     python -m sparse_mixture_experts_gate_amd.profile_summary --stats OUT/trace/kt_kernel_stats.csv \\
-        --steps 7 --markdown M --command "..."
+        --trace OUT/trace/kt_kernel_trace.csv --steps 7 --markdown M --command "..."
 
 MFMA utilisation and clock per GEMM stage, from one counter run:
 
     rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 \\
         SQ_INSTS_MFMA SQ_CYCLES GRBM_GUI_ACTIVE -d OUT/mfma -o mfma --output-format csv -- \\
-        python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline
+        python3 bench.py --steps 1 --warmup 0 --gemm-steps 0 --no-cpu-baseline
     python -m sparse_mixture_experts_gate_amd.profile_summary --mfma OUT/mfma/mfma_counter_collection.csv \\
         --markdown M --command "..."
 
@@ -178,8 +178,36 @@ def _short(name):
     return name[:120]
 
 
-def stats_markdown(path, steps, title, command):
-    """Per-kernel calls / total / average / min / max from a rocprofv3 kernel_stats.csv."""
+def stage_durations(trace_csv):
+    """Per stage of the training step, from a rocprofv3 kernel_trace.csv: launches per
+    step, average launch duration and time per step, over every traced step.  The
+    library's kernels are mapped to stages in launch order; a step starts at the
+    router-logits GEMM."""
+    rows = list(csv.DictReader(open(trace_csv)))
+    key = "Dispatch_Id" if rows and "Dispatch_Id" in rows[0] else "Start_Timestamp"
+    rows.sort(key=lambda r: int(r[key]))
+    acc, steps, state = {}, 0, {"stage": None, "wgrad": 0}
+    for r in rows:
+        st = _stage_of(r["Kernel_Name"], state)
+        if st == "router_logits":
+            steps += 1
+            state = {"stage": None, "wgrad": 0}
+            st = _stage_of(r["Kernel_Name"], state)
+        if steps == 0 or st is None:
+            continue
+        state["stage"] = st
+        e = acc.setdefault(st, {"ns": 0, "launches": 0})
+        e["ns"] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        e["launches"] += 1
+    return steps, {st: {"launches_per_step": e["launches"] / steps,
+                        "avg_launch_ms": e["ns"] / e["launches"] / 1e6,
+                        "ms_per_step": e["ns"] / steps / 1e6} for st, e in acc.items()}
+
+
+def stats_markdown(path, steps, title, command, trace_csv=None):
+    """Per-kernel calls / total / average / min / max from a rocprofv3 kernel_stats.csv,
+    and with the kernel_trace.csv of the same run, the same per stage of the step (one
+    kernel template can serve two stages, e.g. both weight-gradient GEMMs)."""
     rows = list(csv.DictReader(open(path)))
     lines = [f"# {title}", "", "Command (repository root, one MI355X):", "", "```", command, "```", "",
              f"{steps} training steps are traced (warm-up and timed); per-step time = total / {steps}.",
@@ -192,6 +220,13 @@ def stats_markdown(path, steps, title, command):
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {tot:.2f} | {tot / steps:.3f} | "
                      f"{float(r['AverageNs']) / 1e6:.3f} | {float(r['MinNs']) / 1e6:.3f} | "
                      f"{float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
+    if trace_csv:
+        n, per = stage_durations(trace_csv)
+        lines += ["", f"Per stage of the step, from the per-dispatch trace of the same run ({n} steps):", "",
+                  "| stage | launches per step | average launch (ms) | ms per step |", "|---|---|---|---|"]
+        for st, e in per.items():
+            lines.append(f"| {st} | {e['launches_per_step']:g} | {e['avg_launch_ms']:.3f} | {e['ms_per_step']:.3f} |")
+        lines.append(f"| total | | | {sum(e['ms_per_step'] for e in per.values()):.3f} |")
     return "\n".join(lines) + "\n"
 
 
@@ -262,13 +297,14 @@ def main(argv=None):
     if argv and argv[0] == "--stats":
         ap = argparse.ArgumentParser()
         ap.add_argument("--stats", required=True)
+        ap.add_argument("--trace", help="kernel_trace.csv of the same run: per-stage table")
         ap.add_argument("--steps", type=int, required=True)
         ap.add_argument("--workload", default="grouped_sigmoid_t32768_d7168_e256")
         ap.add_argument("--markdown", required=True)
         ap.add_argument("--command", default="")
         a = ap.parse_args(argv)
         open(a.markdown, "w").write(stats_markdown(a.stats, a.steps, f"Kernel trace, training step, {a.workload}",
-                                                   a.command))
+                                                   a.command, a.trace))
         return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("fetch_csv")
