@@ -49,6 +49,11 @@ the design notes of the repository.
       this rule and no bias, selection ranks fl32(s).
   R19 route scale: the renormalised gates are multiplied by a constant
       (default 1); its gradient enters through the renormalisation.
+  R20 shared experts (optional): a replicated branch that every token goes
+      through, one SwiGLU with hidden size n_shared * ffn (weights Ws1, Ws3
+      [Hs, d] and Ws2 [d, Hs]); its output is added to the routed combine with
+      no gate, so its upstream gradient is dY itself; it is trained by the same
+      SGD.
 
 Parity pins (tests/test_oracle_*.py): brute-force top-k over all subsets,
 gates summing to one and closed forms of the renormalisation, routing
@@ -426,9 +431,26 @@ def route(X, Wg, shp: Shape, topk_idx=None, e_bias=None):
             "q": aux_probs(l, shp.score)}
 
 
+def shared_forward(X, P):
+    """Shared branch (R20): one SwiGLU with weights Ws1, Ws3, Ws2 over every token."""
+    return expert_forward("swiglu", X, P["Ws1"], None, P["Ws2"], None, P["Ws3"])
+
+
+def shared_backward(X, P, saved, dY):
+    """Gradients of the shared branch: its output enters Y with no gate, so the
+    upstream gradient is dY itself (R20)."""
+    g = expert_backward("swiglu", X, P["Ws1"], P["Ws2"], P["Ws3"], saved, dY)
+    return {"dWs1": g["dW1"], "dWs2": g["dW2"], "dWs3": g["dW3"], "dX": g["dXp"]}
+
+
+# trained parameters: router, routed experts, shared branch (R20)
+PARAM_NAMES = ("Wg", "W1", "b1", "W2", "b2", "W3", "Ws1", "Ws2", "Ws3")
+
+
 def layer_forward(X, P: Dict[str, Optional[np.ndarray]], shp: Shape, topk_idx=None):
-    """Forward of the whole layer.  P holds Wg, W1, b1, W2, b2, W3 (float64) and
-    optionally e_bias, the correction bias (R17), which no gradient reaches."""
+    """Forward of the whole layer.  P holds Wg, W1, b1, W2, b2, W3 (float64),
+    optionally the shared branch Ws1, Ws2, Ws3 (R20), and optionally e_bias, the
+    correction bias (R17), which no gradient reaches."""
     fw = route(X, P["Wg"], shp, topk_idx, P.get("e_bias"))
     r = fw["routing"]
     T, d = X.shape
@@ -445,6 +467,9 @@ def layer_forward(X, P: Dict[str, Optional[np.ndarray]], shp: Shape, topk_idx=No
     fw["EO"] = EO
     fw["saved"] = saved
     fw["Y"] = combine(EO, r.slot_of, fw["gates"])
+    if P.get("Ws1") is not None:                # shared branch over every token (R20)
+        fw["shared"] = shared_forward(X, P)
+        fw["Y"] = fw["Y"] + fw["shared"]["EO"]
     aux, f, Pm = aux_loss(r.counts, fw["q"], shp.k)
     fw["aux"], fw["f"], fw["P"] = aux, f, Pm
     return fw
@@ -474,6 +499,10 @@ def layer_backward(X, P, shp: Shape, fw, dY, aux_coef):
                 grads[n][e] = g[n]
         dXp[lo:hi] = g["dXp"]
     dX = scatter_rows(dXp, r.slot_of)
+    if P.get("Ws1") is not None:                # shared branch: upstream gradient dY (R20)
+        gs = shared_backward(X, P, fw["shared"], dY)
+        grads["dWs1"], grads["dWs2"], grads["dWs3"] = gs["dWs1"], gs["dWs2"], gs["dWs3"]
+        dX = dX + gs["dX"]
     dw = renorm_backward(dgate, fw["gates"], fw["w"], shp.route_scale)
     dq = aux_grad_q(r.counts, T, shp.k, E, aux_coef)
     dl = router_backward(fw["logits"], r.topk_idx, dw, dq, shp.score)
@@ -491,6 +520,6 @@ def train_step(X, Yt, P, shp: Shape, lr, aux_coef, topk_idx=None):
     loss = m + aux_coef * fw["aux"]
     grads = layer_backward(X, P, shp, fw, dY, aux_coef)
     newP = {"e_bias": P.get("e_bias")}          # the correction bias is not trained (R17)
-    for n in ("Wg", "W1", "b1", "W2", "b2", "W3"):
+    for n in PARAM_NAMES:
         newP[n] = None if P.get(n) is None else sgd(P[n], grads["d" + n], lr)
     return {"fw": fw, "grads": grads, "mse": m, "loss": loss, "params": newP, "dY": dY}

@@ -10,6 +10,7 @@ from oracle import moe_oracle as O
 
 import tests.test_oracle_layer as L
 import tests.test_oracle_routing as R
+import tests.test_oracle_shared as S
 import tests.test_oracle_variants as V
 
 
@@ -96,6 +97,25 @@ def _scale_missing_in_backward(dgate, gates, w, route_scale=1.0):
     return _orig_renorm_backward(dgate, gates, w, 1.0)
 
 
+_orig_shared_backward = O.shared_backward
+
+
+def _shared_roles_swapped(X, P):
+    # gate and up projections exchanged: A = silu(X Ws3^T) * (X Ws1^T)
+    return O.expert_forward("swiglu", X, P["Ws3"], None, P["Ws2"], None, P["Ws1"])
+
+
+def _shared_dx_dropped(X, P, saved, dY):
+    g = _orig_shared_backward(X, P, saved, dY)
+    g["dX"] = np.zeros_like(g["dX"])
+    return g
+
+
+def _shared_half_gradient(X, P, saved, dY):
+    # upstream gradient scaled as if the branch carried a gate of 1/2
+    return _orig_shared_backward(X, P, saved, 0.5 * dY)
+
+
 def _run_all(fns):
     failed = 0
     for fn, args in fns:
@@ -123,6 +143,9 @@ PINS = [
     (V.test_golden_bias_selects_and_gates_stay_unbiased, ()),
     (V.test_route_scale_gates_sum_to_the_scale, (2.5,)),
     (V.test_variant_central_differences, ()),
+    (S.test_shared_branch_is_one_routed_expert_over_every_token, ("swiglu",)),
+    (S.test_shared_central_differences, ("swiglu",)),
+    (S.test_zero_output_projection_and_linearity, ()),
 ]
 
 
@@ -139,6 +162,9 @@ PINS = [
     ("select_topk", _group_rule_ignored),
     ("gate_weights", _scale_dropped),
     ("renorm_backward", _scale_missing_in_backward),
+    ("shared_forward", _shared_roles_swapped),
+    ("shared_backward", _shared_dx_dropped),
+    ("shared_backward", _shared_half_gradient),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, repl):
     monkeypatch.setattr(O, name, repl)
