@@ -44,7 +44,9 @@ def stage_work(w, fused=False):
     n_up, n_dn = E * hid * d, E * d * ffn              # expert parameters of each projection
     n_small = E * d + (0 if glu else E * ffn + E * d)  # router weight and biases
     wg_out = 8 + s if fused else 4                     # per weight-gradient element
-    sgd_params = n_small if fused else n_small + n_up + n_dn
+    hs = getattr(w, "n_shared", 0) * ffn               # shared branch hidden width
+    n_sh = 3 * hs * d                                  # shared-branch parameters
+    sgd_params = n_small if fused else n_small + n_up + n_dn + n_sh
 
     def fl(n):
         return {"flop": n, "byte": 0}
@@ -60,8 +62,11 @@ def stage_work(w, fused=False):
         "up_fwd": {"flop": 2.0 * R * d * hid, "byte": (R * d + n_up + R * hid + R * ffn) * s},
         # A, W2 in; EO out
         "down_fwd": {"flop": 2.0 * R * ffn * d, "byte": (R * ffn + n_dn + R * d) * s},
-        # read k rows, gates, slots; write Y; read Y_target; write dY
-        "combine_loss": by((R * d + 3 * T * d) * s + R * 8),
+        # shared branch over all T rows: [H1|H3] = X [Ws1;Ws3]^T, A, Ys = A Ws2^T
+        "shared_fwd": {"flop": 6.0 * T * d * hs,
+                       "byte": (T * d + 2 * hs * d + 3 * T * hs + hs * d + T * d) * s if hs else 0},
+        # read k rows, gates, slots (and Ys); write Y; read Y_target; write dY
+        "combine_loss": by((R * d + 3 * T * d + (T * d if hs else 0)) * s + R * 8),
         # read dY and k rows of EO, write k rows of dEO; slots, gates, dgate
         "combine_bwd": by((T * d + 2 * R * d) * s + R * 12),
         # dEO, W2, H in; dH out
@@ -72,12 +77,18 @@ def stage_work(w, fused=False):
         "up_dgrad": {"flop": 2.0 * R * hid * d, "byte": (R * hid + n_up + R * d) * s},
         # dH, Xp in; dW1|dW3 out (or the SGD step on W1|W3)
         "up_wgrad": {"flop": 2.0 * R * hid * d, "byte": (R * hid + R * d) * s + n_up * wg_out},
+        # shared branch backward, its four contractions from dY: dgrad + activation
+        # backward (dY, Ws2, H in; dH out), dWs2 (dY, A in), dXs (dH, Ws1|Ws3 in; dXs out),
+        # dWs1|dWs3 (dH, X in); weight gradients out (or the SGD step)
+        "shared_bwd": {"flop": 12.0 * T * d * hs,
+                       "byte": ((T * d + hs * d + 4 * T * hs) + (T * d + T * hs) + (2 * T * hs + 2 * hs * d
+                                + T * d) + (2 * T * hs + T * d)) * s + n_sh * wg_out if hs else 0},
         "bias_grads": by((R * d + R * ffn) * s if not glu else 0),
         "router_bwd": by(T * E * (4 + s) + T * k * 16),
         "router_dwg": {"flop": 2.0 * T * E * d, "byte": (T * E + T * d) * s + E * d * 4},
         "router_dx": {"flop": 2.0 * T * E * d, "byte": (T * E + E * d) * s + T * d * 4},
-        # read k rows of dXp and the fp32 router part, write dX, read slots
-        "scatter": by(R * d * s + T * d * (4 + s) + R * 4),
+        # read k rows of dXp, the fp32 router part (and the shared part), write dX, read slots
+        "scatter": by(R * d * s + T * d * (4 + s) + (T * d * s if hs else 0) + R * 4),
         # master read + write, gradient read, working copy write
         "sgd": by(sgd_params * (4 + 4 + 4 + s)),
     }
@@ -219,6 +230,9 @@ def main(argv=None) -> int:
     ap.add_argument("--sgd", choices=("fused", "stored"), default="fused",
                     help="fused: the expert weight-gradient GEMMs apply the SGD step themselves "
                          "(no expert gradients stored); stored: gradients written, then one SGD pass")
+    ap.add_argument("--shared-experts", type=int, default=0,
+                    help="add the shared-experts branch: one SwiGLU of hidden N * ffn over every "
+                         "token, timed as its own stages")
     ap.add_argument("--gemm-steps", type=int, default=3,
                     help="with --sgd fused: profiled steps that store the expert gradients, run "
                          "after the timed region, for the GEMM-only stage times")
@@ -237,6 +251,8 @@ def main(argv=None) -> int:
     from sparse_mixture_experts_gate_amd import workloads as W
 
     w = W.BY_NAME[a.workload]
+    if a.shared_experts:
+        w = w.replace(n_shared=a.shared_experts)
     dev = "cuda"
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
@@ -247,12 +263,12 @@ def main(argv=None) -> int:
     fused = a.sgd == "fused"
     g = L.alloc_grads(w, dev)
     if fused:
-        for n in ("dW1", "dW2", "dW3"):
+        for n in ("dW1", "dW2", "dW3", "dWs1", "dWs2", "dWs3"):
             g.pop(n, None)
     Y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
     loss = torch.empty(3, dtype=torch.float32, device=dev)
     params = {}
-    for n in ("Wg", "W1", "b1", "W2", "b2", "W3"):
+    for n in ("Wg", "W1", "b1", "W2", "b2", "W3", "Ws1", "Ws3", "Ws2"):
         if inp.get(n) is not None:
             params[n] = inp[n]
             params[n + "_w"] = inp[n + "_w"]
@@ -360,7 +376,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "ffn": w.ffn, "k": w.k,
                    "n_groups": w.n_groups, "topk_groups": w.topk_groups, "score": w.score,
-                   "expert": w.expert, "step": "forward+loss+backward+sgd",
+                   "expert": w.expert, "n_shared": w.n_shared, "step": "forward+loss+backward+sgd",
                    "sgd": "fused into the expert weight-gradient GEMMs" if fused
                    else "one pass over stored gradients"},
         "roofline": roof,

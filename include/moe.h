@@ -88,8 +88,13 @@ extern "C" {
  * Selection values: the logits when group_score == MOE_GROUP_MAX and no
  * correction bias is given (exact); otherwise the fp32 scores (softmax
  * probabilities or sigmoid values) plus the correction bias, added in fp32.
+ * n_shared >= 0 and n_shared * ffn <= 2^24: the shared-experts branch, one
+ * SwiGLU over every token with hidden width Hs = n_shared * ffn (0 = none).
  * Kernel limits (MOE_ERR_UNSUPPORTED): E <= 256, k <= 16; float32: d and ffn
- * multiples of 4; bfloat16: d and ffn multiples of 64 and E a multiple of 8.
+ * multiples of 4; bfloat16: d and ffn multiples of 64, E a multiple of 8, and
+ * T * max(d, hcols, 2 Hs) * 2 < 2^31 (hcols = 2 ffn for SwiGLU, else ffn): an
+ * expert's rows of a k-strided GEMM operand, up to T of them, must span less
+ * than 2 GiB.
  */
 typedef struct moe_config {
     int32_t T;            /* tokens */
@@ -104,6 +109,7 @@ typedef struct moe_config {
     int32_t dtype;        /* MOE_DTYPE_* */
     int32_t group_score;  /* MOE_GROUP_* */
     float   route_scale;  /* gate multiplier after renormalisation; 0 = 1 */
+    int32_t n_shared;     /* shared experts (hidden Hs = n_shared * ffn); 0 = none */
 } moe_config;
 
 /*
@@ -114,6 +120,10 @@ typedef struct moe_config {
  * = none; only with MOE_SCORE_SIGMOID, else MOE_ERR_INVALID_ARG): it is added
  * to the scores for selection only; gates and every gradient use the unbiased
  * scores, and no gradient is computed for it.
+ * Shared-experts branch ("AI Infra Kernel Lab", the benchmark's shared branch:
+ * one replicated SwiGLU whose output is added to the routed combine with no
+ * gate): Ws1, Ws3 [Hs,d] and Ws2 [d,Hs] in the working dtype, required when
+ * n_shared > 0 and ignored otherwise.
  */
 typedef struct moe_weights {
     const void* Wg;
@@ -123,6 +133,9 @@ typedef struct moe_weights {
     const void* b2;
     const void* W3;
     const float* e_bias;
+    const void* Ws1;
+    const void* Ws3;
+    const void* Ws2;
 } moe_weights;
 
 /*
@@ -150,8 +163,9 @@ typedef struct moe_routing {
 
 /*
  * Gradients written by moe_backward / moe_train_step.  dX is dtype [T,d]
- * (expert path plus router path); the rest are float32 with the shapes of
- * the weights.  db1/db2 are required for the MLP kinds, dW3 for SwiGLU.
+ * (expert path plus router path plus shared branch); the rest are float32
+ * with the shapes of the weights.  db1/db2 are required for the MLP kinds,
+ * dW3 for SwiGLU, dWs1/dWs3/dWs2 when n_shared > 0.
  */
 typedef struct moe_grads {
     void*  dX;
@@ -161,6 +175,9 @@ typedef struct moe_grads {
     float* dW2;
     float* db2;
     float* dW3;
+    float* dWs1;
+    float* dWs3;
+    float* dWs2;
 } moe_grads;
 
 /*
@@ -174,6 +191,8 @@ typedef struct moe_params {
     float* Wg;  float* W1;  float* b1;  float* W2;  float* b2;  float* W3;
     void*  Wg_w; void* W1_w; void* b1_w; void* W2_w; void* b2_w; void* W3_w;
     const float* e_bias;
+    float* Ws1; float* Ws3; float* Ws2;        /* shared branch (n_shared > 0) */
+    void*  Ws1_w; void* Ws3_w; void* Ws2_w;
 } moe_params;
 
 /* Workspace buffers whose byte offsets moe_workspace_offset() reports.
@@ -234,14 +253,15 @@ int moe_backward(const moe_config* cfg, const void* X, const moe_weights* w,
  * parameter (masters, then working copies).  Y_target dtype [T,d].
  * Writes Y, *r, *g and loss_out (device float[3] = {mse, aux, loss}).
  *
- * The expert weight gradients g->dW1, g->dW2 (and g->dW3 for SwiGLU) are
- * either all given or all NULL; a mix fails with MOE_ERR_NULL_PTR.  When
- * they are NULL, nothing is stored for them: the weight-gradient
- * contractions apply the SGD step to W1, W2 (W3) and their working copies
- * directly, which saves writing and re-reading those gradients (about 8
- * bytes per expert parameter).  Each updated value is the same in both
- * modes: master = fma(-lr, grad, master) in float32, with grad the same
- * float32 sum.  The other gradients (dX, dWg, db1, db2) are always written.
+ * The expert weight gradients g->dW1, g->dW2 (g->dW3 for SwiGLU; g->dWs1,
+ * g->dWs3, g->dWs2 when n_shared > 0) are either all given or all NULL; a
+ * mix fails with MOE_ERR_NULL_PTR.  When they are NULL, nothing is stored
+ * for them: the weight-gradient contractions apply the SGD step to those
+ * weights and their working copies directly, which saves writing and
+ * re-reading the gradients (about 8 bytes per expert parameter).  Each
+ * updated value is the same in both modes: master = fma(-lr, grad, master)
+ * in float32, with grad the same float32 sum.  The other gradients (dX, dWg,
+ * db1, db2) are always written.
  */
 int moe_train_step(const moe_config* cfg, const void* X, const void* Y_target,
                    moe_params* p, float lr, float aux_coef,
@@ -254,20 +274,22 @@ int moe_train_step(const moe_config* cfg, const void* X, const void* Y_target,
 #define MOE_STAGE_GATHER          2   /* F4  Xp = X[token_of]                    */
 #define MOE_STAGE_UP_FWD          3   /* F5  H = Xp W1^T (|W3^T), A = act(H)      */
 #define MOE_STAGE_DOWN_FWD        4   /* F6  EO = A W2^T (+ b2)                   */
-#define MOE_STAGE_COMBINE_LOSS    5   /* F7-F8 Y, MSE, dY, loss scalars           */
-#define MOE_STAGE_COMBINE_BWD     6   /* B1  dgate, dEO                           */
-#define MOE_STAGE_DOWN_DGRAD      7   /* B2  dA = dEO W2, activation backward     */
-#define MOE_STAGE_DOWN_WGRAD      8   /* B3  dW2 = dEO^T A (fused: + SGD on W2)    */
-#define MOE_STAGE_UP_DGRAD        9   /* B4  dXp = dH W1 (+ dH3 W3)               */
-#define MOE_STAGE_UP_WGRAD       10   /* B5  dW1 (| dW3) = dH^T Xp (fused: + SGD)  */
-#define MOE_STAGE_BIAS_GRADS     11   /*     db1, db2 (MLP kinds)                 */
-#define MOE_STAGE_ROUTER_BWD     12   /* B7  dlogits                              */
-#define MOE_STAGE_ROUTER_DWG     13   /* B8  dWg = dl^T X                         */
-#define MOE_STAGE_ROUTER_DX      14   /* B8  router part of dX = dl Wg            */
-#define MOE_STAGE_SCATTER        15   /* B6  dX = sum of dXp rows + router part   */
-#define MOE_STAGE_SGD            16   /* S1  masters and working copies (fused:
+#define MOE_STAGE_SHARED_FWD      5   /*     shared branch Ys = SwiGLU(X) (n_shared > 0) */
+#define MOE_STAGE_COMBINE_LOSS    6   /* F7-F8 Y (+ Ys), MSE, dY, loss scalars    */
+#define MOE_STAGE_COMBINE_BWD     7   /* B1  dgate, dEO                           */
+#define MOE_STAGE_DOWN_DGRAD      8   /* B2  dA = dEO W2, activation backward     */
+#define MOE_STAGE_DOWN_WGRAD      9   /* B3  dW2 = dEO^T A (fused: + SGD on W2)    */
+#define MOE_STAGE_UP_DGRAD       10   /* B4  dXp = dH W1 (+ dH3 W3)               */
+#define MOE_STAGE_UP_WGRAD       11   /* B5  dW1 (| dW3) = dH^T Xp (fused: + SGD)  */
+#define MOE_STAGE_SHARED_BWD     12   /*     shared branch dgrad and wgrad (fused: + SGD) */
+#define MOE_STAGE_BIAS_GRADS     13   /*     db1, db2 (MLP kinds)                 */
+#define MOE_STAGE_ROUTER_BWD     14   /* B7  dlogits                              */
+#define MOE_STAGE_ROUTER_DWG     15   /* B8  dWg = dl^T X                         */
+#define MOE_STAGE_ROUTER_DX      16   /* B8  router part of dX = dl Wg            */
+#define MOE_STAGE_SCATTER        17   /* B6  dX = sum of dXp rows + router part (+ shared) */
+#define MOE_STAGE_SGD            18   /* S1  masters and working copies (fused:
                                            Wg and the biases only)                  */
-#define MOE_NUM_STAGES           17
+#define MOE_NUM_STAGES           19
 
 /*
  * moe_train_step with timing marks: the same launches, plus

@@ -28,9 +28,9 @@ EXPORTS = ["moe_workspace_bytes", "moe_workspace_offset", "moe_route", "moe_forw
            "moe_backward", "moe_train_step", "moe_train_step_profiled", "moe_status_string",
            "moe_abi_version"]
 
-STAGES = ["router_logits", "route", "gather", "up_fwd", "down_fwd", "combine_loss", "combine_bwd",
-          "down_dgrad", "down_wgrad", "up_dgrad", "up_wgrad", "bias_grads", "router_bwd",
-          "router_dwg", "router_dx", "scatter", "sgd"]
+STAGES = ["router_logits", "route", "gather", "up_fwd", "down_fwd", "shared_fwd", "combine_loss",
+          "combine_bwd", "down_dgrad", "down_wgrad", "up_dgrad", "up_wgrad", "shared_bwd", "bias_grads",
+          "router_bwd", "router_dwg", "router_dx", "scatter", "sgd"]
 
 
 class MoeError(RuntimeError):
@@ -42,11 +42,13 @@ class MoeError(RuntimeError):
 class moe_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "d", "E", "ffn", "k", "n_groups", "topk_groups", "score", "expert", "dtype",
-                 "group_score")] + [("route_scale", ctypes.c_float)]
+                 "group_score")] + [("route_scale", ctypes.c_float), ("n_shared", ctypes.c_int32)]
 
 
-WEIGHTS = ("Wg", "W1", "b1", "W2", "b2", "W3", "e_bias")
-PARAMS = ("Wg", "W1", "b1", "W2", "b2", "W3", "Wg_w", "W1_w", "b1_w", "W2_w", "b2_w", "W3_w", "e_bias")
+WEIGHTS = ("Wg", "W1", "b1", "W2", "b2", "W3", "e_bias", "Ws1", "Ws3", "Ws2")
+PARAMS = ("Wg", "W1", "b1", "W2", "b2", "W3", "Wg_w", "W1_w", "b1_w", "W2_w", "b2_w", "W3_w", "e_bias",
+          "Ws1", "Ws3", "Ws2", "Ws1_w", "Ws3_w", "Ws2_w")
+GRADS = ("dX", "dWg", "dW1", "db1", "dW2", "db2", "dW3", "dWs1", "dWs3", "dWs2")
 
 
 class moe_weights(ctypes.Structure):
@@ -59,7 +61,7 @@ class moe_routing(ctypes.Structure):
 
 
 class moe_grads(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("dX", "dWg", "dW1", "db1", "dW2", "db2", "dW3")]
+    _fields_ = [(n, ctypes.c_void_p) for n in GRADS]
 
 
 class moe_params(ctypes.Structure):
@@ -118,7 +120,8 @@ def config(w, group_score=None, route_scale=None) -> moe_config:
     gs = group_score if group_score is not None else getattr(w, "group_score", "max")
     rs = route_scale if route_scale is not None else getattr(w, "route_scale", 1.0)
     return moe_config(w.T, w.d, w.E, w.ffn, w.k, w.n_groups, w.topk_groups, code(SCORE, w.score),
-                      code(EXPERT, w.expert), code(DTYPE, w.dtype), code(GROUP, gs), float(rs))
+                      code(EXPERT, w.expert), code(DTYPE, w.dtype), code(GROUP, gs), float(rs),
+                      int(getattr(w, "n_shared", 0)))
 
 
 def _p(t: Optional[torch.Tensor]):
@@ -162,7 +165,7 @@ def weights_struct(w: dict) -> moe_weights:
 
 
 def grads_struct(g: dict) -> moe_grads:
-    return moe_grads(*[_p(g.get(n)) for n in ("dX", "dWg", "dW1", "db1", "dW2", "db2", "dW3")])
+    return moe_grads(*[_p(g.get(n)) for n in GRADS])
 
 
 def params_struct(p: dict) -> moe_params:
@@ -287,6 +290,11 @@ def alloc_grads(w, device) -> dict:
     else:
         g["db1"] = torch.empty(w.E, w.ffn, dtype=f32, device=device)
         g["db2"] = torch.empty(w.E, w.d, dtype=f32, device=device)
+    hs = getattr(w, "n_shared", 0) * w.ffn
+    if hs:
+        g["dWs1"] = torch.empty(hs, w.d, dtype=f32, device=device)
+        g["dWs3"] = torch.empty(hs, w.d, dtype=f32, device=device)
+        g["dWs2"] = torch.empty(w.d, hs, dtype=f32, device=device)
     return g
 
 

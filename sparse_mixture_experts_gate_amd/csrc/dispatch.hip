@@ -73,6 +73,12 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
                 for (int j = 0; j < N; ++j) acc[j] = fmaf(g[i], x[j], acc[j]);
             }
             const size_t o = (size_t)t * a.vec + v;
+            if (a.Ys) {                    // shared branch: added with no gate
+                float ys[N];
+                Vec16<T>::unpack(reinterpret_cast<const uint4*>(a.Ys)[o], ys);
+#pragma unroll
+                for (int j = 0; j < N; ++j) acc[j] += ys[j];
+            }
             reinterpret_cast<uint4*>(a.Y)[o] = Vec16<T>::pack(acc);
             if (LOSS) {
                 float yt[N], dy[N];
@@ -168,6 +174,12 @@ __global__ void __launch_bounds__(256) scatter_kernel(ScatterArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < N; ++j) acc[j] += dxr[v * N + j];
+        if (a.dXs) {                       // shared branch
+            float xs[N];
+            Vec16<T>::unpack(reinterpret_cast<const uint4*>(a.dXs)[(size_t)t * a.vec + v], xs);
+#pragma unroll
+            for (int j = 0; j < N; ++j) acc[j] += xs[j];
+        }
         reinterpret_cast<uint4*>(a.dX)[(size_t)t * a.vec + v] = Vec16<T>::pack(acc);
     }
 }
@@ -243,6 +255,18 @@ __global__ void __launch_bounds__(256) sgd_kernel(SgdArgs a) {
     }
 }
 
+__global__ void shared_table_kernel(int32_t* tab, int T) {
+    if (threadIdx.x != 0) return;
+    tab[0] = 0;
+    tab[1] = T;
+    for (int b = 0; b < 3; ++b) {
+        int32_t* tp = tab + 2 + b * (MOE_MAX_EXPERTS + 1);
+        const int bm = 64 << b;
+        tp[0] = 0;
+        tp[1] = (T + bm - 1) / bm;
+    }
+}
+
 // ---- host launchers ------------------------------------------------------------
 static inline dim3 tok_grid(int T) { return dim3((T + TOK_WAVES - 1) / TOK_WAVES); }
 int combine_loss_blocks(int T) { return (T + TOK_WAVES - 1) / TOK_WAVES; }
@@ -312,6 +336,11 @@ hipError_t launch_sgd(SgdArgs& a, int dtype, hipStream_t s) {
     a.blk0[a.nseg] = b;
     if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(sgd_kernel<float>, dim3(b), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(sgd_kernel<bf16>, dim3(b), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_shared_table(int32_t* tab, int T, hipStream_t s) {
+    hipLaunchKernelGGL(shared_table_kernel, dim3(1), dim3(64), 0, s, tab, T);
     return hipGetLastError();
 }
 

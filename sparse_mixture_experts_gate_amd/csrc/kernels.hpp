@@ -73,6 +73,7 @@ struct GatherArgs {
 };
 struct CombineArgs {
     const void* EO; const int32_t* slot_of; const float* gates; void* Y;
+    const void* Ys;        // shared-branch output [T, d] added to Y, or NULL
     const void* Yt;        // NULL: no loss
     void* dY;              // written when Yt != NULL: 2 (Y - Yt) / (T d)
     float* lpart;          // per-workgroup sum of squared residuals
@@ -86,6 +87,7 @@ struct CombineBwdArgs {
 };
 struct ScatterArgs {
     const void* dXp; const int32_t* slot_of; const float* dXr; void* dX;
+    const void* dXs;       // shared-branch part of dX [T, d] added last, or NULL
     int T, k, vec;
 };
 struct ColSumArgs {
@@ -93,7 +95,7 @@ struct ColSumArgs {
 };
 // One SGD launch updates up to MOE_SGD_MAX_SEG parameter tensors; segment s owns
 // workgroups [blk0[s], blk0[s+1]).
-constexpr int MOE_SGD_MAX_SEG = 6;
+constexpr int MOE_SGD_MAX_SEG = 9;
 struct SgdSeg {
     float* master; const float* grad; void* work; long n;
 };
@@ -112,6 +114,10 @@ hipError_t launch_colsum(const ColSumArgs& a, int dtype, hipStream_t s);
 // Fills blk0 from the segment sizes and launches one SGD kernel over all segments.
 hipError_t launch_sgd(SgdArgs& a, int dtype, hipStream_t s);
 int combine_loss_blocks(int T);
+// Tables of the shared-experts branch as one expert segment of all T rows:
+// offsets {0, T} in tab[0..1], then the m-tile prefix per tile height (64, 128,
+// 256 rows) at tab + 2 + b * (MOE_MAX_EXPERTS + 1), as the routing writes it.
+hipError_t launch_shared_table(int32_t* tab, int T, hipStream_t s);
 
 // ---- expert / router contractions -------------------------------------------------
 enum GemmEpi {

@@ -28,8 +28,13 @@ constexpr int kChunk = 64;
 
 enum WsBuf {
     B_XP = 0, B_H, B_A, B_EO, B_DEO, B_DH, B_DXP, B_DY, B_DXR, B_DL, B_DGATE, B_GATEOF,
-    B_HIST, B_CBASE, B_QPART, B_LPART, B_TPREFIX, B_DWGPART, B_COUNT
+    B_HIST, B_CBASE, B_QPART, B_LPART, B_TPREFIX, B_DWGPART,
+    // shared-experts branch: [H1 | H3] [T, 2 Hs], A [T, Hs], Ys [T, d], dH [T, 2 Hs],
+    // dX part [T, d], and its one-segment tables (offsets {0, T}, tile prefixes)
+    B_HS, B_AS, B_YS, B_DHS, B_DXS, B_STAB,
+    B_COUNT
 };
+constexpr int kSharedTab = 2 + 3 * (MOE_MAX_EXPERTS + 1);   // int32 entries of B_STAB
 
 struct Layout {
     size_t off[B_COUNT];
@@ -53,8 +58,11 @@ bool shape_ok(const moe_config* c) {
     if (c->group_score != MOE_GROUP_MAX && c->group_score != MOE_GROUP_TOP2_SUM) return false;
     if (c->group_score == MOE_GROUP_TOP2_SUM && c->n_groups > 1 && c->E / c->n_groups < 2) return false;
     if (!std::isfinite(c->route_scale) || c->route_scale < 0.f) return false;
+    if (c->n_shared < 0 || (int64_t)c->n_shared * c->ffn > (int64_t(1) << 24)) return false;
     return true;
 }
+
+inline int shared_hidden(const moe_config* c) { return c->n_shared * c->ffn; }
 
 inline float route_scale(const moe_config* c) { return c->route_scale == 0.f ? 1.f : c->route_scale; }
 
@@ -73,7 +81,9 @@ int supported(const moe_config* c) {
         if (c->d % 64 || c->ffn % 64 || c->E % 8) return MOE_ERR_UNSUPPORTED;
         // The grouped GEMMs address an expert's rows of a k-strided operand (up to T rows of
         // up to max(d, hcols) bf16) through one buffer descriptor with 32-bit offsets.
-        const int64_t widest = std::max<int64_t>(c->d, c->expert == MOE_EXPERT_SWIGLU ? 2 * (int64_t)c->ffn : c->ffn);
+        const int64_t widest = std::max<int64_t>({(int64_t)c->d,
+                                                  c->expert == MOE_EXPERT_SWIGLU ? 2 * (int64_t)c->ffn : c->ffn,
+                                                  2 * (int64_t)c->n_shared * c->ffn});
         if ((int64_t)c->T * widest * 2 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
     }
     return MOE_OK;
@@ -108,6 +118,13 @@ Layout layout(const moe_config* c) {
     // split-K partials of the router weight gradient (bf16 path only)
     const int nsplit = c->dtype == MOE_DTYPE_F32 ? 0 : router_dwg_splits(c->T);
     sz[B_DWGPART] = nsplit > 1 ? (size_t)nsplit * E * d * 4 : 0;
+    const size_t hs = shared_hidden(c);
+    sz[B_HS] = T * 2 * hs * s;
+    sz[B_AS] = T * hs * s;
+    sz[B_YS] = hs ? T * d * s : 0;
+    sz[B_DHS] = T * 2 * hs * s;
+    sz[B_DXS] = hs ? T * d * s : 0;
+    sz[B_STAB] = hs ? kSharedTab * 4 : 0;
     size_t o = 0;
     for (int b = 0; b < B_COUNT; ++b) {
         L.off[b] = o;
@@ -121,11 +138,17 @@ Layout layout(const moe_config* c) {
 // Device pointers of one call.  Token-sized tensors (tok = true) may be NULL
 // when T == 0, since they then hold no elements.
 struct Ptrs {
-    const void* list[40];
-    bool tok[40];
+    static constexpr int kMax = 64;
+    const void* list[kMax];
+    bool tok[kMax];
     int n = 0;
-    void add(const void* p, bool t = false) { list[n] = p; tok[n] = t; ++n; }
+    bool overflow = false;
+    void add(const void* p, bool t = false) {
+        if (n == kMax) { overflow = true; return; }
+        list[n] = p; tok[n] = t; ++n;
+    }
     int check(int T) const {
+        if (overflow) return MOE_ERR_INVALID_ARG;
         for (int i = 0; i < n; ++i) {
             if (!list[i]) {
                 if (tok[i] && T == 0) continue;
@@ -150,6 +173,7 @@ void add_weights(Ptrs& P, const moe_config* c, const moe_weights* w) {
     P.add(w->Wg); P.add(w->W1); P.add(w->W2);
     if (c->expert == MOE_EXPERT_SWIGLU) P.add(w->W3);
     else { P.add(w->b1); P.add(w->b2); }
+    if (c->n_shared > 0) { P.add(w->Ws1); P.add(w->Ws3); P.add(w->Ws2); }
 }
 
 void add_routing(Ptrs& P, const moe_routing* r, bool logits) {
@@ -164,6 +188,7 @@ void add_grads(Ptrs& P, const moe_config* c, const moe_grads* g, bool experts = 
     if (experts) {
         P.add(g->dW1); P.add(g->dW2);
         if (c->expert == MOE_EXPERT_SWIGLU) P.add(g->dW3);
+        if (c->n_shared > 0) { P.add(g->dWs1); P.add(g->dWs3); P.add(g->dWs2); }
     }
     if (c->expert != MOE_EXPERT_SWIGLU) { P.add(g->db1); P.add(g->db2); }
 }
@@ -221,6 +246,23 @@ ExpertGemmArgs expert_args(const Ctx& x, const moe_weights* w, const moe_routing
     return a;
 }
 
+// The shared-experts branch as one expert segment of all T rows: the expert
+// contractions run it with E = 1 and the token rows themselves in place of the
+// gathered rows.  Its tables (offsets {0, T}, tile prefixes) are in B_STAB.
+ExpertGemmArgs shared_args(const Ctx& x, const void* X, const moe_weights* w) {
+    const moe_config* c = x.c;
+    ExpertGemmArgs a = {};
+    a.T = c->T; a.d = c->d; a.E = 1; a.ffn = shared_hidden(c); a.k = 1; a.rows = c->T;
+    a.offsets = x.buf<int32_t>(B_STAB);
+    a.tile_prefix = x.buf<int32_t>(B_STAB) + 2;
+    a.Xp = X;
+    a.W1 = w->Ws1; a.W3 = w->Ws3; a.W2 = w->Ws2;
+    a.H = x.buf<void>(B_HS); a.A = x.buf<void>(B_AS); a.EO = x.buf<void>(B_YS);
+    a.dH = x.buf<void>(B_DHS); a.dXp = x.buf<void>(B_DXS);
+    a.expert = MOE_EXPERT_SWIGLU;
+    return a;
+}
+
 int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_routing* r,
                 const void* Yt, float aux_coef, float* loss_out) {
     const moe_config* c = x.c;
@@ -240,8 +282,17 @@ int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_
     TRY(f32 ? simple_up_fwd(ea, x.s) : mfma_up_fwd(ea, x.s));
     TRY(x.mark(MOE_STAGE_DOWN_FWD));
     TRY(f32 ? simple_down_fwd(ea, x.s) : mfma_down_fwd(ea, x.s));
+    TRY(x.mark(MOE_STAGE_SHARED_FWD));
+    const bool shared = c->n_shared > 0;
+    if (shared) {
+        TRY(launch_shared_table(x.buf<int32_t>(B_STAB), c->T, x.s));
+        ExpertGemmArgs sa = shared_args(x, X, w);
+        TRY(f32 ? simple_up_fwd(sa, x.s) : mfma_up_fwd(sa, x.s));
+        TRY(f32 ? simple_down_fwd(sa, x.s) : mfma_down_fwd(sa, x.s));
+    }
     TRY(x.mark(MOE_STAGE_COMBINE_LOSS));
-    CombineArgs ca = {x.buf<void>(B_EO), r->slot_of, r->gates, Y, Yt, x.buf<void>(B_DY),
+    CombineArgs ca = {x.buf<void>(B_EO), r->slot_of, r->gates, Y,
+                      shared ? x.buf<void>(B_YS) : nullptr, Yt, x.buf<void>(B_DY),
                       x.buf<float>(B_LPART), c->T > 0 ? 2.0f / ((float)c->T * (float)c->d) : 0.f,
                       c->T, c->k, vec};
     TRY(launch_combine(ca, c->dtype, x.s));
@@ -284,6 +335,26 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
     TRY(f32 ? simple_up_dgrad(ea, x.s) : mfma_up_dgrad(ea, x.s));
     TRY(x.mark(MOE_STAGE_UP_WGRAD));
     TRY(f32 ? simple_up_wgrad(ea, x.s) : mfma_up_wgrad(ea, x.s));
+    TRY(x.mark(MOE_STAGE_SHARED_BWD));
+    const bool shared = c->n_shared > 0;
+    if (shared) {
+        // its output enters Y with no gate: the upstream gradient is dY itself; each
+        // dgrad reads a working copy before the wgrad that may update it
+        ExpertGemmArgs sa = shared_args(x, X, w);
+        sa.dEO = dY;
+        sa.dW1 = g->dWs1; sa.dW3 = g->dWs3; sa.dW2 = g->dWs2;
+        if (sgd) {
+            sa.dW1 = sa.dW3 = sa.dW2 = nullptr;
+            sa.W1m = sgd->Ws1; sa.W1w = sgd->Ws1_w;
+            sa.W3m = sgd->Ws3; sa.W3w = sgd->Ws3_w;
+            sa.W2m = sgd->Ws2; sa.W2w = sgd->Ws2_w;
+            sa.lr = lr;
+        }
+        TRY(f32 ? simple_down_dgrad(sa, x.s) : mfma_down_dgrad(sa, x.s));
+        TRY(f32 ? simple_down_wgrad(sa, x.s) : mfma_down_wgrad(sa, x.s));
+        TRY(f32 ? simple_up_dgrad(sa, x.s) : mfma_up_dgrad(sa, x.s));
+        TRY(f32 ? simple_up_wgrad(sa, x.s) : mfma_up_wgrad(sa, x.s));
+    }
     TRY(x.mark(MOE_STAGE_BIAS_GRADS));
     if (c->expert != MOE_EXPERT_SWIGLU) {
         ColSumArgs b2 = {x.buf<void>(B_DEO), c->d, r->offsets, g->db2, c->d, c->E};
@@ -302,7 +373,8 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
     TRY(f32 ? simple_router_dwg(rg, x.s) : mfma_router_dwg(rg, x.s));
     TRY(x.mark(MOE_STAGE_ROUTER_DX));
     TRY(f32 ? simple_router_dx(rg, x.s) : mfma_router_dx(rg, x.s));
-    ScatterArgs sa = {x.buf<void>(B_DXP), r->slot_of, x.buf<float>(B_DXR), g->dX, c->T, c->k, vec};
+    ScatterArgs sa = {x.buf<void>(B_DXP), r->slot_of, x.buf<float>(B_DXR), g->dX,
+                      shared ? x.buf<void>(B_DXS) : nullptr, c->T, c->k, vec};
     TRY(x.mark(MOE_STAGE_SCATTER));
     TRY(launch_scatter(sa, c->dtype, x.s));
     return MOE_OK;
@@ -312,7 +384,7 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 const char* moe_status_string(int st) {
     switch (st) {
@@ -400,14 +472,19 @@ static int train_step_impl(const moe_config* cfg, const void* X, const void* Y_t
     const bool glu = cfg->expert == MOE_EXPERT_SWIGLU;
     // expert weight gradients: all given (stored, then SGD over every parameter) or all
     // NULL (SGD fused into the weight-gradient contractions, nothing stored)
-    const int n_null = !g->dW1 + !g->dW2 + (glu ? !g->dW3 : 0);
-    const bool fused = n_null == (glu ? 3 : 2);
+    const bool shared = cfg->n_shared > 0;
+    const int n_null = !g->dW1 + !g->dW2 + (glu ? !g->dW3 : 0) +
+                       (shared ? !g->dWs1 + !g->dWs3 + !g->dWs2 : 0);
+    const bool fused = n_null == (glu ? 3 : 2) + (shared ? 3 : 0);
     if (n_null && !fused) return MOE_ERR_NULL_PTR;
     Ptrs P;
     P.add(X, true); P.add(Y_target, true); P.add(Y, true); P.add(loss_out);
     P.add(p->Wg); P.add(p->W1); P.add(p->W2); P.add(p->Wg_w); P.add(p->W1_w); P.add(p->W2_w);
     if (glu) { P.add(p->W3); P.add(p->W3_w); }
     else { P.add(p->b1); P.add(p->b2); P.add(p->b1_w); P.add(p->b2_w); }
+    if (shared) {
+        P.add(p->Ws1); P.add(p->Ws3); P.add(p->Ws2); P.add(p->Ws1_w); P.add(p->Ws3_w); P.add(p->Ws2_w);
+    }
     add_routing(P, r, true);
     add_grads(P, cfg, g, !fused);
     if ((st = P.check(cfg->T)) != MOE_OK) return st;
@@ -417,20 +494,25 @@ static int train_step_impl(const moe_config* cfg, const void* X, const void* Y_t
     }
     Ctx x{cfg, (char*)workspace, layout(cfg), (hipStream_t)stream, events};
     moe_weights w = {p->Wg_w, p->W1_w, glu ? nullptr : p->b1_w, p->W2_w, glu ? nullptr : p->b2_w,
-                     glu ? p->W3_w : nullptr, p->e_bias};
+                     glu ? p->W3_w : nullptr, p->e_bias,
+                     shared ? p->Ws1_w : nullptr, shared ? p->Ws3_w : nullptr, shared ? p->Ws2_w : nullptr};
     st = run_forward(x, X, &w, Y, r, Y_target, aux_coef, loss_out);
     if (st != MOE_OK) return st;
     st = run_backward(x, X, &w, r, x.buf<void>(B_DY), aux_coef, g, fused ? p : nullptr, lr);
     if (st != MOE_OK) return st;
     const long E = cfg->E, d = cfg->d, ffn = cfg->ffn;
-    // (the expert weights W1, W2, W3 were already updated when the step is fused)
-    struct { float* m; const float* g; void* w; long n; } upd[6] = {
+    const long hs = shared_hidden(cfg);
+    // (the expert and shared weights were already updated when the step is fused)
+    struct { float* m; const float* g; void* w; long n; } upd[MOE_SGD_MAX_SEG] = {
         {p->Wg, g->dWg, p->Wg_w, E * d},
         {fused ? nullptr : p->W1, g->dW1, p->W1_w, E * ffn * d},
         {fused ? nullptr : p->W2, g->dW2, p->W2_w, E * d * ffn},
         {glu && !fused ? p->W3 : nullptr, g->dW3, p->W3_w, E * ffn * d},
         {glu ? nullptr : p->b1, g->db1, p->b1_w, E * ffn},
         {glu ? nullptr : p->b2, g->db2, p->b2_w, E * d},
+        {shared && !fused ? p->Ws1 : nullptr, g->dWs1, p->Ws1_w, hs * d},
+        {shared && !fused ? p->Ws3 : nullptr, g->dWs3, p->Ws3_w, hs * d},
+        {shared && !fused ? p->Ws2 : nullptr, g->dWs2, p->Ws2_w, d * hs},
     };
     TRY(x.mark(MOE_STAGE_SGD));
     SgdArgs sa = {};

@@ -48,7 +48,8 @@ STAGE_SOURCE = {
     "combine_bwd": "dispatch.hip", "down_dgrad": "gemm_mfma.hip", "down_wgrad": "gemm_mfma.hip",
     "up_dgrad": "gemm_mfma.hip", "up_wgrad": "gemm_mfma.hip", "bias_grads": "dispatch.hip",
     "router_bwd": "routing.hip", "router_dwg": "gemm_mfma.hip", "router_dx": "gemm_mfma.hip",
-    "scatter": "dispatch.hip", "sgd": "dispatch.hip",
+    "scatter": "dispatch.hip", "sgd": "dispatch.hip", "shared_fwd": "gemm_mfma.hip",
+    "shared_bwd": "gemm_mfma.hip",
 }
 
 
@@ -75,9 +76,21 @@ def _calibration(rows, mib):
 
 
 def _stage_of(name, state):
-    """Stage of a library kernel, given the kernels of the step seen so far."""
+    """Stage of a library kernel, given the kernels of the step seen so far.  The
+    shared-experts branch reuses the expert GEMM templates: its forward follows its
+    table kernel, its backward runs between the up-projection wgrad and the router."""
     if "gemm_bf16_kernel<2, false, false" in name or "s_router_logits" in name:
         return "router_logits"
+    if "shared_table_kernel" in name:
+        state["shared"] = True
+        return "shared_fwd"
+    if state["stage"] == "shared_fwd" and "gemm_bf16_kernel<0, false, false" in name:
+        return "shared_fwd"
+    if state.get("shared") and state["stage"] in ("up_wgrad", "shared_bwd") and "gemm_bf16_kernel<0" in name:
+        return "shared_bwd"
+    if state.get("shared") and "gemm_bf16_kernel<1, true, true" in name and state["wgrad"] in (2, 3):
+        state["wgrad"] += 1
+        return "shared_bwd"
     if any(k in name for k in ("route_topk", "expert_scan", "slot_assign")):
         return "route"
     if "finalize_kernel" in name:
@@ -99,6 +112,8 @@ def _stage_of(name, state):
     if "gemm_bf16_kernel<1, true, true" in name:
         state["wgrad"] += 1
         return {1: "down_wgrad", 2: "up_wgrad"}.get(state["wgrad"], "router_dwg")
+    if "sum_partials_kernel" in name:
+        return "router_dwg"
     if "colsum_kernel" in name:
         return "bias_grads"
     if "router_bwd_kernel" in name:

@@ -50,6 +50,7 @@ class Workload:
     group_score: str = "max"      # "max" | "top2"
     route_scale: float = 1.0
     e_bias: float = 0.0           # std of the seeded correction bias; 0 = no bias
+    n_shared: int = 0             # shared experts: one SwiGLU of hidden n_shared * ffn; 0 = none
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -92,7 +93,8 @@ WORKLOADS = [
 
 BY_NAME = {w.name: w for w in WORKLOADS}
 
-_TENSOR_ID = {"X": 1, "Yt": 2, "Wg": 3, "W1": 4, "W2": 5, "W3": 6, "dY": 7, "logits": 8, "e_bias": 9}
+_TENSOR_ID = {"X": 1, "Yt": 2, "Wg": 3, "W1": 4, "W2": 5, "W3": 6, "dY": 7, "logits": 8, "e_bias": 9,
+              "Ws1": 10, "Ws2": 11, "Ws3": 12}
 
 
 def tensor_seed(base: int, tensor: str, expert: int = 0) -> int:
@@ -130,6 +132,15 @@ def make_gate(w: Workload, seed: int = 0, device="cpu") -> torch.Tensor:
     raise ValueError(w.gate)
 
 
+def make_shared(w: Workload, which: str, seed: int = 0, device="cpu") -> torch.Tensor:
+    """A shared-branch master weight, float32: Ws1/Ws3 [Hs, d], Ws2 [d, Hs], Hs = n_shared * ffn;
+    initialised like the routed experts (fan-in of the shared hidden width for Ws2)."""
+    hs = w.n_shared * w.ffn
+    shape = (w.d, hs) if which == "Ws2" else (hs, w.d)
+    std = 0.02 if w.init == "std0.02" else (hs if which == "Ws2" else w.d) ** -0.5
+    return _normal(shape, std, tensor_seed(seed, which), device)
+
+
 def make_expert(w: Workload, which: str, e: int, seed: int = 0, device="cpu") -> torch.Tensor:
     """One expert's master weight, float32: W1/W3 [ffn, d], W2 [d, ffn]."""
     shape = (w.d, w.ffn) if which == "W2" else (w.ffn, w.d)
@@ -140,10 +151,10 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu",
                 masters: bool = True) -> Dict[str, Optional[torch.Tensor]]:
     """All inputs of one layer step: activations, targets, master and working weights.
 
-    Returned keys: X, Yt (working dtype); Wg, W1, b1, W2, b2, W3 (float32
-    masters); and the same names with a ``_w`` suffix for the working copies;
-    e_bias, the float32 correction bias [E] ~ N(0, w.e_bias^2) (None when
-    w.e_bias == 0).
+    Returned keys: X, Yt (working dtype); Wg, W1, b1, W2, b2, W3, Ws1, Ws3, Ws2
+    (float32 masters; the Ws* are the shared branch, None when w.n_shared == 0);
+    the same names with a ``_w`` suffix for the working copies; e_bias, the
+    float32 correction bias [E] ~ N(0, w.e_bias^2) (None when w.e_bias == 0).
     Tensors that the expert kind does not use are None.  With masters=False
     the float32 masters are not kept (their keys hold None) and only the
     working copies are built, one expert at a time.
@@ -175,6 +186,12 @@ def make_inputs(w: Workload, seed: int = 0, device="cpu",
         out["b1"] = out["b2"] = out["b1_w"] = out["b2_w"] = None
     out["e_bias"] = (_normal((w.E,), w.e_bias, tensor_seed(seed, "e_bias"), device)
                      if w.e_bias > 0 else None)
+    for n in ("Ws1", "Ws3", "Ws2"):
+        if w.n_shared > 0:
+            t = make_shared(w, n, seed, device)
+            out[n], out[n + "_w"] = (t if masters else None), t.to(wd)
+        else:
+            out[n] = out[n + "_w"] = None
     return out
 
 

@@ -144,6 +144,10 @@ def resolve_routing(l64, gpu_idx, w, eps, e_bias=None):
     return resolved, n_amb
 
 
+# trained weights: router, routed experts, shared branch
+WEIGHT_NAMES = ("Wg", "W1", "b1", "W2", "b2", "W3", "Ws1", "Ws3", "Ws2")
+
+
 class GpuRun:
     """Buffers and results of one moe_forward (+ moe_backward) on the GPU."""
 
@@ -157,7 +161,7 @@ class GpuRun:
         self.grads = L.alloc_grads(w, device)
         self.X = inp["X"].to(device)
         self.weights = {n: (None if inp.get(n + "_w") is None else inp[n + "_w"].to(device))
-                        for n in ("Wg", "W1", "b1", "W2", "b2", "W3")}
+                        for n in WEIGHT_NAMES}
         self.weights["e_bias"] = None if inp.get("e_bias") is None else inp["e_bias"].to(device)
 
     def forward(self):
@@ -174,7 +178,7 @@ class GpuRun:
 
 
 def oracle_params(inp):
-    P = {n: to64(inp.get(n + "_w")) for n in ("Wg", "W1", "b1", "W2", "b2", "W3")}
+    P = {n: to64(inp.get(n + "_w")) for n in WEIGHT_NAMES}
     P["e_bias"] = None if inp.get("e_bias") is None else inp["e_bias"].cpu().numpy().astype(np.float32)
     return P
 
@@ -231,7 +235,7 @@ def full_parity(w, inp, dY, aux_coef, check_saved=True, label=""):
         assert_close("H", to64(saved["H"]), Hs, rtol, atol)
         assert_close("A", to64(saved["A"]), As, rtol, atol)
         assert_close("EO", to64(saved["EO"]), fw["EO"], rtol, atol)
-    for n in ("dX", "dWg", "dW1", "db1", "dW2", "db2", "dW3"):
+    for n in ("dX", "dWg", "dW1", "db1", "dW2", "db2", "dW3", "dWs1", "dWs2", "dWs3"):
         if n in run.grads:
             assert_close(n, to64(run.grads[n]), gr[n], rtol, atol)
     return run, fw, gr, n_amb

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert L.abi_version() == 2
+    assert L.abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert L.status_string(code) and L.status_string(code) != "unknown status"
     assert L.status_string(12345) == "unknown status"
@@ -116,6 +116,21 @@ def test_router_variant_rules(lib, kw, code):
     else:
         assert L.workspace_bytes(cfg) == 0
         assert _call_forward(cfg) == code
+
+
+def test_shared_branch_rules(lib):
+    w = W.WORKLOADS[0]
+    assert _call_forward(L.config(w.replace(n_shared=-1))) == -1
+    assert L.workspace_bytes(L.config(w.replace(n_shared=-1))) == 0
+    assert L.workspace_bytes(L.config(w.replace(n_shared=1 << 20))) == 0      # Hs > 2^24
+    # the shared weights are required once there is a shared branch (rejected before launch)
+    assert _call_forward(L.config(w.replace(n_shared=2))) == -2
+    # its buffers grow the workspace
+    assert L.workspace_bytes(L.config(w.replace(n_shared=2))) > L.workspace_bytes(L.config(w))
+    # bf16: the shared hidden width counts in the 2 GiB operand-span rule
+    wb = W.BY_NAME["gelu_mlp_t4096_d1024_e8"]
+    n = (1 << 31) // (2 * 2 * wb.ffn * 4) + 1          # T * 2 Hs * 2 >= 2^31 with n_shared = 4
+    assert _call_forward(L.config(wb.replace(n_shared=4, T=n))) == -5
 
 
 def test_top2_group_score_needs_two_members_per_group(lib):

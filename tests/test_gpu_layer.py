@@ -61,11 +61,23 @@ VARIANT_CASES = [
 ]
 
 
+# shared-experts branch (one SwiGLU of hidden n_shared * ffn over every token)
+SHARED_CASES = [
+    wl("f32_swiglu_shared2", expert="swiglu", n_shared=2),
+    wl("f32_relu_shared1", n_shared=1, T=33),
+    wl("bf16_swiglu_shared_ragged", T=1000, d=512, E=8, ffn=640, k=2, dtype="bf16", expert="swiglu",
+       n_shared=1),
+    wl("bf16_gelu_shared2", T=600, d=320, E=8, ffn=576, k=2, dtype="bf16", expert="gelu", n_shared=2),
+    wl("bf16_swiglu_sigmoid_groups_shared", T=700, d=384, E=16, ffn=192, k=3, n_groups=4, topk_groups=2,
+       dtype="bf16", expert="swiglu", score="sigmoid", n_shared=3),
+]
+
+
 def _inputs(w, seed=0):
     return W.make_inputs(w, seed=seed, masters=True)
 
 
-@pytest.mark.parametrize("w", F32_CASES + BF16_CASES + VARIANT_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("w", F32_CASES + BF16_CASES + VARIANT_CASES + SHARED_CASES, ids=lambda w: w.name)
 def test_forward_backward_parity(w):
     say(f"layer parity {w}")
     inp = _inputs(w)
@@ -138,7 +150,8 @@ def test_inputs_unchanged_and_calls_repeatable():
         assert torch.equal(run.grads[n], g1[n]), n
 
 
-EXPERT_GRADS = ("dW1", "dW2", "dW3")
+EXPERT_GRADS = ("dW1", "dW2", "dW3", "dWs1", "dWs2", "dWs3")
+PARAM_NAMES = ("Wg", "W1", "b1", "W2", "b2", "W3", "Ws1", "Ws3", "Ws2")
 
 
 def train_step_parity(w, inp, label, fused=False):
@@ -156,7 +169,7 @@ def train_step_parity(w, inp, label, fused=False):
     Y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
     loss = torch.empty(3, dtype=torch.float32, device=dev)
     params = {}
-    for n in ("Wg", "W1", "b1", "W2", "b2", "W3"):
+    for n in PARAM_NAMES:
         if inp.get(n) is not None:
             params[n] = inp[n].clone().to(dev)
             params[n + "_w"] = inp[n + "_w"].clone().to(dev)
@@ -179,7 +192,7 @@ def train_step_parity(w, inp, label, fused=False):
         assert_close(n, to64(g[n]), st["grads"][n], rtol, atol)
     if "e_bias" in params:
         assert torch.equal(params["e_bias"].cpu(), inp["e_bias"]), "the correction bias was written"
-    for n in ("Wg", "W1", "b1", "W2", "b2", "W3"):
+    for n in PARAM_NAMES:
         if n not in params:
             continue
         new = to64(params[n])
@@ -201,7 +214,12 @@ def test_train_step_parity(w):
 
 
 FUSED_CASES = [F32_CASES[0], F32_CASES[2], BF16_CASES[0], BF16_CASES[1], BF16_CASES[2], BF16_CASES[5],
-               VARIANT_CASES[2]]
+               VARIANT_CASES[2], SHARED_CASES[0], SHARED_CASES[2], SHARED_CASES[3]]
+
+
+@pytest.mark.parametrize("w", [SHARED_CASES[1], SHARED_CASES[4]], ids=lambda w: w.name)
+def test_train_step_parity_shared(w):
+    train_step_parity(w, _inputs(w), w.name)
 
 
 @pytest.mark.parametrize("w", FUSED_CASES, ids=lambda w: w.name)
@@ -221,7 +239,7 @@ def _one_step(w, inp, fused, Wg_override=None):
     Y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
     loss = torch.empty(3, dtype=torch.float32, device=dev)
     params = {}
-    for n in ("Wg", "W1", "b1", "W2", "b2", "W3"):
+    for n in PARAM_NAMES:
         if inp.get(n) is not None:
             params[n] = inp[n].clone().to(dev)
             params[n + "_w"] = inp[n + "_w"].clone().to(dev)
@@ -234,8 +252,8 @@ def _one_step(w, inp, fused, Wg_override=None):
     return out
 
 
-@pytest.mark.parametrize("w", [F32_CASES[2], BF16_CASES[0], BF16_CASES[1], BF16_CASES[5]],
-                         ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [F32_CASES[2], BF16_CASES[0], BF16_CASES[1], BF16_CASES[5], SHARED_CASES[0],
+                               SHARED_CASES[2]], ids=lambda w: w.name)
 def test_fused_sgd_equals_stored_gradient_step(w):
     """The fused step and the step through stored gradients give bitwise the same
     parameters, outputs and remaining gradients: the gradient is the same float32
@@ -283,6 +301,35 @@ def test_train_step_rejects_partial_expert_gradients():
     Y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
     loss = torch.empty(3, dtype=torch.float32, device=dev)
     for drop in (("dW1",), ("dW3",), ("dW1", "dW2")):
+        g = L.alloc_grads(w, dev)
+        for n in drop:
+            g.pop(n)
+        with pytest.raises(L.MoeError) as ei:
+            L.moe_train_step(cfg, inp["X"].to(dev), inp["Yt"].to(dev), params, w.lr, w.aux_coef, Y, r,
+                             g, loss, ws)
+        assert L.STATUS[ei.value.status] == "MOE_ERR_NULL_PTR"
+    torch.cuda.synchronize()
+    for n, v in keep.items():
+        assert torch.equal(params[n], v), n
+
+
+def test_train_step_rejects_partial_shared_gradients():
+    """With a shared branch its gradients join the all-or-none rule."""
+    w = SHARED_CASES[2]
+    dev = "cuda"
+    cfg = L.config(w)
+    ws = L.alloc_workspace(cfg, dev)
+    r = L.alloc_routing(w, dev)
+    inp = _inputs(w)
+    params = {}
+    for n in PARAM_NAMES:
+        if inp.get(n) is not None:
+            params[n] = inp[n].clone().to(dev)
+            params[n + "_w"] = inp[n + "_w"].clone().to(dev)
+    keep = {n: v.clone() for n, v in params.items()}
+    Y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
+    loss = torch.empty(3, dtype=torch.float32, device=dev)
+    for drop in (("dW1", "dW2", "dW3"), ("dWs2",), ("dWs1", "dWs2", "dWs3")):
         g = L.alloc_grads(w, dev)
         for n in drop:
             g.pop(n)
