@@ -184,17 +184,58 @@ __global__ void __launch_bounds__(256) scatter_kernel(ScatterArgs a) {
     }
 }
 
-// Column sums of each expert's row segment (bias gradients), fixed row order.
+// Column sums of each expert's row segment (bias gradients).  A workgroup owns
+// 32 16-byte column vectors of one expert; its 16 row groups of 32 lanes each sum
+// the rows r = lo + g, lo + g + 16, ... (four loads in flight per lane), and the
+// 16 partial sums are then added in row-group order: a fixed order, so the
+// result is deterministic.
+constexpr int COLSUM_RG = 16;
 template <class T>
-__global__ void __launch_bounds__(256) colsum_kernel(ColSumArgs a) {
+__global__ void __launch_bounds__(COLSUM_RG * 32) colsum_kernel(ColSumArgs a) {
+    constexpr int N = Vec16<T>::N;
+    __shared__ float part[COLSUM_RG][32 * N];
     const int e = blockIdx.y;
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= a.ncols) return;
+    const int vl = threadIdx.x & 31, rg = threadIdx.x >> 5;
+    const int c = (blockIdx.x * 32 + vl) * N;              // first column of this lane
+    const bool ok = c < a.ncols;
     const int lo = a.offsets[e], hi = a.offsets[e + 1];
     const T* src = reinterpret_cast<const T*>(a.src);
-    float s = 0.f;
-    for (int r = lo; r < hi; ++r) s += to_f<T>(src[(size_t)r * a.ld + c]);
-    a.dst[(size_t)e * a.ncols + c] = s;
+    float acc[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) acc[j] = 0.f;
+    if (ok) {
+        int r = lo + rg;
+        for (; r + 3 * COLSUM_RG < hi; r += 4 * COLSUM_RG) {
+            float x[4][N];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                Vec16<T>::unpack(*reinterpret_cast<const uint4*>(src + (size_t)(r + u * COLSUM_RG) * a.ld + c), x[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < N; ++j) acc[j] += x[u][j];
+        }
+        for (; r < hi; r += COLSUM_RG) {
+            float x[N];
+            Vec16<T>::unpack(*reinterpret_cast<const uint4*>(src + (size_t)r * a.ld + c), x);
+#pragma unroll
+            for (int j = 0; j < N; ++j) acc[j] += x[j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) part[rg][vl * N + j] = acc[j];
+    __syncthreads();
+    if (rg == 0 && ok) {
+        float out[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            float t = part[0][vl * N + j];
+            for (int g = 1; g < COLSUM_RG; ++g) t += part[g][vl * N + j];
+            out[j] = t;
+        }
+#pragma unroll
+        for (int j = 0; j < N; ++j) a.dst[(size_t)e * a.ncols + c + j] = out[j];
+    }
 }
 
 // theta <- theta - lr * grad on the float32 master; working copy = RNE(master).
@@ -314,9 +355,11 @@ hipError_t launch_scatter(const ScatterArgs& a, int dtype, hipStream_t s) {
     return hipGetLastError();
 }
 hipError_t launch_colsum(const ColSumArgs& a, int dtype, hipStream_t s) {
-    dim3 grid((a.ncols + 255) / 256, a.E);
-    if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(256), 0, s, a);
+    // columns in 16-byte vectors: ncols, ld and the row base are multiples of 16 bytes
+    const int per_wg = 32 * (dtype == MOE_DTYPE_F32 ? 4 : 8);
+    dim3 grid((a.ncols + per_wg - 1) / per_wg, a.E);
+    if (dtype == MOE_DTYPE_F32) hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(COLSUM_RG * 32), 0, s, a);
+    else hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(COLSUM_RG * 32), 0, s, a);
     return hipGetLastError();
 }
 hipError_t launch_sgd(SgdArgs& a, int dtype, hipStream_t s) {
