@@ -699,17 +699,21 @@ gemm_bf16_kernel(GemmParams p) {
             }
             return;
         }
-        if constexpr (EPI == EPI_DN_SWIGLU || EPI == EPI_DN_RELU || EPI == EPI_DN_GELU) {
-            // Activation backward.  dA (the fp32 accumulators) goes out in passes of 32 rows
-            // through LDS (1 KB rows, 16-byte chunk c of row r at c ^ r, two buffers, one
-            // barrier per pass); each thread then takes 8 consecutive columns of a row, reads
-            // H (H1 and H3 for SwiGLU) as 16-byte vectors loaded two passes ahead, and writes
-            // dH.  H and dH go through buffer descriptors bounded to the tile's rows, and every
-            // load and store is issued unconditionally (a lane outside the tile gets an offset
-            // past the bound: its store is dropped, its load reads zeros), so the waits for H
-            // count exactly and never cover the stores of the two passes before.
+        if constexpr (EPI == EPI_DN_SWIGLU || EPI == EPI_DN_RELU || EPI == EPI_DN_GELU ||
+                      EPI == EPI_UP_RELU || EPI == EPI_UP_GELU) {
+            // Row-pass epilogue of the MLP forward (bias + activation: H and A out) and of the
+            // activation backward (H in, dH out).  The fp32 accumulators go out in passes of
+            // 32 rows through LDS (1 KB rows, 16-byte chunk c of row r at c ^ r, two buffers,
+            // one barrier per pass); each thread then takes 8 consecutive columns of a row.
+            // The forward loads its 8 biases once, before the passes; the backward reads H
+            // (H1 and H3 for SwiGLU) as 16-byte vectors loaded two passes ahead.  Every load and
+            // store inside the passes goes through a buffer descriptor bounded to the tile's
+            // rows and is issued unconditionally (a lane outside the tile gets an offset past the
+            // bound: its store is dropped, its load reads zeros), so the waits for H count
+            // exactly and never cover the stores of the two passes before.
+            constexpr bool UP = EPI == EPI_UP_RELU || EPI == EPI_UP_GELU;
             constexpr bool GLU = EPI == EPI_DN_SWIGLU;
-            constexpr int NH = GLU ? 2 : 1;                    // H vectors per 8 columns
+            constexpr int NH = GLU ? 2 : 1;                    // H vectors per 8 columns (backward)
             constexpr uint32_t OUT = 0x80000000u;              // past every bound
             float* stage = reinterpret_cast<float*>(&lds[0][0][0]);   // 2 x 32 rows x 1 KB
             const int c8 = tid & 31, rs = tid >> 5;            // 8-column chunk; row of an 8-row step
@@ -717,19 +721,31 @@ gemm_bf16_kernel(GemmParams p) {
             const bool col_ok = n < p.N;
             const long rowg = row_base + m0;                   // first row of the tile
             const int ldh = (int)p.ldh, ldc = (int)p.ldc, ffn = p.ffn;
-            const rsrc_t rh = make_rsrc(p.H + rowg * ldh, (long)rows_valid * ldh * 2);
-            const rsrc_t rd = make_rsrc(reinterpret_cast<bf16*>(p.C) + rowg * ldc, (long)rows_valid * ldc * 2);
             const int npass = (rows_valid + 31) >> 5;
+            // backward: H in, dH out; forward: A out (C), H out (C2)
+            const rsrc_t rh = make_rsrc(UP ? p.C2 : p.H + rowg * ldh,
+                                        UP ? 0 : (long)rows_valid * ldh * 2);
+            const rsrc_t rd = make_rsrc(reinterpret_cast<bf16*>(p.C) + rowg * ldc, (long)rows_valid * ldc * 2);
+            const rsrc_t rh_out = make_rsrc(UP ? reinterpret_cast<bf16*>(p.C2) + rowg * ldc : p.C2,
+                                            UP ? (long)rows_valid * ldc * 2 : 0);
+            float bias8[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) bias8[k] = 0.f;
+            if constexpr (UP) {
+                if (col_ok) unpack8(*reinterpret_cast<const nu4*>(p.bias + (long)e * p.bias_es + n), bias8);
+            }
             nu4 hb[3][4][NH];
             auto prefetch = [&](int q, nu4 (*dst)[NH]) {
+                if constexpr (!UP) {
 #pragma unroll
-                for (int it = 0; it < 4; ++it) {
-                    const int r = q * 32 + it * 8 + rs;
-                    const bool ok = r < rows_valid && col_ok;
+                    for (int it = 0; it < 4; ++it) {
+                        const int r = q * 32 + it * 8 + rs;
+                        const bool ok = r < rows_valid && col_ok;
 #pragma unroll
-                    for (int h = 0; h < NH; ++h)
-                        dst[it][h] = __builtin_bit_cast(nu4, __builtin_amdgcn_raw_buffer_load_b128(
-                            rh, ok ? (uint32_t)(r * ldh + n + h * ffn) * 2 : OUT, 0, 0));
+                        for (int h = 0; h < NH; ++h)
+                            dst[it][h] = __builtin_bit_cast(nu4, __builtin_amdgcn_raw_buffer_load_b128(
+                                rh, ok ? (uint32_t)(r * ldh + n + h * ffn) * 2 : OUT, 0, 0));
+                    }
                 }
             };
             prefetch(0, hb[0]);
@@ -761,57 +777,40 @@ gemm_bf16_kernel(GemmParams p) {
                     const bool ok = rt < rows_valid && col_ok;
                     const nf4 x0 = *reinterpret_cast<const nf4*>(S + r * 256 + (((2 * c8) ^ r) << 2));
                     const nf4 x1 = *reinterpret_cast<const nf4*>(S + r * 256 + (((2 * c8 + 1) ^ r) << 2));
-                    const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                    float h1[8], o1[8];
-                    unpack8(hb[q % 3][it][0], h1);
-                    if constexpr (GLU) {
-                        float h3[8], o3[8];
-                        unpack8(hb[q % 3][it][NH - 1], h3);
+                    float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    const uint32_t o = ok ? (uint32_t)(rt * ldc + n) * 2 : OUT;
+                    if constexpr (UP) {
+                        float av[8];
 #pragma unroll
                         for (int k = 0; k < 8; ++k) {
-                            o1[k] = v[k] * h3[k] * silu_gradf_(h1[k]);
-                            o3[k] = v[k] * siluf_(h1[k]);
+                            v[k] += bias8[k];
+                            av[k] = (EPI == EPI_UP_RELU) ? fmaxf(v[k], 0.f) : geluf_(v[k]);
                         }
-                        __builtin_amdgcn_raw_buffer_store_b128(pack8(o3), rd,
-                            ok ? (uint32_t)(rt * ldc + n + ffn) * 2 : OUT, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(pack8(v), rh_out, o, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(pack8(av), rd, o, 0, 0);
                     } else {
+                        float h1[8], o1[8];
+                        unpack8(hb[q % 3][it][0], h1);
+                        if constexpr (GLU) {
+                            float h3[8], o3[8];
+                            unpack8(hb[q % 3][it][NH - 1], h3);
 #pragma unroll
-                        for (int k = 0; k < 8; ++k)
-                            o1[k] = v[k] * ((EPI == EPI_DN_RELU) ? (h1[k] > 0.f ? 1.f : 0.f) : gelu_gradf_(h1[k]));
+                            for (int k = 0; k < 8; ++k) {
+                                o1[k] = v[k] * h3[k] * silu_gradf_(h1[k]);
+                                o3[k] = v[k] * siluf_(h1[k]);
+                            }
+                            __builtin_amdgcn_raw_buffer_store_b128(pack8(o3), rd,
+                                ok ? (uint32_t)(rt * ldc + n + ffn) * 2 : OUT, 0, 0);
+                        } else {
+#pragma unroll
+                            for (int k = 0; k < 8; ++k)
+                                o1[k] = v[k] * ((EPI == EPI_DN_RELU) ? (h1[k] > 0.f ? 1.f : 0.f) : gelu_gradf_(h1[k]));
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b128(pack8(o1), rd, o, 0, 0);
                     }
-                    __builtin_amdgcn_raw_buffer_store_b128(pack8(o1), rd, ok ? (uint32_t)(rt * ldc + n) * 2 : OUT, 0, 0);
                 }
             }
             return;
-        }
-        // MLP forward: straight from the accumulator layout
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int ml = rb + i * 32 + rr;               // local row
-            if (ml >= rows_valid) continue;
-            const long row = (MODE == MODE_ROWS) ? row_base + m0 + ml : (long)(m0 + ml);
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    float v[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = acc[i][j][g * 4 + q];
-                    const int n = n0 + cb + j * 32 + g * 8 + hk * 4;    // first of 4 columns
-                    if (n >= p.N) continue;
-                    if (EPI == EPI_UP_RELU || EPI == EPI_UP_GELU) {
-                        float b[4], a[4];
-                        load4(p.bias + (long)e * p.bias_es + n, b);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            v[q] += b[q];
-                            a[q] = (EPI == EPI_UP_RELU) ? fmaxf(v[q], 0.f) : geluf_(v[q]);
-                        }
-                        store4(reinterpret_cast<bf16*>(p.C2) + row * p.ldc + n, v);
-                        store4(reinterpret_cast<bf16*>(p.C) + row * p.ldc + n, a);
-                    }
-                }
-            }
         }
     };
 
