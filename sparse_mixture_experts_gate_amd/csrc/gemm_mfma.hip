@@ -574,8 +574,6 @@ gemm_bf16_kernel(GemmParams p) {
                 }
                 __syncthreads();
                 const int n = n0 + qt * 4;
-                float b[4] = {0.f, 0.f, 0.f, 0.f};
-                if (p.bias && n < p.N) load4(p.bias + (long)e * p.bias_es + n, b);
                 // the output halves as locals: a per-lane choice between two kernel-argument
                 // fields compiles to a load of the chosen field and a full wait before the store
                 float* const C1 = reinterpret_cast<float*>(p.C);
@@ -587,7 +585,7 @@ gemm_bf16_kernel(GemmParams p) {
                     const int ml = pass * 128 + r;
                     const float4 x = *reinterpret_cast<const float4*>(stage + r * 256 + ((qt ^ (r & 63)) << 2));
                     if (ml < rows_valid && n < p.N) {
-                        const float v[4] = {x.x + b[0], x.y + b[1], x.z + b[2], x.w + b[3]};
+                        const float v[4] = {x.x, x.y, x.z, x.w};
                         const long row = (MODE == MODE_ROWS) ? row_base + m0 + ml : (long)(m0 + ml);
                         if (MODE == MODE_KSEG) {
                             const bool sec = row >= c2;
@@ -601,7 +599,7 @@ gemm_bf16_kernel(GemmParams p) {
             }
             return;
         }
-        if constexpr ((EPI == EPI_STORE || EPI == EPI_UP_SWIGLU) && !OUT_F32) {
+        if constexpr ((EPI == EPI_STORE || EPI == EPI_STORE_BIAS || EPI == EPI_UP_SWIGLU) && !OUT_F32) {
             // bf16 tile written out through LDS: 512-byte rows of 32 chunks, chunk q of row r
             // at q ^ (r & 31); each lane puts its 4 consecutive columns (8 bytes) in place,
             // then the 256 threads store whole rows with 16-byte vectors
@@ -621,14 +619,16 @@ gemm_bf16_kernel(GemmParams p) {
                     dst(r, q * 8, x);
                 }
             };
-            if constexpr (EPI == EPI_STORE) {
-                float bias[NJ][4][4];
+            if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_BIAS) {
+                // the bias (MLP down projection only) is added before the rounding to bf16
+                constexpr int NB = EPI == EPI_STORE_BIAS ? NJ : 1;
+                float bias[NB][4][4];
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
+                for (int j = 0; j < NB; ++j)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int n = n0 + cb + j * 32 + g * 8 + hk * 4;
-                        if (p.bias && n < p.N) load4(p.bias + (long)e * p.bias_es + n, bias[j][g]);
+                        if (EPI == EPI_STORE_BIAS && n < p.N) load4(p.bias + (long)e * p.bias_es + n, bias[j][g]);
                         else bias[j][g][0] = bias[j][g][1] = bias[j][g][2] = bias[j][g][3] = 0.f;
                     }
 #pragma unroll
@@ -639,7 +639,8 @@ gemm_bf16_kernel(GemmParams p) {
                         for (int g = 0; g < 4; ++g) {
                             float v[4];
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) v[q] = acc[i][j][g * 4 + q] + bias[j][g][q];
+                            for (int q = 0; q < 4; ++q)
+                                v[q] = acc[i][j][g * 4 + q] + (EPI == EPI_STORE_BIAS ? bias[j < NB ? j : 0][g][q] : 0.f);
                             put(rb + i * 32 + rr, cb + j * 32 + g * 8 + hk * 4, v);
                         }
                 __syncthreads();
@@ -875,8 +876,11 @@ hipError_t mfma_down_fwd(const ExpertGemmArgs& a, hipStream_t s) {
     p.B = (const bf16*)a.W2; p.ldb = a.ffn; p.bes = (long)a.d * a.ffn;
     p.N = a.d; p.K = a.ffn;
     p.C = a.EO; p.ldc = a.d;
-    p.bias = (const bf16*)a.b2; p.bias_es = a.d;
     const int NT = (a.d + BN - 1) / BN;
+    if (a.b2) {
+        p.bias = (const bf16*)a.b2; p.bias_es = a.d;
+        return run<MODE_ROWS, false, false, EPI_STORE_BIAS, false>(p, p.mtiles_ub * NT, s);
+    }
     return run<MODE_ROWS, false, false, EPI_STORE, false>(p, p.mtiles_ub * NT, s);
 }
 

@@ -121,7 +121,7 @@ hipError_t launch_shared_table(int32_t* tab, int T, hipStream_t s);
 
 // ---- expert / router contractions -------------------------------------------------
 enum GemmEpi {
-    EPI_STORE = 0,         // C = acc (+ bias per column), dtype or fp32
+    EPI_STORE = 0,         // C = acc, dtype or fp32
     EPI_UP_SWIGLU = 1,     // H1|H3 and A = silu(H1) * H3
     EPI_UP_RELU = 2,       // H = acc + b1, A = relu(H)
     EPI_UP_GELU = 3,       // H = acc + b1, A = gelu(H)
@@ -130,6 +130,7 @@ enum GemmEpi {
     EPI_DN_GELU = 6,       // dH = dA * gelu'(H)
     EPI_SGD = 7,           // weight gradient applied as an SGD step instead of stored:
                            // master = fma(-lr, acc, master), working copy = bf16(master)
+    EPI_STORE_BIAS = 8,    // bf16 C = acc + bias per column (MLP down projection)
 };
 
 // Expert contractions of the layer.  All row-major; see each field.
