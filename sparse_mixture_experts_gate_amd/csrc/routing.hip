@@ -320,40 +320,58 @@ slot_assign_kernel(SlotArgs a) {
     }
 }
 
-// Single workgroup: P_e, f_e, aux and (optionally) the MSE from partial sums.
-__global__ void __launch_bounds__(256)
+// Single workgroup: P_e, f_e, aux and (optionally) the MSE from partial sums.  The
+// 1024 threads split the chunk partials of each expert into nslice = 1024 / E
+// interleaved slices (several loads in flight per thread); slices, then experts,
+// then the MSE partials are added in a fixed order, so the result is deterministic.
+constexpr int FIN_THREADS = 1024;
+__global__ void __launch_bounds__(FIN_THREADS)
 finalize_kernel(FinalizeArgs a) {
-    __shared__ float s_red[256];
+    __shared__ float s_red[FIN_THREADS];
     const int tid = threadIdx.x;
-    float part = 0.f;
-    if (a.T > 0) {
-        for (int e = tid; e < a.E; e += 256) {
-            float P = 0.f;
-            for (int c = 0; c < a.nchunk; ++c) P += a.qpart[(size_t)c * a.E + e];
-            P /= (float)a.T;
-            float f = (float)a.counts[e] / ((float)a.T * (float)a.k);
-            part += f * P;
+    const int E = a.E;
+    const int nslice = FIN_THREADS / E;                // E <= MOE_MAX_EXPERTS <= 1024
+    float q = 0.f;
+    if (a.T > 0 && tid < E * nslice) {
+        const int e = tid % E, sl = tid / E;
+        int c = sl;
+        for (; c + 3 * nslice < a.nchunk; c += 4 * nslice) {
+            const float v0 = a.qpart[(size_t)c * E + e], v1 = a.qpart[(size_t)(c + nslice) * E + e];
+            const float v2 = a.qpart[(size_t)(c + 2 * nslice) * E + e], v3 = a.qpart[(size_t)(c + 3 * nslice) * E + e];
+            q += v0; q += v1; q += v2; q += v3;
         }
+        for (; c < a.nchunk; c += nslice) q += a.qpart[(size_t)c * E + e];
     }
+    s_red[tid] = q;
+    __syncthreads();
+    float part = 0.f;                                  // f_e P_e of expert tid
+    if (a.T > 0 && tid < E) {
+        float P = 0.f;
+        for (int sl = 0; sl < nslice; ++sl) P += s_red[sl * E + tid];
+        P /= (float)a.T;
+        const float f = (float)a.counts[tid] / ((float)a.T * (float)a.k);
+        part = f * P;
+    }
+    __syncthreads();
     s_red[tid] = part;
     __syncthreads();
-    for (int s = 128; s >= 1; s >>= 1) {
-        if (tid < s) s_red[tid] += s_red[tid + s];
+    for (int st = FIN_THREADS / 2; st >= 1; st >>= 1) {
+        if (tid < st) s_red[tid] += s_red[tid + st];
         __syncthreads();
     }
-    float aux = (float)a.E * s_red[0];
+    const float aux = (float)E * s_red[0];
     __syncthreads();
     float mse = 0.f;
     if (a.lpart != nullptr) {
         float v = 0.f;
-        for (int b = tid; b < a.nlpart; b += 256) v += a.lpart[b];
+        for (int b = tid; b < a.nlpart; b += FIN_THREADS) v += a.lpart[b];
         s_red[tid] = v;
         __syncthreads();
-        for (int s = 128; s >= 1; s >>= 1) {
-            if (tid < s) s_red[tid] += s_red[tid + s];
+        for (int st = FIN_THREADS / 2; st >= 1; st >>= 1) {
+            if (tid < st) s_red[tid] += s_red[tid + st];
             __syncthreads();
         }
-        double n = (double)a.T * (double)a.d;
+        const double n = (double)a.T * (double)a.d;
         mse = (n > 0) ? (float)((double)s_red[0] / n) : 0.f;
     }
     if (tid == 0) {
@@ -448,7 +466,7 @@ hipError_t launch_slot_assign(const SlotArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(FIN_THREADS), 0, s, a);
     return hipGetLastError();
 }
 hipError_t launch_router_bwd(const RouterBwdArgs& a, int dtype, hipStream_t s) {
