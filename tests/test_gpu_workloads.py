@@ -211,3 +211,63 @@ def test_grouped_sigmoid_e64_sampled():
 
 def test_grouped_sigmoid_e256_d7168_sampled():
     _sampled_parity(W.BY_NAME["grouped_sigmoid_t32768_d7168_e256"], n_tokens=16, n_experts_checked=4)
+
+
+def _expert_checksums(t):
+    """Per-expert integer checksum of a [E, ...] tensor: the sum of its elements'
+    bit patterns as int64, one expert at a time (no large temporaries)."""
+    iv = t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+    return torch.stack([iv[e].to(torch.int64).sum() for e in range(t.shape[0])]).cpu()
+
+
+def _train_once(w, lr, fused):
+    dev = "cuda"
+    inp = W.make_inputs(w, device=dev, masters=True)
+    cfg = L.config(w)
+    ws = L.alloc_workspace(cfg, dev)
+    r = L.alloc_routing(w, dev)
+    g = L.alloc_grads(w, dev)
+    if fused:
+        for n in ("dW1", "dW2", "dW3"):
+            g.pop(n)
+    Y = torch.empty(w.T, w.d, dtype=w.torch_dtype, device=dev)
+    loss = torch.empty(3, dtype=torch.float32, device=dev)
+    params = {n: inp[n] for n in ("Wg", "W1", "W2", "W3")}
+    params.update({n + "_w": inp[n + "_w"] for n in ("Wg", "W1", "W2", "W3")})
+    sample = [0, 77, 200, 255]
+    before = {n: params[n][sample].cpu() for n in ("W1", "W2", "W3")}
+    L.moe_train_step(cfg, inp["X"], inp["Yt"], params, lr, w.aux_coef, Y, r, g, loss, ws)
+    torch.cuda.synchronize()
+    out = {"Y": Y.cpu(), "loss": loss.cpu(), "dX": g["dX"].cpu(), "dWg": g["dWg"].cpu(),
+           "Wg": params["Wg"].cpu(), "Wg_w": params["Wg_w"].cpu(), "counts": r["counts"].cpu()}
+    for n in ("W1", "W2", "W3"):
+        for suffix in ("", "_w"):
+            out["sum " + n + suffix] = _expert_checksums(params[n + suffix])
+            out["sample " + n + suffix] = params[n + suffix][sample].cpu()
+    for n in ("W1", "W2", "W3"):
+        out["moved " + n] = (out["sample " + n] != before[n]).flatten(1).any(dim=1)
+    del inp, params, g, ws, Y
+    torch.cuda.empty_cache()
+    return out
+
+
+def test_fused_sgd_step_full_size_equals_stored():
+    """The launch configuration the benchmark times: the T=32768, d=7168, E=256
+    training step with the SGD step fused into the weight-gradient GEMMs gives
+    bitwise the outputs and parameters of the step that stores the gradients
+    (sampled experts compared element by element, every expert by checksum);
+    the stored gradients are the ones test_grouped_sigmoid_e256_d7168_sampled
+    checks against the oracle.  lr is raised from 1e-3 to 100 so that the step
+    moves the float32 masters (at 1e-3 the update is below their resolution)."""
+    w = W.BY_NAME["grouped_sigmoid_t32768_d7168_e256"]
+    say(f"[{w.name}] stored-gradient step")
+    a = _train_once(w, 100.0, fused=False)
+    say(f"[{w.name}] fused step")
+    b = _train_once(w, 100.0, fused=True)
+    assert a.keys() == b.keys()
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+    # the step moved the masters of the sampled experts (all of which received rows)
+    assert int(a["counts"][[0, 77, 200, 255]].min()) > 0
+    for n in ("W1", "W2", "W3"):
+        assert bool(a["moved " + n].all()), f"the step left a sampled {n} master unchanged"
