@@ -210,8 +210,12 @@ def cpu_baseline(w, inp, budget_s: float):
         if t_route + t_exp >= budget_s:
             break
     full = t_route + t_exp * (w.T * w.k / max(rows, 1))
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    pools = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in pools] or [1])
+    blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+            for i in pools if i.get("user_api") == "blas"]
     return {"value": w.T / full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "blas": ", ".join(blas) or None, "host_cpus": os.cpu_count(),
             "sample": (f"float64 oracle: routing of all {w.T} tokens ({t_route:.1f} s) + expert "
                        f"forward/backward of {n_exp} whole expert segments ({rows} of {w.T * w.k} "
                        f"rows, {t_exp:.1f} s), expert part extrapolated to all rows by row count: "
@@ -233,6 +237,9 @@ def main(argv=None) -> int:
     ap.add_argument("--shared-experts", type=int, default=0,
                     help="add the shared-experts branch: one SwiGLU of hidden N * ffn over every "
                          "token, timed as its own stages")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one training step in a HIP graph and time --steps replays "
+                         "(reported beside the eager figure)")
     ap.add_argument("--gemm-steps", type=int, default=3,
                     help="with --sgd fused: profiled steps that store the expert gradients, run "
                          "after the timed region, for the GEMM-only stage times")
@@ -335,6 +342,25 @@ def main(argv=None) -> int:
     roof["traffic"] = measured_traffic(dom, w.name, a.sgd)
     roof["kernel"] = dom
 
+    graph = None
+    if a.graph:
+        # the same step captured once and replayed: no per-kernel launch cost on the host
+        g_ = torch.cuda.CUDAGraph()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g_, stream=stream):
+            L.moe_train_step(cfg, X, Yt, params, w.lr, w.aux_coef, Y, r, g, loss, ws, stream=stream)
+        torch.cuda.synchronize()
+        g_.replay()
+        torch.cuda.synchronize()
+        tg0 = time.perf_counter()
+        for _ in range(a.steps):
+            g_.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter() - tg0
+        graph = {"value": round(w.T * a.steps / tg, 1), "ms_per_step": round(tg / a.steps * 1e3, 3),
+                 "steps": a.steps}
+        del g_
+
     # GEMM-only times: with the fused step, a few more profiled steps (outside the
     # timed region) that store the expert weight gradients
     gemm_avg, gemm_mode, gemm_ms_steps = avg, a.sgd, stage_ms
@@ -397,6 +423,7 @@ def main(argv=None) -> int:
         "combine_gbps": stages["combine_loss"].get("gbs"),
         "stages": stages,
         "stages_stored_gradients": stages_stored,
+        "graph": graph,
         "loss": [round(x, 6) for x in loss.tolist()],
         "counts_min_max": [int(r["counts"].min()), int(r["counts"].max())],
         "empty_experts": int((r["counts"] == 0).sum()),
