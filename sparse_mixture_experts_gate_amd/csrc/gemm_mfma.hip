@@ -14,7 +14,10 @@
 //     with fp32 accumulators; the last m-tile of an expert with at most 128
 //     (64) valid rows puts the 4 wavefronts side by side on 64 columns each,
 //     4 x 2 (2 x 2) MFMA tiles, so that it costs a fraction of a full tile's
-//     MFMA work;
+//     MFMA work; the up-projection weight gradient with the SGD step runs
+//     128 x 256 tiles (2 x 4 MFMA tiles a wavefront, a 3-stage ring) with two
+//     workgroups per CU, so that one's SGD epilogue runs under the other's
+//     main loop;
 //   * every operand goes straight from global memory into LDS (buffer loads
 //     with an LDS destination, bounds checked by the buffer descriptor so
 //     ragged rows and k tails read as zero) through a ring of 4 LDS stages,
@@ -139,24 +142,34 @@ __device__ __forceinline__ OpPlan plan_direct(rsrc_t r0, rsrc_t r1, uint32_t ld,
     }
     return o;
 }
+// K-strided operand [k][W columns], W = 256 (two k-rows per wave load) or 128 (four):
+// 16-byte chunk c of k-row r sits at chunk c ^ 2 (r & 3) of its LDS row
+template <int W = 256>
 __device__ __forceinline__ OpPlan plan_strided(rsrc_t r0, rsrc_t r1, uint32_t ld, int kswitch) {
     OpPlan o;
     o.r0 = r0; o.r1 = r1; o.ld_bytes = ld; o.paired = 0; o.kswitch = kswitch; o.strided = 1;
     const int lane = threadIdx.x & 63;
-    const uint32_t row_off = (uint32_t)(lane >> 5) * ld;
-    o.vo[0] = row_off + ((uint32_t)((lane & 31) ^ (2 * (lane >> 5))) << 4);
-    o.vo[1] = row_off + ((uint32_t)((lane & 31) ^ (4 + 2 * (lane >> 5))) << 4);
+    if (W == 256) {
+        const uint32_t row_off = (uint32_t)(lane >> 5) * ld;
+        o.vo[0] = row_off + ((uint32_t)((lane & 31) ^ (2 * (lane >> 5))) << 4);
+        o.vo[1] = row_off + ((uint32_t)((lane & 31) ^ (4 + 2 * (lane >> 5))) << 4);
+    } else {
+        const uint32_t r = (uint32_t)(lane >> 4);
+        o.vo[0] = o.vo[1] = r * ld + ((uint32_t)((lane & 15) ^ (2 * r)) << 4);
+    }
     return o;
 }
 // load i (0 .. IPW-1) of this wave for k-tile starting at k0, into the tile at lds byte address t
-template <bool STRIDED>
+template <bool STRIDED, int W = 256>
 __device__ __forceinline__ void dma_one(const OpPlan& o, int i, uint32_t t, int k0, int wave) {
     if (STRIDED) {
-        const int j = wave * STRIDED_IPW + i;
+        constexpr int RPL = 512 / W;                  // k-rows per wave load
+        constexpr int IPW = BK / RPL / 4;              // loads per wave per k-tile
+        const int j = wave * IPW + i;
         rsrc_t r = o.r0;
         int kk = k0;
         if (k0 >= o.kswitch) { r = o.r1; kk = k0 - o.kswitch; }
-        dma16(r, t + j * 1024, o.vo[i & 1], (uint32_t)(kk + 2 * j) * o.ld_bytes);
+        dma16(r, t + j * 1024, o.vo[i & 1], (uint32_t)(kk + RPL * j) * o.ld_bytes);
     } else {
         const int j = wave * DIRECT_IPW + i;
         const int row0 = DIRECT_ROWS * j;
@@ -172,14 +185,15 @@ __device__ __forceinline__ void dma_one(const OpPlan& o, int i, uint32_t t, int 
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+template <int W = 256>
 __device__ __forceinline__ bf16x8 read_strided(const bf16* T, int colbase, int ks) {
     const int lane = threadIdx.x & 63;
     const int L = lane & 15;
     const int col = colbase + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
     const int pc = (col >> 3) ^ (2 * (L >> 2));
     const int k = 16 * ks + 8 * (lane >> 5) + (L >> 2);
-    const bf16* p0 = T + k * 256 + pc * 8 + (col & 7);
-    const bf16* p1 = p0 + 4 * 256;
+    const bf16* p0 = T + k * W + pc * 8 + (col & 7);
+    const bf16* p1 = p0 + 4 * W;
     v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(p0));
     v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(p1));
     typedef short v8s __attribute__((ext_vector_type(8)));
@@ -236,17 +250,25 @@ __device__ __forceinline__ void grouped(int q, int mt, int nt, int& tm, int& tn)
     tn = ng * gn + (rem - tm * gsz);
 }
 
-template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32>
-__global__ void __launch_bounds__(NTHR, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// TM: tile rows.  256: one workgroup per CU, a 4-stage ring; 128 (the SGD epilogue of the
+// weight gradients): two workgroups per CU, 128 accumulators a lane and a 3-stage ring,
+// so that one workgroup's epilogue runs under the other's main loop.
+template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256>
+__global__ void __launch_bounds__(NTHR, TM == 128 ? 2 : 1)
+__attribute__((amdgpu_waves_per_eu(TM == 128 ? 2 : 1, TM == 128 ? 2 : 1)))
 gemm_bf16_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) bf16 lds[NS][2][TILE_ELEMS];
+    static_assert(TM == 256 || (TM == 128 && MODE == MODE_KSEG && EPI == EPI_SGD), "128-row tiles: SGD epilogue");
+    constexpr int NSt = TM == 128 ? 3 : NS;
+    constexpr int TILE_A = TM * BK, STAGE = TILE_A + TILE_ELEMS;
+    static_assert(DIST <= NSt - 1, "prefetch distance");
+    __shared__ __attribute__((aligned(1024))) bf16 lds[NSt * STAGE];
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
     const int NT = p.paired ? (p.ffn + 127) / 128 : (p.N + BN - 1) / BN;
     int nreal;
     if (MODE == MODE_ROWS) nreal = p.tile_prefix[p.E] * NT;
-    else if (MODE == MODE_KSEG) nreal = p.E * ((p.M + BM - 1) / BM) * NT;
+    else if (MODE == MODE_KSEG) nreal = p.E * ((p.M + TM - 1) / TM) * NT;
     else nreal = ((p.M + BM - 1) / BM) * NT;
     nreal = uni(nreal);
     int L = blockIdx.x;
@@ -284,12 +306,12 @@ gemm_bf16_kernel(GemmParams p) {
         const int seg = p.offsets[e + 1] - p.offsets[e];
         rows_valid = min(BM, seg - m0);
     } else if (MODE == MODE_KSEG) {
-        const int MT = (p.M + BM - 1) / BM;
+        const int MT = (p.M + TM - 1) / TM;
         e = L / (MT * NT);
         int tm;
         grouped(L - e * MT * NT, MT, NT, tm, n_t);
-        m0 = tm * BM;
-        rows_valid = min(BM, p.M - m0);
+        m0 = tm * TM;
+        rows_valid = min(TM, p.M - m0);
         if (p.offsets) {
             row_base = p.offsets[e];
             K = p.offsets[e + 1] - p.offsets[e];
@@ -315,7 +337,7 @@ gemm_bf16_kernel(GemmParams p) {
     if (AT) {   // A[k][m]
         const bf16* base = p.A + row_base * p.lda + m0;
         rsrc_t r = make_rsrc(base, ((long)K * p.lda - m0) * 2);
-        pa = plan_strided(r, r, (uint32_t)(p.lda * 2), 0x7fffffff);
+        pa = plan_strided<TM>(r, r, (uint32_t)(p.lda * 2), 0x7fffffff);
     } else {    // A[m][k]
         const bf16* base = p.A + (row_base + m0) * p.lda;
         rsrc_t r = make_rsrc(base, (long)rows_valid * p.lda * 2);
@@ -345,27 +367,28 @@ gemm_bf16_kernel(GemmParams p) {
         }
     }
 
-    f32x16 acc[4][4];
+    constexpr int NIMAX = TM / 64;                    // MFMA row blocks per wave
+    f32x16 acc[NIMAX][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NIMAX; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    constexpr int IPW_A = AT ? STRIDED_IPW : DIRECT_IPW;
+    constexpr int IPW_A = AT ? BK / (512 / TM) / 4 : DIRECT_IPW;
     constexpr int IPW_B = BT ? STRIDED_IPW : DIRECT_IPW;
     constexpr int LPW = IPW_A + IPW_B;                 // loads per wave per k-tile
     static_assert(LPW % KSTEPS == 0 && LPW / KSTEPS <= 8, "load parts");
     constexpr int PART = LPW / KSTEPS;
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&lds[0][0][0];
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
     const int nk = (K + BK - 1) / BK;
     // load q (0 .. LPW-1) of k-tile kt; tiles past the end load harmless data (the buffer
     // bounds make them zeros or rows of this operand) into a stage nobody reads again
     auto dma = [&](int q, int kt) {
-        const uint32_t st = (uint32_t)(kt % NS) * (2 * TILE_ELEMS * 2);
-        if (q < IPW_A) dma_one<AT>(pa, q, lds_base + st, kt * BK, wave);
-        else dma_one<BT>(pb, q - IPW_A, lds_base + st + TILE_ELEMS * 2, kt * BK, wave);
+        const uint32_t st = (uint32_t)(kt % NSt) * (STAGE * 2);
+        if (q < IPW_A) dma_one<AT, TM>(pa, q, lds_base + st, kt * BK, wave);
+        else dma_one<BT>(pb, q - IPW_A, lds_base + st + TILE_A * 2, kt * BK, wave);
     };
     const int rr = lane & 31, hk = lane >> 5;
 
@@ -377,10 +400,10 @@ gemm_bf16_kernel(GemmParams p) {
         constexpr int NI = decltype(lay)::NI, NJ = decltype(lay)::NJ;
         constexpr int NMF = NI * NJ;                   // MFMA slots per k-step
         constexpr int NR = NI + NJ;                    // fragment reads per k-step
-        const int rb = (NJ == 4) ? wm * 128 : 0;       // first row / column of the wave
+        const int rb = (NJ == 4) ? wm * (NI * 32) : 0;  // first row / column of the wave
         const int cb = (NJ == 4) ? wn * 128 : wave * 64;
         auto read_one = [&](const bf16* As, const bf16* Bs, int ks, Frags& f, int idx) {
-            if (idx < NI) f.a[idx] = AT ? read_strided(As, rb + idx * 32, ks) : read_contig(As, rb + idx * 32, ks);
+            if (idx < NI) f.a[idx] = AT ? read_strided<TM>(As, rb + idx * 32, ks) : read_contig(As, rb + idx * 32, ks);
             else f.b[idx - NI] = BT ? read_strided(Bs, cb + (idx - NI) * 32, ks) : read_contig(Bs, cb + (idx - NI) * 32, ks);
         };
         auto mfma_one = [&](const Frags& f, int i) {
@@ -420,7 +443,8 @@ gemm_bf16_kernel(GemmParams p) {
             const int r = sec ? ml - n1 : ml;
             return (ml < rows_valid && col_ok) ? (uint32_t)((long)r * ldc + n) : OUT;
         };
-        nf4 mb[3][8];
+        constexpr int PD = TM == 128 ? 1 : 2;         // passes of masters loaded ahead
+        nf4 mb[PD + 1][8];
         auto prefetch = [&](int q, nf4* dst) {
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
@@ -430,7 +454,7 @@ gemm_bf16_kernel(GemmParams p) {
                     sec ? rm2 : rm1, o == OUT ? OUT : o * 4, 0, 2));
             }
         };
-        if constexpr (EPI == EPI_SGD) {
+        if constexpr (EPI == EPI_SGD && TM == 256) {
             prefetch(0, mb[0]);
             prefetch(1, mb[1]);
         }
@@ -444,11 +468,11 @@ gemm_bf16_kernel(GemmParams p) {
             __syncthreads();
             Frags fa, fb;
 #pragma unroll
-            for (int idx = 0; idx < NR; ++idx) read_one(lds[0][0], lds[0][1], 0, fa, idx);
+            for (int idx = 0; idx < NR; ++idx) read_one(lds, lds + TILE_A, 0, fa, idx);
             for (int kt = 0; kt < nk; ++kt) {
-                const int st = kt % NS;
-                const bf16* As = lds[st][0];
-                const bf16* Bs = lds[st][1];
+                const int st = kt % NSt;
+                const bf16* As = lds + st * STAGE;
+                const bf16* Bs = lds + st * STAGE + TILE_A;
                 const int pf = kt + DIST;
 #pragma unroll
                 for (int s = 0; s < KSTEPS; ++s) {
@@ -478,13 +502,13 @@ gemm_bf16_kernel(GemmParams p) {
                         wait_vm<LPW * (DIST - 1)>();
                         wait_lgkm0();
                         __syncthreads();
-                        const int sn = (kt + 1) % NS;
+                        const int sn = (kt + 1) % NSt;
 #pragma unroll
                         for (int i = h1; i < NMF; ++i) {
                             mfma_one(cur, i);
 #pragma unroll
                             for (int idx = (i - h1) * NR / (NMF - h1); idx < (i - h1 + 1) * NR / (NMF - h1); ++idx)
-                                read_one(lds[sn][0], lds[sn][1], 0, nxt, idx);
+                                read_one(lds + sn * STAGE, lds + sn * STAGE + TILE_A, 0, nxt, idx);
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
@@ -502,25 +526,29 @@ gemm_bf16_kernel(GemmParams p) {
             // whole rows.  Each thread loads its masters two passes ahead into registers:
             // vector memory operations retire in issue order, so a wait for those loads
             // never covers the stores of the two passes before.
-            static_assert(MODE == MODE_KSEG && OUT_F32 && NI == 4 && NJ == 4,
+            static_assert(MODE == MODE_KSEG && OUT_F32 && NI == TM / 64 && NJ == 4,
                           "SGD epilogue: weight gradients, full wave layout");
             {
-                float* stage = reinterpret_cast<float*>(&lds[0][0][0]);   // 2 x 32 rows x 1 KB
+                float* stage = reinterpret_cast<float*>(lds);   // 2 x 32 rows x 1 KB
+                constexpr int NP = TM / 32;                    // passes
+                if constexpr (TM == 128) prefetch(0, mb[0]);
                 __syncthreads();                               // every wave is past its last LDS read
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
+                for (int q = 0; q < NP; ++q) {
                     if (q * 32 >= rows_valid) break;           // uniform
-                    if (q + 2 < 8) prefetch(q + 2, mb[(q + 2) % 3]);
+                    if (q + PD < NP) prefetch(q + PD, mb[(q + PD) % (PD + 1)]);
                     float* S = stage + (q & 1) * (32 * 256);
-                    if (rb == (q >> 2) * 128) {                // the waves that own rows q*32 ..
+#pragma unroll
+                    for (int i = 0; i < NI; ++i) {
+                        if (rb + i * 32 != q * 32) continue;   // the waves that own rows q*32 ..
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
 #pragma unroll
                             for (int g = 0; g < 4; ++g) {
                                 const int c = (cb + j * 32 + g * 8 + hk * 4) >> 2;
                                 *reinterpret_cast<nf4*>(S + rr * 256 + ((c ^ rr) << 2)) =
-                                    nf4{acc[q & 3][j][g * 4], acc[q & 3][j][g * 4 + 1],
-                                        acc[q & 3][j][g * 4 + 2], acc[q & 3][j][g * 4 + 3]};
+                                    nf4{acc[i][j][g * 4], acc[i][j][g * 4 + 1],
+                                        acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
                             }
                     }
                     __syncthreads();
@@ -530,7 +558,7 @@ gemm_bf16_kernel(GemmParams p) {
                         const nf4 gr = *reinterpret_cast<const nf4*>(S + r * 256 + ((qt ^ r) << 2));
                         bool sec;
                         const uint32_t o = elem(q * 32 + r, sec);
-                        const nf4 mv = mb[q % 3][it];
+                        const nf4 mv = mb[q % (PD + 1)][it];
                         nf4 w;
                         w.x = __builtin_fmaf(nlr, gr.x, mv.x);
                         w.y = __builtin_fmaf(nlr, gr.y, mv.y);
@@ -553,7 +581,7 @@ gemm_bf16_kernel(GemmParams p) {
             // wavefronts that own those rows put their accumulators in LDS as 1 KB rows
             // (16-byte chunk q of row r at chunk q ^ (r & 63)), then all 256 threads store
             // whole rows
-            float* stage = reinterpret_cast<float*>(&lds[0][0][0]);
+            float* stage = reinterpret_cast<float*>(lds);
             __syncthreads();                                   // every wave is past its last LDS read
             const int qt = tid & 63;
             const int npass = rows_valid > 128 ? 2 : 1;
@@ -603,7 +631,7 @@ gemm_bf16_kernel(GemmParams p) {
             // bf16 tile written out through LDS: 512-byte rows of 32 chunks, chunk q of row r
             // at q ^ (r & 31); each lane puts its 4 consecutive columns (8 bytes) in place,
             // then the 256 threads store whole rows with 16-byte vectors
-            bf16* stage = &lds[0][0][0];
+            bf16* stage = lds;
             __syncthreads();
             auto put = [&](int r, int c, const float* v) {      // c: first of 4 columns
                 const int q = c >> 3;
@@ -716,7 +744,7 @@ gemm_bf16_kernel(GemmParams p) {
             constexpr bool GLU = EPI == EPI_DN_SWIGLU;
             constexpr int NH = GLU ? 2 : 1;                    // H vectors per 8 columns (backward)
             constexpr uint32_t OUT = 0x80000000u;              // past every bound
-            float* stage = reinterpret_cast<float*>(&lds[0][0][0]);   // 2 x 32 rows x 1 KB
+            float* stage = reinterpret_cast<float*>(lds);   // 2 x 32 rows x 1 KB
             const int c8 = tid & 31, rs = tid >> 5;            // 8-column chunk; row of an 8-row step
             const int n = n0 + c8 * 8;
             const bool col_ok = n < p.N;
@@ -820,12 +848,12 @@ gemm_bf16_kernel(GemmParams p) {
         else if (rows_valid <= 128) tile(Layout<4, 2>{});
         else tile(Layout<4, 4>{});
     } else {
-        tile(Layout<4, 4>{});
+        tile(Layout<TM / 64, 4>{});
     }
 }
 
 // ---- host side -------------------------------------------------------------------------------
-template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32>
+template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256>
 static hipError_t run(GemmParams p, int grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
     // Whole XCD rounds; surplus workgroups exit at once. A multiple of 8 is a multiple of
@@ -833,7 +861,7 @@ static hipError_t run(GemmParams p, int grid, hipStream_t s) {
     grid = (grid + 7) & ~7;
     if (p.xcd_group == 0) p.xcd_group = 8;
     if (p.xcd_group != 1 && p.xcd_group != 2 && p.xcd_group != 4 && p.xcd_group != 8) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, AT, BT, EPI, OUT_F32>), dim3(grid), dim3(NTHR), 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, AT, BT, EPI, OUT_F32, TM>), dim3(grid), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
 
@@ -946,7 +974,9 @@ hipError_t mfma_up_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     if (a.W1m) {    // SGD step on W1 (and W3) in place of storing dW1 (dW3)
         p.C = a.W1m; p.W = a.W1w; p.lr = a.lr;
         if (glu) { p.C2 = a.W3m; p.W2 = a.W3w; }
-        return run<MODE_KSEG, true, true, EPI_SGD, true>(p, grid, s);
+        // 128-row tiles, two workgroups per CU: one's SGD epilogue runs under the other's
+        // main loop (measured 3-4% faster here; the same for dW2 brought nothing)
+        return run<MODE_KSEG, true, true, EPI_SGD, true, 128>(p, a.E * ((hcols + 127) / 128) * ((a.d + BN - 1) / BN), s);
     }
     return run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
 }
