@@ -35,19 +35,22 @@
 //     barrier per k-tile publishes the next stage, with the first fragments of
 //     that stage read under the last MFMAs of the current one;
 //   * the MFMA is issued with the N operand first, so each lane's
-//     accumulators hold 4 consecutive output columns; plain stores (bf16 or
-//     fp32) and the SwiGLU forward outputs go out through LDS, so that every
-//     store instruction writes whole rows with 16-byte vectors; the
-//     activation-backward epilogues read H and write directly from the
-//     accumulator layout;
+//     accumulators hold 4 consecutive output columns; every epilogue goes
+//     out through LDS, so that each store instruction writes whole rows with
+//     16-byte vectors: plain stores (bf16 or fp32) and the SwiGLU forward in
+//     one or two passes, and the MLP forward (bias + activation), the
+//     activation backward (H in, dH out) and the fused SGD step (masters in
+//     and out, bf16 copies out) in 32-row passes whose global loads and stores
+//     go through buffer descriptors, issued unconditionally so that the wait
+//     counts stay exact;
 //   * tiles are scheduled on the device from the expert offsets: ROWS mode
 //     walks the m-tiles of every expert's row segment (prefix of per-expert
 //     tile counts, binary search per workgroup); KSEG mode gives each expert
 //     its own output and runs K over its row segment (empty segment -> the
-//     output is written as zeros); DENSE is one plain GEMM.  Workgroups are
-//     dealt round-robin to the 8 XCDs; in KSEG mode each XCD is given a
-//     contiguous, equal share of the tiles so that tiles of one expert meet
-//     in its L2.
+//     output is written as zeros); DENSE is one plain GEMM.  The hardware
+//     deals workgroups round-robin to the 8 XCDs; the kernel groups the XCDs
+//     (G per group) and gives each group a contiguous, equal share of the
+//     tiles, dealt round-robin among its members.
 #include "common.hpp"
 #include "kernels.hpp"
 
