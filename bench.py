@@ -146,7 +146,6 @@ def measured_traffic(stage: str, workload: str, sgd: str):
     """HBM bytes per step of a stage from the committed counter summary, or None when
     there is none, it was taken in the other SGD mode, or the kernel source has
     changed since the counters were taken."""
-    import hashlib
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -156,9 +155,10 @@ def measured_traffic(stage: str, workload: str, sgd: str):
     if rec.get("sgd", "stored") != sgd:
         return None
     src = os.path.join(ROOT, "sparse_mixture_experts_gate_amd", "csrc", STAGE_SOURCE[stage])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    from sparse_mixture_experts_gate_amd.profile_summary import code_sha256
+    sha = code_sha256(open(src).read())
     ent = rec["stages"][stage]
-    if ent.get("source_sha256") != sha:
+    if ent.get("source_code_sha256") != sha:
         return None
     return ent["hbm_bytes"]
 

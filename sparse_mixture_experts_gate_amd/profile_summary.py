@@ -53,6 +53,15 @@ STAGE_SOURCE = {
 }
 
 
+def code_sha256(text: str) -> str:
+    """SHA-256 of a C++/HIP source with its comments and blank lines removed, so that a
+    change to comments alone does not count as a change to the kernels."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln.strip()).encode()).hexdigest()
+
+
 def _rows(path, counter):
     out = []
     for r in csv.DictReader(open(path)):
@@ -160,7 +169,7 @@ def summarize(fetch_csv, write_csv, mib):
             "hbm_bytes": round(fs[st]["bytes"] + ws.get(st, {}).get("bytes", 0.0)),
             "launches": fs[st]["launches"], "ms_under_counters": round(fs[st]["ns"] / 1e6, 3),
             "source": STAGE_SOURCE[st],
-            "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+            "source_code_sha256": code_sha256(open(src).read()),
         }
     return {"calibration": {"copy_mib": mib, "fetch_scale": round(f_scale, 4),
                             "write_scale": round(w_scale, 4),
