@@ -97,4 +97,40 @@ __device__ __forceinline__ float gelu_gradf_(float x) {
     return cdf + x * pdf;
 }
 
+// Faster forms for the bfloat16 GEMM epilogues, whose outputs are rounded to bf16
+// (relative step 2^-8) right after:
+//  * the logistic function with the hardware reciprocal (v_rcp_f32, 1 ulp);
+//  * erf by the rational approximation 7.1.26 of Abramowitz and Stegun's Handbook
+//    of Mathematical Functions: for z >= 0, with t = 1 / (1 + p z),
+//    erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2), absolute error
+//    at most 1.5e-7, and erf(-z) = -erf(z).  GELU' shares exp(-x^2 / 2) between the
+//    normal CDF and density.
+// The float32 layer and the routing keep the forms above.
+__device__ __forceinline__ float sigmoid_fast_(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+__device__ __forceinline__ float silu_fast_(float x) { return x * sigmoid_fast_(x); }
+__device__ __forceinline__ float silu_grad_fast_(float x) {
+    const float s = sigmoid_fast_(x);
+    return s * (1.0f + x * (1.0f - s));
+}
+// Phi(x) = (1 + erf(x / sqrt 2)) / 2 with e = exp(-x^2 / 2) given
+__device__ __forceinline__ float normal_cdf_as_(float x, float e) {
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    float poly = fmaf(1.061405429f, t, -1.453152027f);
+    poly = fmaf(poly, t, 1.421413741f);
+    poly = fmaf(poly, t, -0.284496736f);
+    poly = fmaf(poly, t, 0.254829592f);
+    const float erf_z = 1.0f - poly * t * e;          // erf(|x| / sqrt 2)
+    return 0.5f + 0.5f * copysignf(erf_z, x);
+}
+__device__ __forceinline__ float gelu_fast_(float x) {
+    return x * normal_cdf_as_(x, __expf(-0.5f * x * x));
+}
+__device__ __forceinline__ float gelu_grad_fast_(float x) {
+    const float e = __expf(-0.5f * x * x);
+    return normal_cdf_as_(x, e) + x * (0.39894228040143268f * e);
+}
+
 }  // namespace moe

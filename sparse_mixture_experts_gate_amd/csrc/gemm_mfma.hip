@@ -717,7 +717,7 @@ gemm_bf16_kernel(GemmParams p) {
                         for (int g = 0; g < 4; ++g) {
                             float a[4];
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) a[q] = siluf_(acc[i][j][g * 4 + q]) * acc[i][j + 1][g * 4 + q];
+                            for (int q = 0; q < 4; ++q) a[q] = silu_fast_(acc[i][j][g * 4 + q]) * acc[i][j + 1][g * 4 + q];
                             put(rb + i * 32 + rr, ((cb + j * 32) >> 6) * 32 + g * 8 + hk * 4, a);
                         }
                 __syncthreads();
@@ -816,7 +816,7 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
                         for (int k = 0; k < 8; ++k) {
                             v[k] += bias8[k];
-                            av[k] = (EPI == EPI_UP_RELU) ? fmaxf(v[k], 0.f) : geluf_(v[k]);
+                            av[k] = (EPI == EPI_UP_RELU) ? fmaxf(v[k], 0.f) : gelu_fast_(v[k]);
                         }
                         __builtin_amdgcn_raw_buffer_store_b128(pack8(v), rh_out, o, 0, 0);
                         __builtin_amdgcn_raw_buffer_store_b128(pack8(av), rd, o, 0, 0);
@@ -828,15 +828,15 @@ gemm_bf16_kernel(GemmParams p) {
                             unpack8(hb[q % 3][it][NH - 1], h3);
 #pragma unroll
                             for (int k = 0; k < 8; ++k) {
-                                o1[k] = v[k] * h3[k] * silu_gradf_(h1[k]);
-                                o3[k] = v[k] * siluf_(h1[k]);
+                                o1[k] = v[k] * h3[k] * silu_grad_fast_(h1[k]);
+                                o3[k] = v[k] * silu_fast_(h1[k]);
                             }
                             __builtin_amdgcn_raw_buffer_store_b128(pack8(o3), rd,
                                 ok ? (uint32_t)(rt * ldc + n + ffn) * 2 : OUT, 0, 0);
                         } else {
 #pragma unroll
                             for (int k = 0; k < 8; ++k)
-                                o1[k] = v[k] * ((EPI == EPI_DN_RELU) ? (h1[k] > 0.f ? 1.f : 0.f) : gelu_gradf_(h1[k]));
+                                o1[k] = v[k] * ((EPI == EPI_DN_RELU) ? (h1[k] > 0.f ? 1.f : 0.f) : gelu_grad_fast_(h1[k]));
                         }
                         __builtin_amdgcn_raw_buffer_store_b128(pack8(o1), rd, o, 0, 0);
                     }
