@@ -237,6 +237,9 @@ def main(argv=None) -> int:
     ap.add_argument("--shared-experts", type=int, default=0,
                     help="add the shared-experts branch: one SwiGLU of hidden N * ffn over every "
                          "token, timed as its own stages")
+    ap.add_argument("--api-steps", type=int, default=5,
+                    help="after the timed steps: moe_forward + moe_backward call pairs timed with "
+                         "events (median and p90 reported)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one training step in a HIP graph and time --steps replays "
                          "(reported beside the eager figure)")
@@ -361,6 +364,30 @@ def main(argv=None) -> int:
                  "steps": a.steps}
         del g_
 
+    # forward + backward through the two entry points themselves (moe_forward, then
+    # moe_backward from a fixed upstream gradient), each call pair timed with events
+    fb_api = None
+    if a.api_steps > 0:
+        ga = L.alloc_grads(w, dev)
+        dYa = W.make_upstream_grad(w, device=dev)
+        wts = {n: params.get(n + "_w") for n in ("Wg", "W1", "b1", "W2", "b2", "W3", "Ws1", "Ws3", "Ws2")}
+        with torch.cuda.stream(stream):
+            for _ in range(2):                       # warm-up, outside the timing
+                L.moe_forward(cfg, X, wts, Y, r, ws, stream=stream)
+                L.moe_backward(cfg, X, wts, r, dYa, w.aux_coef, ga, ws, stream=stream)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(a.api_steps)]
+            for e0, e1 in evs:
+                e0.record(stream)
+                L.moe_forward(cfg, X, wts, Y, r, ws, stream=stream)
+                L.moe_backward(cfg, X, wts, r, dYa, w.aux_coef, ga, ws, stream=stream)
+                e1.record(stream)
+            stream.synchronize()
+        t_api = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        fb_api = {"median_ms": round(pct(t_api, 0.5), 3), "p90_ms": round(pct(t_api, 0.9), 3),
+                  "tokens_per_s": round(w.T / (pct(t_api, 0.5) * 1e-3), 1), "calls": a.api_steps}
+        del ga, dYa
+
     # GEMM-only times: with the fused step, a few more profiled steps (outside the
     # timed region) that store the expert weight gradients
     gemm_avg, gemm_mode, gemm_ms_steps = avg, a.sgd, stage_ms
@@ -407,6 +434,7 @@ def main(argv=None) -> int:
                    else "one pass over stored gradients"},
         "roofline": roof,
         "fwd_bwd_tokens_per_s": round(w.T / (fwd_bwd_ms * 1e-3), 1),
+        "fwd_bwd_api": fb_api,
         "sgd": a.sgd,
         "expert_gemm_from": f"{gemm_mode} gradients" + (f", {a.gemm_steps} extra profiled steps"
                                                         if gemm_mode != a.sgd else ""),
