@@ -296,7 +296,7 @@ int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_
                       x.buf<float>(B_LPART), c->T > 0 ? 2.0f / ((float)c->T * (float)c->d) : 0.f,
                       c->T, c->k, vec};
     TRY(launch_combine(ca, c->dtype, x.s));
-    if (Yt) {
+    if (loss_out) {                 // the training step; Yt may be NULL only when T = 0
         FinalizeArgs fa = {x.buf<float>(B_QPART), r->counts, x.buf<float>(B_LPART),
                            combine_loss_blocks(c->T), nullptr, loss_out, aux_coef,
                            c->T, c->d, c->E, c->k, nchunk(c)};

@@ -353,3 +353,37 @@ def test_router_path_alone(w):
         if n in run.grads:
             assert torch.count_nonzero(run.grads[n]).item() == 0, n
     assert torch.count_nonzero(run.grads["dX"]).item() > 0
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["stored", "fused"])
+def test_train_step_no_tokens_bf16_shared(fused):
+    """T = 0 through the bf16 path with a shared branch: every kernel runs on empty
+    row segments, the loss is zero, the gradients are exact zeros and the step leaves
+    every master as it was (its bf16 copy is the master rounded)."""
+    w = wl("bf16_no_tokens_shared", T=0, d=128, E=8, ffn=128, k=2, dtype="bf16", expert="swiglu", n_shared=1)
+    dev = "cuda"
+    cfg = L.config(w)
+    ws = L.alloc_workspace(cfg, dev)
+    r = L.alloc_routing(w, dev)
+    g = L.alloc_grads(w, dev)
+    if fused:
+        for n in EXPERT_GRADS:
+            g.pop(n, None)
+    inp = _inputs(w)
+    params = {}
+    for n in PARAM_NAMES:
+        if inp.get(n) is not None:
+            params[n] = inp[n].clone().to(dev)
+            params[n + "_w"] = inp[n + "_w"].clone().to(dev)
+    Y = torch.empty(0, w.d, dtype=w.torch_dtype, device=dev)
+    loss = torch.full((3,), 7.0, dtype=torch.float32, device=dev)
+    L.moe_train_step(cfg, inp["X"].to(dev), inp["Yt"].to(dev), params, w.lr, w.aux_coef, Y, r, g, loss, ws)
+    torch.cuda.synchronize()
+    assert loss.tolist() == [0.0, 0.0, 0.0]
+    assert r["counts"].cpu().tolist() == [0] * w.E
+    for n, v in g.items():
+        assert torch.count_nonzero(v).item() == 0, n
+    for n in PARAM_NAMES:
+        if n in params:
+            assert torch.equal(params[n].cpu(), inp[n]), n
+            assert torch.equal(params[n + "_w"].cpu(), inp[n].to(torch.bfloat16)), n
