@@ -3,16 +3,16 @@
 HBM traffic per stage, from two counter runs:
 
     rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o fetch --output-format csv -- \\
-        python3 bench.py --steps 1 --warmup 0 --gemm-steps 0 --no-cpu-baseline --copy-calibration-mib 1024
+        python3 bench.py --steps 1 --warmup 0 --gemm-steps 0 --api-steps 0 --no-cpu-baseline --copy-calibration-mib 1024
     rocprofv3 --pmc WRITE_SIZE -d OUT/write -o write --output-format csv -- \\
-        python3 bench.py --steps 1 --warmup 0 --gemm-steps 0 --no-cpu-baseline --copy-calibration-mib 1024
+        python3 bench.py --steps 1 --warmup 0 --gemm-steps 0 --api-steps 0 --no-cpu-baseline --copy-calibration-mib 1024
     python -m sparse_mixture_experts_gate_amd.profile_summary OUT/fetch/fetch_counter_collection.csv \\
         OUT/write/write_counter_collection.csv --calibration-mib 1024 --json J --markdown M
 
 Kernel time per kernel, from one kernel-trace run:
 
     rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o kt -- \\
-        python3 bench.py --steps 5 --warmup 2 --gemm-steps 0 --no-cpu-baseline
+        python3 bench.py --steps 5 --warmup 2 --gemm-steps 0 --api-steps 0 --no-cpu-baseline
     python -m sparse_mixture_experts_gate_amd.profile_summary --stats OUT/trace/kt_kernel_stats.csv \\
         --trace OUT/trace/kt_kernel_trace.csv --steps 7 --markdown M --command "..."
 
@@ -20,7 +20,7 @@ MFMA utilisation and clock per GEMM stage, from one counter run:
 
     rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 \\
         SQ_INSTS_MFMA SQ_CYCLES GRBM_GUI_ACTIVE -d OUT/mfma -o mfma --output-format csv -- \\
-        python3 bench.py --steps 1 --warmup 0 --gemm-steps 0 --no-cpu-baseline
+        python3 bench.py --steps 1 --warmup 0 --gemm-steps 0 --api-steps 0 --no-cpu-baseline
     python -m sparse_mixture_experts_gate_amd.profile_summary --mfma OUT/mfma/mfma_counter_collection.csv \\
         --markdown M --command "..."
 
