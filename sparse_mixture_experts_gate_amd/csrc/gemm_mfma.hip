@@ -277,16 +277,27 @@ gemm_bf16_kernel(GemmParams p) {
     int L = blockIdx.x;
     {
         // Workgroups are dealt to the 8 XCDs round-robin by blockIdx. The XCDs form 8/G groups
-        // of G; each group takes a contiguous, equal share of the tiles and deals it round-robin
-        // to its members. G = 8 spreads neighbouring tiles over every L2 (each operand row is
+        // of G; each group takes a contiguous, equal share of the tiles (of each segment's
+        // tiles, for the weight gradients) and deals it round-robin to its members. G = 8 spreads neighbouring tiles over every L2 (each operand row is
         // fetched into all of them); G = 1 keeps them on one XCD (least fabric traffic, but the
         // requests of the co-resident tiles crowd one L2).
         const int G = p.xcd_group;
         const int x = L & 7, i = L >> 3, g = x / G, u = x - g * G, ng = 8 / G;
-        const int q = nreal / ng, r = nreal - q * ng;
         const int li = i * G + u;
-        if (li >= q + (g < r ? 1 : 0)) return;
-        L = g * q + min(g, r) + li;
+        if (MODE == MODE_KSEG) {
+            // A weight-gradient tile costs in proportion to its segment's rows (K), so equal
+            // tile counts per group are not equal work once the routing is skewed: every
+            // group takes the same contiguous share of each segment's tiles instead.
+            const int tps = uni(nreal / p.E);
+            const int s0 = (g * tps) / ng, cg = ((g + 1) * tps) / ng - s0;
+            if (cg == 0 || li >= p.E * cg) return;
+            const int seg = li / cg;
+            L = seg * tps + s0 + (li - seg * cg);
+        } else {
+            const int q = nreal / ng, r = nreal - q * ng;
+            if (li >= q + (g < r ? 1 : 0)) return;
+            L = g * q + min(g, r) + li;
+        }
     }
 
     int e = 0, m0 = 0, n_t = 0;
@@ -861,9 +872,19 @@ static hipError_t run(GemmParams p, int grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
     // Whole XCD rounds; surplus workgroups exit at once. A multiple of 8 is a multiple of
     // every group count, so each group's slots cover its share of the tiles.
-    grid = (grid + 7) & ~7;
     if (p.xcd_group == 0) p.xcd_group = 8;
     if (p.xcd_group != 1 && p.xcd_group != 2 && p.xcd_group != 4 && p.xcd_group != 8) return hipErrorInvalidValue;
+    if (MODE == MODE_KSEG) {
+        // each of the 8/G groups needs slots for its share, ceil(tiles per segment / (8/G)),
+        // of every segment
+        const int ng = 8 / p.xcd_group;
+        const long tps = (long)((p.M + TM - 1) / TM) * ((p.N + BN - 1) / BN);
+        const long need = (long)ng * p.E * ((tps + ng - 1) / ng);
+        if (need > 0x7ffffff0L) return hipErrorInvalidValue;
+        grid = (int)need;
+        if (grid <= 0) return hipSuccess;
+    }
+    grid = (grid + 7) & ~7;
     hipLaunchKernelGGL((gemm_bf16_kernel<MODE, AT, BT, EPI, OUT_F32, TM>), dim3(grid), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
