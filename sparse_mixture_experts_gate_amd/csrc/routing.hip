@@ -18,7 +18,7 @@
 namespace moe {
 
 constexpr int CHUNK = 64;       // tokens per histogram chunk
-constexpr int RT_WAVES = 4;     // wavefronts per routing workgroup
+constexpr int RT_WAVES = 16;    // wavefronts per routing workgroup (4 tokens each)
 constexpr int EPL = MOE_MAX_EXPERTS / 64;  // expert values held per lane
 
 // a beats b in the selection order (-value, id): larger value, then smaller id.
@@ -26,14 +26,57 @@ __device__ __forceinline__ bool beats(float va, int ia, float vb, int ib) {
     return (va > vb) || (va == vb && ia < ib);
 }
 
+// Wave reductions on DPP row moves: the quad swaps (lane ^ 1, lane ^ 2), then the
+// half-row and row mirrors, leave every lane of each 16-lane row holding the row's
+// result (each step combines two disjoint halves, and the two lanes of a pair get
+// the same value since max and + are commutative).  The four row results are then
+// read as scalars and combined in a fixed order, so every lane gets the same,
+// deterministic value.  No LDS round trips, unlike a butterfly of ds_bpermute.
+constexpr int DPP_QXOR1 = 0xB1, DPP_QXOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+template <int C> __device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, C, 0xF, 0xF, false);
+}
+template <int C> __device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(dpp_i<C>(__float_as_int(v)));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+__device__ __forceinline__ float wv_sum(float v) {
+    v += dpp_f<DPP_QXOR1>(v);
+    v += dpp_f<DPP_QXOR2>(v);
+    v += dpp_f<DPP_HALF_MIRROR>(v);
+    v += dpp_f<DPP_MIRROR>(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ float wv_max(float v) {
+    v = fmaxf(v, dpp_f<DPP_QXOR1>(v));
+    v = fmaxf(v, dpp_f<DPP_QXOR2>(v));
+    v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+    v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+template <int C> __device__ __forceinline__ void argmax_step(float& v, int& i) {
+    const float vo = dpp_f<C>(v);
+    const int io = dpp_i<C>(i);
+    if (beats(vo, io, v, i)) { v = vo; i = io; }
+}
 // Wave-wide arg-max under (-value, id); every lane gets the winner.
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
+    argmax_step<DPP_QXOR1>(v, i);
+    argmax_step<DPP_QXOR2>(v, i);
+    argmax_step<DPP_HALF_MIRROR>(v, i);
+    argmax_step<DPP_MIRROR>(v, i);
+    float bv = lane_f(v, 0);
+    int bi = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        float vo = __shfl_xor(v, o, MOE_WAVE);
-        int io = __shfl_xor(i, o, MOE_WAVE);
-        if (beats(vo, io, v, i)) { v = vo; i = io; }
+    for (int r = 1; r < 4; ++r) {
+        const float rv = lane_f(v, 16 * r);
+        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+        if (beats(rv, ri, bv, bi)) { bv = rv; bi = ri; }
     }
+    v = bv; i = bi;
 }
 
 struct TokenScores {
@@ -43,19 +86,24 @@ struct TokenScores {
     float mx, z;      // softmax max and denominator; sigmoid: z = sum of s
 };
 
-__device__ __forceinline__ void score_token(const float* __restrict__ lrow, int E, int score,
-                                            TokenScores& ts) {
+__device__ __forceinline__ void load_logits(const float* __restrict__ lrow, int E, float (&l)[EPL]) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int m = 0; m < EPL; ++m) {
         int e = lane + 64 * m;
-        ts.l[m] = (e < E) ? lrow[e] : -INFINITY;
+        l[m] = (e < E) ? lrow[e] : -INFINITY;
     }
+}
+
+__device__ __forceinline__ void score_token(const float (&l)[EPL], int E, int score, TokenScores& ts) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) ts.l[m] = l[m];
     if (score == MOE_SCORE_SOFTMAX) {
         float mx = -INFINITY;
 #pragma unroll
         for (int m = 0; m < EPL; ++m) mx = fmaxf(mx, ts.l[m]);
-        mx = wave_max(mx);
+        mx = wv_max(mx);
         float z = 0.f;
 #pragma unroll
         for (int m = 0; m < EPL; ++m) {
@@ -63,7 +111,7 @@ __device__ __forceinline__ void score_token(const float* __restrict__ lrow, int 
             ts.s[m] = (e < E) ? expf(ts.l[m] - mx) : 0.f;
             z += ts.s[m];
         }
-        z = wave_sum(z);
+        z = wv_sum(z);
         float inv = 1.0f / z;
 #pragma unroll
         for (int m = 0; m < EPL; ++m) { ts.s[m] *= inv; ts.q[m] = ts.s[m]; }
@@ -76,7 +124,7 @@ __device__ __forceinline__ void score_token(const float* __restrict__ lrow, int 
             ts.s[m] = (e < E) ? 1.0f / (1.0f + expf(-ts.l[m])) : 0.f;
             z += ts.s[m];
         }
-        z = wave_sum(z);
+        z = wv_sum(z);
         float inv = 1.0f / z;
 #pragma unroll
         for (int m = 0; m < EPL; ++m) ts.q[m] = ts.s[m] * inv;
@@ -92,7 +140,7 @@ __device__ __forceinline__ float selected_score(float l, const TokenScores& ts, 
 
 // Selection ranks the logits (exact) for the plain gate, or the fp32 scores plus
 // the correction bias when a bias or the top-2-sum group score is in use.
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * RT_WAVES)
 route_topk_kernel(RouteArgs a) {
     __shared__ int s_hist[MOE_MAX_EXPERTS];
     __shared__ float s_q[RT_WAVES][MOE_MAX_EXPERTS];
@@ -109,11 +157,19 @@ route_topk_kernel(RouteArgs a) {
     for (int m = 0; m < EPL; ++m) qacc[m] = 0.f;
 
     const int gsize = E / G;
-    for (int it = 0; it < CHUNK / RT_WAVES; ++it) {
-        const int t = chunk * CHUNK + wave * (CHUNK / RT_WAVES) + it;
+    constexpr int TPW = CHUNK / RT_WAVES;           // tokens per wavefront
+    const int t0 = chunk * CHUNK + wave * TPW;
+    float lnext[EPL];                               // the next token's logits, in flight
+    if (t0 < a.T) load_logits(a.logits + (size_t)t0 * E, E, lnext);
+    for (int it = 0; it < TPW; ++it) {
+        const int t = t0 + it;
         if (t >= a.T) break;                        // wave-uniform
+        float lcur[EPL];
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) lcur[m] = lnext[m];
+        if (it + 1 < TPW && t + 1 < a.T) load_logits(a.logits + (size_t)(t + 1) * E, E, lnext);
         TokenScores ts;
-        score_token(a.logits + (size_t)t * E, E, a.score, ts);
+        score_token(lcur, E, a.score, ts);
 #pragma unroll
         for (int m = 0; m < EPL; ++m) qacc[m] += ts.q[m];
 
@@ -142,8 +198,19 @@ route_topk_kernel(RouteArgs a) {
                 const int g = lane + 64 * h;
                 if (g < G) {
                     float b1 = -INFINITY, b2 = -INFINITY;
-                    for (int j = 0; j < gsize; ++j) {
-                        const float x = s_v[wave][g * gsize + j];
+                    const float* gvals = &s_v[wave][g * gsize];
+                    int j = 0;
+                    for (; j + 8 <= gsize; j += 8) {        // eight LDS reads in flight
+                        float x[8];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) x[u] = gvals[j + u];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            if (x[u] > b1) { b2 = b1; b1 = x[u]; } else if (x[u] > b2) b2 = x[u];
+                        }
+                    }
+                    for (; j < gsize; ++j) {
+                        const float x = gvals[j];
                         if (x > b1) { b2 = b1; b1 = x; } else if (x > b2) b2 = x;
                     }
                     gv[h] = top2 ? b1 + b2 : b1;
@@ -194,7 +261,7 @@ route_topk_kernel(RouteArgs a) {
         if (lane < k && (sel_e < 0 || sel_e >= E)) sel_e = 0;
         // gates from the unbiased score of each pick
         float w = (lane < k) ? selected_score(s_l[wave][sel_e], ts, a.score) : 0.f;
-        float S = wave_sum(w);
+        float S = wv_sum(w);
         if (lane < k) {
             a.topk_idx[(size_t)t * k + lane] = sel_e;
             a.gates[(size_t)t * k + lane] = (w / S) * a.route_scale;
@@ -244,10 +311,20 @@ expert_scan_kernel(ScanArgs a) {
 }
 
 // One wavefront per chunk of 64 tokens: stable slots in ascending token order.
+// The rank of a pick within the chunk is the number of earlier tokens (lanes) of
+// the chunk that picked the same expert: a 64-bit mask of picking lanes is built
+// per expert with integer LDS ORs (order-independent), and the rank is the
+// popcount of that mask below the lane.  A token never picks an expert twice.
 __global__ void __launch_bounds__(64)
 slot_assign_kernel(SlotArgs a) {
     __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+    __shared__ unsigned long long s_mask[MOE_MAX_EXPERTS];
     const int lane = threadIdx.x, chunk = blockIdx.x, E = a.E, k = a.k;
+    const int t = chunk * CHUNK + lane;
+    const bool valid = t < a.T;
+    int ex[MOE_MAX_K];
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_K; ++i) ex[i] = (valid && i < k) ? a.topk_idx[(size_t)t * k + i] : -1;
     // offsets = exclusive scan of counts (lane owns experts 4*lane .. 4*lane+3)
     int c4[4], loc = 0;
 #pragma unroll
@@ -265,7 +342,13 @@ slot_assign_kernel(SlotArgs a) {
         run += c4[j];
     }
     if (lane == 63) s_off[E] = incl;
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_K; ++i)
+        if (ex[i] >= 0) s_mask[ex[i]] = 0ull;
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_K; ++i)
+        if (ex[i] >= 0) atomicOr(&s_mask[ex[i]], 1ull << lane);
     if (chunk == 0) {
         for (int e = lane; e <= E; e += 64) a.offsets[e] = s_off[e];
         // m-tile prefix of every supported tile height (64, 128, 256 rows)
@@ -286,37 +369,25 @@ slot_assign_kernel(SlotArgs a) {
             if (lane == 63) tp[E] = ti;
         }
     }
-    const int t = chunk * CHUNK + lane;
-    const bool valid = t < a.T;
-    int ex[MOE_MAX_K];
-#pragma unroll
-    for (int i = 0; i < MOE_MAX_K; ++i) ex[i] = (valid && i < k) ? a.topk_idx[(size_t)t * k + i] : -1;
-    int cnt[MOE_MAX_K];
-#pragma unroll
-    for (int i = 0; i < MOE_MAX_K; ++i) cnt[i] = 0;
-    // rank among earlier tokens of the chunk that chose the same expert
-    for (int src = 0; src < 63; ++src) {
-        const bool before = src < lane;
-#pragma unroll
-        for (int j = 0; j < MOE_MAX_K; ++j) {
-            if (j >= k) break;
-            int ej = __builtin_amdgcn_readlane(ex[j], src);
-#pragma unroll
-            for (int i = 0; i < MOE_MAX_K; ++i) {
-                if (i >= k) break;
-                cnt[i] += (before && ej == ex[i]) ? 1 : 0;
-            }
-        }
-    }
+    __syncthreads();
     if (!valid) return;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int base[MOE_MAX_K];
+    float gt[MOE_MAX_K];
 #pragma unroll
     for (int i = 0; i < MOE_MAX_K; ++i) {
-        if (i >= k) break;
-        const int e = ex[i];
-        const int slot = s_off[e] + a.cbase[(size_t)e * a.nchunk + chunk] + cnt[i];
-        a.slot_of[(size_t)t * k + i] = slot;
-        a.token_of[slot] = t;
-        a.gate_of[slot] = a.gates[(size_t)t * k + i];
+        base[i] = (i < k) ? a.cbase[(size_t)ex[i] * a.nchunk + chunk] : 0;
+        gt[i] = (i < k) ? a.gates[(size_t)t * k + i] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < MOE_MAX_K; ++i) {
+        if (i < k) {
+            const int e = ex[i];
+            const int slot = s_off[e] + base[i] + __popcll(s_mask[e] & below);
+            a.slot_of[(size_t)t * k + i] = slot;
+            a.token_of[slot] = t;
+            a.gate_of[slot] = gt[i];
+        }
     }
 }
 
@@ -393,7 +464,11 @@ router_bwd_kernel(RouterBwdArgs a) {
     if (t >= a.T) return;
     const int E = a.E, k = a.k;
     TokenScores ts;
-    score_token(a.logits + (size_t)t * E, E, a.score, ts);
+    {
+        float l[EPL];
+        load_logits(a.logits + (size_t)t * E, E, l);
+        score_token(l, E, a.score, ts);
+    }
     int e_i = -1;
     float g_i = 0.f, dg_i = 0.f, w_i = 0.f;
     if (lane < k) {
@@ -402,8 +477,8 @@ router_bwd_kernel(RouterBwdArgs a) {
         dg_i = a.dgate[(size_t)t * k + lane];
         w_i = selected_score(a.logits[(size_t)t * E + e_i], ts, a.score);
     }
-    const float S = wave_sum(w_i);
-    const float gdg = wave_sum(g_i * dg_i);
+    const float S = wv_sum(w_i);
+    const float gdg = wv_sum(g_i * dg_i);
     // g = c w / S: dL/dw_i = (c dg_i - sum_j g_j dg_j) / S
     const float dw_i = (lane < k) ? (a.route_scale * dg_i - gdg) / S : 0.f;
     // aux gradient: dq_te = aux_coef * E * f_e / T, f_e = counts_e / (T k)
@@ -427,14 +502,14 @@ router_bwd_kernel(RouterBwdArgs a) {
         float dot = 0.f;
 #pragma unroll
         for (int m = 0; m < EPL; ++m) dot += (dq[m] + sel[m]) * ts.s[m];
-        dot = wave_sum(dot);
+        dot = wv_sum(dot);
 #pragma unroll
         for (int m = 0; m < EPL; ++m) out[m] = ts.s[m] * (dq[m] + sel[m] - dot);
     } else {
         float dot = 0.f;
 #pragma unroll
         for (int m = 0; m < EPL; ++m) dot += dq[m] * ts.q[m];
-        dot = wave_sum(dot);
+        dot = wv_sum(dot);
         const float invZ = 1.0f / ts.z;
 #pragma unroll
         for (int m = 0; m < EPL; ++m) {
@@ -452,7 +527,7 @@ router_bwd_kernel(RouterBwdArgs a) {
 // ---- host launchers ------------------------------------------------------------
 hipError_t launch_route_topk(const RouteArgs& a, hipStream_t s) {
     if (a.nchunk == 0) return hipSuccess;
-    hipLaunchKernelGGL(route_topk_kernel, dim3(a.nchunk), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(route_topk_kernel, dim3(a.nchunk), dim3(64 * RT_WAVES), 0, s, a);
     return hipGetLastError();
 }
 hipError_t launch_expert_scan(const ScanArgs& a, int E, hipStream_t s) {
