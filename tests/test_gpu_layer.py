@@ -73,11 +73,25 @@ SHARED_CASES = [
 ]
 
 
+# the limits: k = MOE_MAX_K = 16 (the dispatch kernels' generic-k path), E = MOE_MAX_EXPERTS = 256
+# with most experts below one 64-row tile (narrow tail tiles, some experts empty), and the
+# compiled k = 6 specialisation of the dispatch kernels
+LIMIT_CASES = [
+    wl("f32_relu_k16_e16", E=16, k=16),
+    wl("bf16_swiglu_k16", T=300, d=128, E=32, ffn=192, k=16, dtype="bf16", expert="swiglu"),
+    wl("bf16_swiglu_e256_groups", T=512, d=128, E=256, ffn=128, k=8, n_groups=8, topk_groups=4,
+       dtype="bf16", expert="swiglu", score="sigmoid"),
+    wl("bf16_gelu_k6_groups", T=300, d=192, E=16, ffn=256, k=6, n_groups=8, topk_groups=4,
+       dtype="bf16", expert="gelu", score="sigmoid"),
+]
+
+
 def _inputs(w, seed=0):
     return W.make_inputs(w, seed=seed, masters=True)
 
 
-@pytest.mark.parametrize("w", F32_CASES + BF16_CASES + VARIANT_CASES + SHARED_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("w", F32_CASES + BF16_CASES + VARIANT_CASES + SHARED_CASES + LIMIT_CASES,
+                         ids=lambda w: w.name)
 def test_forward_backward_parity(w):
     say(f"layer parity {w}")
     inp = _inputs(w)
@@ -214,7 +228,7 @@ def test_train_step_parity(w):
 
 
 FUSED_CASES = [F32_CASES[0], F32_CASES[2], BF16_CASES[0], BF16_CASES[1], BF16_CASES[2], BF16_CASES[5],
-               VARIANT_CASES[2], SHARED_CASES[0], SHARED_CASES[2], SHARED_CASES[3]]
+               VARIANT_CASES[2], SHARED_CASES[0], SHARED_CASES[2], SHARED_CASES[3], LIMIT_CASES[2]]
 
 
 @pytest.mark.parametrize("w", [SHARED_CASES[1], SHARED_CASES[4]], ids=lambda w: w.name)
