@@ -50,7 +50,8 @@
 //     output is written as zeros); DENSE is one plain GEMM.  The hardware
 //     deals workgroups round-robin to the 8 XCDs; the kernel groups the XCDs
 //     (G per group) and gives each group a contiguous, equal share of the
-//     tiles, dealt round-robin among its members.
+//     tiles (in KSEG mode, of each segment's tiles, since a tile's cost there
+//     follows its segment's row count), dealt round-robin among its members.
 #include "common.hpp"
 #include "kernels.hpp"
 
