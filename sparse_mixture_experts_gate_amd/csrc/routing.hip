@@ -7,9 +7,9 @@
 // (group-limited selection, ties to the smaller group/expert id).
 //
 // Layout: one 64-lane wavefront owns one token at a time; lane j holds the
-// logits of experts j, j+64, j+128, j+192.  A workgroup of four wavefronts
-// owns a chunk of 64 consecutive tokens, which is the unit of the histogram
-// and of the stable slot ranking.  No floating-point atomics anywhere; the
+// logits of experts j, j+64, j+128, j+192.  A workgroup of sixteen
+// wavefronts (four tokens each) owns a chunk of 64 consecutive tokens, which
+// is the unit of the histogram and of the stable slot ranking.  No floating-point atomics anywhere; the
 // integer LDS histogram is order-independent and every float sum runs in a
 // fixed order.
 #include "common.hpp"
