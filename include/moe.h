@@ -148,6 +148,11 @@ typedef struct moe_weights {
  *   slot_of  int32 [T,k]   expert-major row of (t, i)
  *   token_of int32 [T*k]   token of each expert-major row
  *   aux      float [1]     aux load-balancing loss (unscaled)
+ *   src_k    int32 [T*k]   pick index i of each expert-major row, so that
+ *                          slot_of[token_of[p], src_k[p]] == p; optional: NULL
+ *                          leaves it unwritten (no kernel of this library reads it)
+ * token_of and src_k are the inverse of slot_of ("Trainable MoE in CUDA" outline
+ * Part 4, the packed dispatch tables).
  * moe_backward reads logits, topk_idx, gates, counts, slot_of and token_of.
  */
 typedef struct moe_routing {
@@ -159,6 +164,7 @@ typedef struct moe_routing {
     int32_t* slot_of;
     int32_t* token_of;
     float*   aux;
+    int32_t* src_k;
 } moe_routing;
 
 /*

@@ -228,6 +228,7 @@ class Routing:
     offsets: np.ndarray    # [E + 1], exclusive scan of counts
     slot_of: np.ndarray    # [T, k]   row of (t, i) in the expert-major buffer
     token_of: np.ndarray   # [T * k]  token of each expert-major row
+    src_k: np.ndarray = None  # [T * k]  pick index i of each expert-major row
 
 
 def routing_tables(topk_idx, E):
@@ -235,7 +236,8 @@ def routing_tables(topk_idx, E):
 
     slot_of[t, i] = offsets[e] + #{t' < t : e in topk_idx[t']} for
     e = topk_idx[t, i]: a stable counting sort of the row-major (t, i) list by
-    expert.
+    expert.  token_of and src_k invert it: row p holds pick src_k[p] of token
+    token_of[p].
     """
     T, k = topk_idx.shape
     flat = topk_idx.reshape(-1)
@@ -246,7 +248,8 @@ def routing_tables(topk_idx, E):
     slot_flat = np.empty(T * k, dtype=np.int64)
     slot_flat[order] = np.arange(T * k)
     token_of = order // k
-    return Routing(topk_idx, counts, offsets, slot_flat.reshape(T, k), token_of)
+    src_k = order % k                               # (t, i) = divmod of the row-major position
+    return Routing(topk_idx, counts, offsets, slot_flat.reshape(T, k), token_of, src_k)
 
 
 def gather_rows(X, token_of):

@@ -55,9 +55,11 @@ class moe_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in WEIGHTS]
 
 
+ROUTING = ("logits", "topk_idx", "gates", "counts", "offsets", "slot_of", "token_of", "aux", "src_k")
+
+
 class moe_routing(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("logits", "topk_idx", "gates", "counts", "offsets", "slot_of", "token_of", "aux")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ROUTING]
 
 
 class moe_grads(ctypes.Structure):
@@ -69,6 +71,7 @@ class moe_params(ctypes.Structure):
 
 
 _lib = None
+ABI_VERSION = 4                 # the structs above, as include/moe.h declares them
 
 
 def load() -> ctypes.CDLL:
@@ -103,6 +106,9 @@ def load() -> ctypes.CDLL:
         lib.moe_status_string.restype = ctypes.c_char_p
         lib.moe_abi_version.argtypes = []
         lib.moe_abi_version.restype = ctypes.c_int32
+        if lib.moe_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {lib.moe_abi_version()}, this binding "
+                               f"expects {ABI_VERSION}: rebuild it")
         _lib = lib
     return _lib
 
@@ -156,8 +162,7 @@ def abi_version() -> int:
 
 
 def routing_struct(r: dict) -> moe_routing:
-    return moe_routing(*[_p(r.get(n)) for n in
-                         ("logits", "topk_idx", "gates", "counts", "offsets", "slot_of", "token_of", "aux")])
+    return moe_routing(*[_p(r.get(n)) for n in ROUTING])
 
 
 def weights_struct(w: dict) -> moe_weights:
@@ -276,7 +281,8 @@ def alloc_routing(w, device) -> dict:
             "offsets": torch.empty(E + 1, dtype=i32, device=device),
             "slot_of": torch.empty(T, k, dtype=i32, device=device),
             "token_of": torch.empty(T * k, dtype=i32, device=device),
-            "aux": torch.empty(1, dtype=f32, device=device)}
+            "aux": torch.empty(1, dtype=f32, device=device),
+            "src_k": torch.empty(T * k, dtype=i32, device=device)}
 
 
 def alloc_grads(w, device) -> dict:

@@ -36,6 +36,7 @@ struct SlotArgs {
     int32_t* slot_of;      // [T,k]
     int32_t* token_of;     // [T*k]
     float* gate_of;        // [T*k]
+    int32_t* src_k;        // [T*k] pick index of each row, or NULL
     int T, E, k, nchunk;
 };
 struct FinalizeArgs {

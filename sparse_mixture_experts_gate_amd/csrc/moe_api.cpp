@@ -143,12 +143,18 @@ struct Ptrs {
     bool tok[kMax];
     int n = 0;
     bool overflow = false;
+    bool misaligned_opt = false;
     void add(const void* p, bool t = false) {
         if (n == kMax) { overflow = true; return; }
         list[n] = p; tok[n] = t; ++n;
     }
+    // an optional output: NULL skips it, otherwise it must be aligned like the rest
+    void add_optional(const void* p) {
+        if (p && !aligned16(p)) misaligned_opt = true;
+    }
     int check(int T) const {
         if (overflow) return MOE_ERR_INVALID_ARG;
+        if (misaligned_opt) return MOE_ERR_MISALIGNED;
         for (int i = 0; i < n; ++i) {
             if (!list[i]) {
                 if (tok[i] && T == 0) continue;
@@ -180,6 +186,7 @@ void add_routing(Ptrs& P, const moe_routing* r, bool logits) {
     if (logits) P.add(r->logits, true);
     P.add(r->topk_idx, true); P.add(r->gates, true); P.add(r->counts); P.add(r->offsets);
     P.add(r->slot_of, true); P.add(r->token_of, true); P.add(r->aux);
+    P.add_optional(r->src_k);
 }
 
 // experts = false: the expert weight gradients (dW1, dW2, dW3) are not stored.
@@ -222,7 +229,7 @@ int run_routing(const Ctx& x, const float* logits, const float* e_bias, moe_rout
     TRY(launch_expert_scan(sa, c->E, x.s));
     SlotArgs sl = {r->counts, x.buf<int32_t>(B_CBASE), r->topk_idx, r->gates, r->offsets,
                    x.buf<int32_t>(B_TPREFIX), r->slot_of, r->token_of, x.buf<float>(B_GATEOF),
-                   c->T, c->E, c->k, nchunk(c)};
+                   r->src_k, c->T, c->E, c->k, nchunk(c)};
     TRY(launch_slot_assign(sl, x.s));
     FinalizeArgs fa = {x.buf<float>(B_QPART), r->counts, nullptr, 0, r->aux, nullptr, 0.f,
                        c->T, c->d, c->E, c->k, nchunk(c)};
@@ -384,7 +391,7 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 3; }
+int32_t moe_abi_version(void) { return 4; }
 
 const char* moe_status_string(int st) {
     switch (st) {

@@ -387,6 +387,7 @@ slot_assign_kernel(SlotArgs a) {
             a.slot_of[(size_t)t * k + i] = slot;
             a.token_of[slot] = t;
             a.gate_of[slot] = gt[i];
+            if (a.src_k) a.src_k[slot] = i;
         }
     }
 }

@@ -190,6 +190,8 @@ def check_routing_tables(r_gpu, resolved, w):
     assert np.array_equal(r_gpu["offsets"].cpu().numpy(), rt.offsets)
     assert np.array_equal(r_gpu["slot_of"].cpu().numpy(), rt.slot_of)
     assert np.array_equal(r_gpu["token_of"].cpu().numpy(), rt.token_of)
+    if "src_k" in r_gpu:
+        assert np.array_equal(r_gpu["src_k"].cpu().numpy(), rt.src_k)
     return rt
 
 

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert L.abi_version() == 3
+    assert L.abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert L.status_string(code) and L.status_string(code) != "unknown status"
     assert L.status_string(12345) == "unknown status"
@@ -170,6 +170,19 @@ def test_pointer_and_workspace_errors(lib):
     st = lib.moe_forward(ctypes.byref(cfg), ctypes.c_void_p(4096), ctypes.byref(w), ctypes.c_void_p(4096),
                          ctypes.byref(r), ctypes.c_void_p(4096), need, None)
     assert st == -2
+
+
+def test_optional_src_k_is_checked_for_alignment(lib):
+    """src_k may be NULL (the default of the other tests); a misaligned one is
+    rejected before any launch."""
+    cfg = L.config(W.WORKLOADS[0])
+    need = L.workspace_bytes(cfg)
+    lib = L.load()
+    w = L.moe_weights(*([4096] * 6))
+    r = L.moe_routing(*([4096] * 8), 4100)
+    st = lib.moe_forward(ctypes.byref(cfg), ctypes.c_void_p(4096), ctypes.byref(w), ctypes.c_void_p(4096),
+                         ctypes.byref(r), ctypes.c_void_p(4096), need, None)
+    assert st == -3
 
 
 def test_binding_raises_on_error_status(lib):

@@ -63,6 +63,7 @@ def test_route_bit_exact(T, E, k, G, TG, score, kind):
     assert np.array_equal(r["offsets"].numpy(), rt.offsets)
     assert np.array_equal(r["slot_of"].numpy(), rt.slot_of)
     assert np.array_equal(r["token_of"].numpy(), rt.token_of)
+    assert np.array_equal(r["src_k"].numpy(), rt.src_k)
     if T:
         g, _ = O.gate_weights(l64, ref, score)
         assert_close("gates", r["gates"].double().numpy(), g, 1e-5, 1e-5)
@@ -120,6 +121,7 @@ def test_route_variants(T, E, k, G, TG, score, kind, bstd, gs, rs):
     assert np.array_equal(r["offsets"].numpy(), rt.offsets)
     assert np.array_equal(r["slot_of"].numpy(), rt.slot_of)
     assert np.array_equal(r["token_of"].numpy(), rt.token_of)
+    assert np.array_equal(r["src_k"].numpy(), rt.src_k)
     g, _ = O.gate_weights(l64, resolved, score, rs)
     assert_close("gates", r["gates"].double().numpy(), g, 1e-5, 1e-5)
     aux, _, _ = O.aux_loss(rt.counts, O.aux_probs(l64, score), k)

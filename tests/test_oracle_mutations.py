@@ -48,7 +48,7 @@ def _bad_silu_grad(x):
 def _descending_slots(topk_idx, E):
     r = _orig_tables(topk_idx[::-1], E)
     T, k = topk_idx.shape
-    return O.Routing(topk_idx, r.counts, r.offsets, r.slot_of[::-1], (T - 1) - r.token_of)
+    return O.Routing(topk_idx, r.counts, r.offsets, r.slot_of[::-1], (T - 1) - r.token_of, r.src_k)
 
 
 _orig_tables = O.routing_tables

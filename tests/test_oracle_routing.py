@@ -130,6 +130,10 @@ def test_routing_tables_definition(T, E, k):
     for t in range(T):
         for i in range(k):
             assert r.token_of[r.slot_of[t, i]] == t
+            assert r.src_k[r.slot_of[t, i]] == i
+    for p in range(T * k):                      # brute force: the unique (t, i) stored at row p
+        hits = [(t, i) for t in range(T) for i in range(k) if r.slot_of[t, i] == p]
+        assert hits == [(r.token_of[p], r.src_k[p])]
     for e in range(E):
         seg = r.token_of[r.offsets[e]:r.offsets[e + 1]]
         assert np.all(np.diff(seg) > 0)
@@ -142,6 +146,7 @@ def test_empty_expert_segments():
     assert r.offsets.tolist() == [0, 3, 3, 6, 6, 6]
     assert r.slot_of.tolist() == [[3, 0], [1, 4], [5, 2]]
     assert r.token_of.tolist() == [0, 1, 2, 0, 1, 2]
+    assert r.src_k.tolist() == [1, 0, 1, 0, 1, 0]
 
 
 @pytest.mark.parametrize("score", ["softmax", "sigmoid"])
