@@ -47,11 +47,15 @@
 //     walks the m-tiles of every expert's row segment (prefix of per-expert
 //     tile counts, binary search per workgroup); KSEG mode gives each expert
 //     its own output and runs K over its row segment (empty segment -> the
-//     output is written as zeros); DENSE is one plain GEMM.  The hardware
+//     output is written as zeros); DENSE is one plain GEMM, or with kchunk
+//     set, one fp32 partial output per K segment (summed afterwards in
+//     segment order).  The hardware
 //     deals workgroups round-robin to the 8 XCDs; the kernel groups the XCDs
 //     (G per group) and gives each group a contiguous, equal share of the
 //     tiles (in KSEG mode, of each segment's tiles, since a tile's cost there
 //     follows its segment's row count), dealt round-robin among its members.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -273,7 +277,7 @@ gemm_bf16_kernel(GemmParams p) {
     int nreal;
     if (MODE == MODE_ROWS) nreal = p.tile_prefix[p.E] * NT;
     else if (MODE == MODE_KSEG) nreal = p.E * ((p.M + TM - 1) / TM) * NT;
-    else nreal = ((p.M + BM - 1) / BM) * NT;
+    else nreal = ((p.M + BM - 1) / BM) * NT * (p.kchunk > 0 ? (p.K + p.kchunk - 1) / p.kchunk : 1);
     nreal = uni(nreal);
     int L = blockIdx.x;
     {
@@ -305,6 +309,7 @@ gemm_bf16_kernel(GemmParams p) {
     long row_base = 0;
     int rows_valid = 0;
     int K = p.K;
+    int kbase = 0;                 // DENSE split over K: first column of this segment's K range
     if (MODE == MODE_ROWS) {
         const int tmg = L / NT;
         int lo = 0, hi = p.E;
@@ -336,12 +341,18 @@ gemm_bf16_kernel(GemmParams p) {
         }
     } else {
         const int MT = (p.M + BM - 1) / BM;
-        int tm;
-        grouped(L, MT, NT, tm, n_t);
+        int tm, Lt = L;
+        if (p.kchunk > 0) {        // segment e: K columns [e kchunk, min((e+1) kchunk, K))
+            e = L / (MT * NT);
+            Lt = L - e * MT * NT;
+            kbase = e * p.kchunk;
+            K = min(p.kchunk, p.K - kbase);
+        }
+        grouped(Lt, MT, NT, tm, n_t);
         m0 = tm * BM;
         rows_valid = min(BM, p.M - m0);
     }
-    e = uni(e); m0 = uni(m0); n_t = uni(n_t); rows_valid = uni(rows_valid); K = uni(K);
+    e = uni(e); m0 = uni(m0); n_t = uni(n_t); rows_valid = uni(rows_valid); K = uni(K); kbase = uni(kbase);
     row_base = (long)uni((int)row_base);
     const int n0 = n_t * BN;
     const int hid0 = n_t * 128;
@@ -354,8 +365,8 @@ gemm_bf16_kernel(GemmParams p) {
         rsrc_t r = make_rsrc(base, ((long)K * p.lda - m0) * 2);
         pa = plan_strided<TM>(r, r, (uint32_t)(p.lda * 2), 0x7fffffff);
     } else {    // A[m][k]
-        const bf16* base = p.A + (row_base + m0) * p.lda;
-        rsrc_t r = make_rsrc(base, (long)rows_valid * p.lda * 2);
+        const bf16* base = p.A + (row_base + m0) * p.lda + kbase;
+        rsrc_t r = make_rsrc(base, ((long)rows_valid * p.lda - kbase) * 2);
         pa = plan_direct(r, r, (uint32_t)(p.lda * 2), 0);
     }
     if (BT) {   // B[k][n]
@@ -377,7 +388,7 @@ gemm_bf16_kernel(GemmParams p) {
                              make_rsrc(B2e + (long)hid0 * p.ldb, (long)(p.ffn - hid0) * p.ldb * 2),
                              (uint32_t)(p.ldb * 2), 1);
         else {
-            rsrc_t r = make_rsrc(Be + (long)n0 * p.ldb, (long)min(BN, p.N - n0) * p.ldb * 2);
+            rsrc_t r = make_rsrc(Be + (long)n0 * p.ldb + kbase, ((long)min(BN, p.N - n0) * p.ldb - kbase) * 2);
             pb = plan_direct(r, r, (uint32_t)(p.ldb * 2), 0);
         }
     }
@@ -633,8 +644,8 @@ gemm_bf16_kernel(GemmParams p) {
                         if (MODE == MODE_KSEG) {
                             const bool sec = row >= c2;
                             store4((sec ? C2 : C1) + (long)e * p.ces + (sec ? row - c2 : row) * p.ldc + n, v);
-                        } else {
-                            store4(C1 + row * p.ldc + n, v);
+                        } else {       // DENSE split over K: segment e's partial output
+                            store4(C1 + (MODE == MODE_DENSE ? (long)e * p.ces : 0L) + row * p.ldc + n, v);
                         }
                     }
                 }
@@ -1006,6 +1017,25 @@ hipError_t mfma_up_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     return run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
 }
 
+__global__ void __launch_bounds__(256) sum_partials_kernel(const float* part, float* out, long n4, int nsplit);
+
+// K segments of the router logits: few output tiles (N = E <= 256 columns) would leave
+// most CUs idle, so K = d is split until the tiles about fill the 256 CUs, keeping at
+// least 256 columns (eight k-tiles) per segment and at most 8 segments.  Segment
+// width is a multiple of 64 columns.
+int router_logit_kchunk(int T, int E, int d) {
+    const int tiles = ((T + BM - 1) / BM) * ((E + BN - 1) / BN);
+    if (tiles <= 0) return 0;                         // no tokens: nothing to split
+    int s = (256 + tiles - 1) / tiles;
+    s = std::min(s, std::min(8, d / 256));
+    if (s <= 1) return 0;
+    return ((d + s - 1) / s + 63) / 64 * 64;
+}
+int router_logit_splits(int T, int E, int d) {
+    const int kc = router_logit_kchunk(T, E, d);
+    return kc > 0 ? (d + kc - 1) / kc : 1;
+}
+
 hipError_t mfma_router_logits(const RouterGemmArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
     GemmParams p = {};
@@ -1014,8 +1044,18 @@ hipError_t mfma_router_logits(const RouterGemmArgs& a, hipStream_t s) {
     p.B = (const bf16*)a.Wg; p.ldb = a.d;
     p.M = a.T; p.N = a.E; p.K = a.d;
     p.C = a.logits; p.ldc = a.E;
-    const int grid = ((a.T + BM - 1) / BM) * ((a.E + BN - 1) / BN);
-    return run<MODE_DENSE, false, false, EPI_STORE, true>(p, grid, s);
+    const int nseg = a.logit_part ? router_logit_splits(a.T, a.E, a.d) : 1;
+    if (nseg > 1) {
+        p.kchunk = router_logit_kchunk(a.T, a.E, a.d);
+        p.C = a.logit_part; p.ces = (long)a.T * a.E;
+    }
+    const int grid = nseg * ((a.T + BM - 1) / BM) * ((a.E + BN - 1) / BN);
+    hipError_t st = run<MODE_DENSE, false, false, EPI_STORE, true>(p, grid, s);
+    if (st != hipSuccess || nseg == 1) return st;
+    const long n4 = (long)a.T * a.E / 4;                 // E is a multiple of 8 on this path
+    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       (const float*)a.logit_part, a.logits, n4, nseg);
+    return hipGetLastError();
 }
 
 hipError_t mfma_router_dx(const RouterGemmArgs& a, hipStream_t s) {

@@ -28,7 +28,7 @@ constexpr int kChunk = 64;
 
 enum WsBuf {
     B_XP = 0, B_H, B_A, B_EO, B_DEO, B_DH, B_DXP, B_DY, B_DXR, B_DL, B_DGATE, B_GATEOF,
-    B_HIST, B_CBASE, B_QPART, B_LPART, B_TPREFIX, B_DWGPART,
+    B_HIST, B_CBASE, B_QPART, B_LPART, B_TPREFIX, B_DWGPART, B_LOGPART,
     // shared-experts branch: [H1 | H3] [T, 2 Hs], A [T, Hs], Ys [T, d], dH [T, 2 Hs],
     // dX part [T, d], and its one-segment tables (offsets {0, T}, tile prefixes)
     B_HS, B_AS, B_YS, B_DHS, B_DXS, B_STAB,
@@ -118,6 +118,9 @@ Layout layout(const moe_config* c) {
     // split-K partials of the router weight gradient (bf16 path only)
     const int nsplit = c->dtype == MOE_DTYPE_F32 ? 0 : router_dwg_splits(c->T);
     sz[B_DWGPART] = nsplit > 1 ? (size_t)nsplit * E * d * 4 : 0;
+    // split-K partials of the router logits (bf16 path only)
+    const int lsplit = c->dtype == MOE_DTYPE_F32 ? 0 : router_logit_splits(c->T, c->E, c->d);
+    sz[B_LOGPART] = lsplit > 1 ? (size_t)lsplit * T * E * 4 : 0;
     const size_t hs = shared_hidden(c);
     sz[B_HS] = T * 2 * hs * s;
     sz[B_AS] = T * hs * s;
@@ -275,7 +278,8 @@ int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_
     const moe_config* c = x.c;
     const bool f32 = c->dtype == MOE_DTYPE_F32;
     const int vec = c->d * esize(c) / 16;
-    RouterGemmArgs rg = {c->T, c->d, c->E, X, w->Wg, nullptr, r->logits, nullptr, nullptr, nullptr};
+    RouterGemmArgs rg = {c->T, c->d, c->E, X, w->Wg, nullptr, r->logits, nullptr, nullptr, nullptr,
+                         !f32 && router_logit_splits(c->T, c->E, c->d) > 1 ? x.buf<float>(B_LOGPART) : nullptr};
     TRY(x.mark(MOE_STAGE_ROUTER_LOGITS));
     TRY(f32 ? simple_router_logits(rg, x.s) : mfma_router_logits(rg, x.s));
     TRY(x.mark(MOE_STAGE_ROUTE));

@@ -172,6 +172,15 @@ def test_pointer_and_workspace_errors(lib):
     assert st == -2
 
 
+@pytest.mark.parametrize("T", [0, 1, 255, 256, 257])
+def test_workspace_sizing_at_few_tokens(lib, T):
+    """The host-side layout (router split choices included) handles T = 0 and
+    single-tile sizes; T = 0 once divided by a zero tile count."""
+    for w in W.WORKLOADS[1:]:
+        n = L.workspace_bytes(L.config(w.replace(T=T)))
+        assert n > 0, (w.name, T)
+
+
 def test_optional_src_k_is_checked_for_alignment(lib):
     """src_k may be NULL (the default of the other tests); a misaligned one is
     rejected before any launch."""
