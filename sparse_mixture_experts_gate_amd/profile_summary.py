@@ -84,6 +84,11 @@ def _calibration(rows, mib):
     return (mib * 1024.0) / big["kib"], big
 
 
+def _starts_step(name):
+    """A training step starts with the router-logits GEMM (bf16 or float32)."""
+    return "gemm_bf16_kernel<2, false, false" in name or "s_router_logits" in name
+
+
 def _stage_of(name, state):
     """Stage of a library kernel, given the kernels of the step seen so far.  The
     shared-experts branch reuses the expert GEMM templates: its forward follows its
@@ -121,8 +126,8 @@ def _stage_of(name, state):
     if "gemm_bf16_kernel<1, true, true" in name:
         state["wgrad"] += 1
         return {1: "down_wgrad", 2: "up_wgrad"}.get(state["wgrad"], "router_dwg")
-    if "sum_partials_kernel" in name:
-        return "router_dwg"
+    if "sum_partials_kernel" in name:      # the K segments of the logits, or of dWg
+        return "router_logits" if state["stage"] == "router_logits" else "router_dwg"
     if "colsum_kernel" in name:
         return "bias_grads"
     if "router_bwd_kernel" in name:
@@ -146,11 +151,11 @@ def summarize(fetch_csv, write_csv, mib):
         acc = {}
         started = False
         for r in rows:
-            st = _stage_of(r["name"], state)
-            if st == "router_logits":
+            if _starts_step(r["name"]):
                 if started:
                     break          # the next step: keep the first one only
                 started = True
+            st = _stage_of(r["name"], state)
             if not started or st is None:
                 continue
             state["stage"] = st
@@ -212,11 +217,10 @@ def stage_durations(trace_csv):
     rows.sort(key=lambda r: int(r[key]))
     acc, steps, state = {}, 0, {"stage": None, "wgrad": 0}
     for r in rows:
-        st = _stage_of(r["Kernel_Name"], state)
-        if st == "router_logits":
+        if _starts_step(r["Kernel_Name"]):
             steps += 1
             state = {"stage": None, "wgrad": 0}
-            st = _stage_of(r["Kernel_Name"], state)
+        st = _stage_of(r["Kernel_Name"], state)
         if steps == 0 or st is None:
             continue
         state["stage"] = st
@@ -276,11 +280,11 @@ def mfma_markdown(path, title, command):
     rows, started = [], False
     for did in sorted(per):
         d = per[did]
-        st = _stage_of(d["name"], state)
-        if st == "router_logits":
+        if _starts_step(d["name"]):
             if started:
                 break
             started = True
+        st = _stage_of(d["name"], state)
         if not started or st is None:
             continue
         state["stage"] = st
