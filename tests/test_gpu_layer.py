@@ -83,6 +83,9 @@ LIMIT_CASES = [
        dtype="bf16", expert="swiglu", score="sigmoid"),
     wl("bf16_gelu_k6_groups", T=300, d=192, E=16, ffn=256, k=6, n_groups=8, topk_groups=4,
        dtype="bf16", expert="gelu", score="sigmoid"),
+    # router logits split over K into segments of 320, 320 and 192 columns (a ragged last one)
+    wl("bf16_swiglu_router_ragged_split", T=300, d=832, E=8, ffn=128, k=2, dtype="bf16",
+       expert="swiglu"),
 ]
 
 
