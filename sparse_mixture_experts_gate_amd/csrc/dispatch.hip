@@ -160,27 +160,51 @@ __global__ void __launch_bounds__(256) scatter_kernel(ScatterArgs a) {
     const uint4* dxp = reinterpret_cast<const uint4*>(a.dXp);
     // router-path gradient is fp32 [T, d]: N floats per vector of T
     const float* dxr = a.dXr + (size_t)t * a.vec * N;
-    for (int v = lane; v < a.vec; v += 64) {
-        float acc[N];
-#pragma unroll
-        for (int j = 0; j < N; ++j) acc[j] = 0.f;
+    // two vectors of the row per pass, all their loads issued before the sums (a lane
+    // past the row's end reloads its first vector and does not store the second)
+    for (int v0 = lane; v0 < a.vec; v0 += 128) {
+        const bool two = v0 + 64 < a.vec;
+        const int v1 = two ? v0 + 64 : v0;
+        uint4 r[2][MOE_MAX_K];
 #pragma unroll
         for (int i = 0; i < MOE_MAX_K; ++i) {
             if (i >= k) break;
-            float x[N];
-            Vec16<T>::unpack(dxp[(size_t)sl[i] * a.vec + v], x);
+            r[0][i] = dxp[(size_t)sl[i] * a.vec + v0];
+            r[1][i] = dxp[(size_t)sl[i] * a.vec + v1];
+        }
+        float4 q[2][N / 4];
 #pragma unroll
-            for (int j = 0; j < N; ++j) acc[j] += x[j];
+        for (int h = 0; h < N / 4; ++h) {
+            q[0][h] = reinterpret_cast<const float4*>(dxr + v0 * N)[h];
+            q[1][h] = reinterpret_cast<const float4*>(dxr + v1 * N)[h];
         }
 #pragma unroll
-        for (int j = 0; j < N; ++j) acc[j] += dxr[v * N + j];
-        if (a.dXs) {                       // shared branch
-            float xs[N];
-            Vec16<T>::unpack(reinterpret_cast<const uint4*>(a.dXs)[(size_t)t * a.vec + v], xs);
+        for (int u = 0; u < 2; ++u) {
+            const int v = u ? v1 : v0;
+            float acc[N];
 #pragma unroll
-            for (int j = 0; j < N; ++j) acc[j] += xs[j];
+            for (int j = 0; j < N; ++j) acc[j] = 0.f;
+#pragma unroll
+            for (int i = 0; i < MOE_MAX_K; ++i) {
+                if (i >= k) break;
+                float x[N];
+                Vec16<T>::unpack(r[u][i], x);
+#pragma unroll
+                for (int j = 0; j < N; ++j) acc[j] += x[j];
+            }
+#pragma unroll
+            for (int h = 0; h < N / 4; ++h) {
+                acc[4 * h] += q[u][h].x; acc[4 * h + 1] += q[u][h].y;
+                acc[4 * h + 2] += q[u][h].z; acc[4 * h + 3] += q[u][h].w;
+            }
+            if (a.dXs) {                       // shared branch
+                float xs[N];
+                Vec16<T>::unpack(reinterpret_cast<const uint4*>(a.dXs)[(size_t)t * a.vec + v], xs);
+#pragma unroll
+                for (int j = 0; j < N; ++j) acc[j] += xs[j];
+            }
+            if (u == 0 || two) reinterpret_cast<uint4*>(a.dX)[(size_t)t * a.vec + v] = Vec16<T>::pack(acc);
         }
-        reinterpret_cast<uint4*>(a.dX)[(size_t)t * a.vec + v] = Vec16<T>::pack(acc);
     }
 }
 
