@@ -405,7 +405,9 @@ gemm_bf16_kernel(GemmParams p) {
     constexpr int IPW_A = AT ? BK / (512 / TM) / 4 : DIRECT_IPW;
     constexpr int IPW_B = BT ? STRIDED_IPW : DIRECT_IPW;
     constexpr int LPW = IPW_A + IPW_B;                 // loads per wave per k-tile
-    static_assert(LPW % KSTEPS == 0 && LPW / KSTEPS <= 8, "load parts");
+    // each k-step issues PART loads in its MFMA slots; the narrowest wave layout (2 x 2)
+    // has 4 slots a k-step, so PART <= 4 keeps every load of a k-tile issued
+    static_assert(LPW % KSTEPS == 0 && LPW / KSTEPS <= 4, "load parts");
     constexpr int PART = LPW / KSTEPS;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
     const int nk = (K + BK - 1) / BK;
