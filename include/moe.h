@@ -275,26 +275,26 @@ int moe_train_step(const moe_config* cfg, const void* X, const void* Y_target,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stages of one training step, in launch order (moe_train_step_profiled). */
-#define MOE_STAGE_ROUTER_LOGITS   0   /* F1  l = X Wg^T                          */
-#define MOE_STAGE_ROUTE           1   /* F2-F3 top-k, gates, histogram, scan, slots, aux */
-#define MOE_STAGE_GATHER          2   /* F4  Xp = X[token_of]                    */
-#define MOE_STAGE_UP_FWD          3   /* F5  H = Xp W1^T (|W3^T), A = act(H)      */
-#define MOE_STAGE_DOWN_FWD        4   /* F6  EO = A W2^T (+ b2)                   */
-#define MOE_STAGE_SHARED_FWD      5   /*     shared branch Ys = SwiGLU(X) (n_shared > 0) */
-#define MOE_STAGE_COMBINE_LOSS    6   /* F7-F8 Y (+ Ys), MSE, dY, loss scalars    */
-#define MOE_STAGE_COMBINE_BWD     7   /* B1  dgate, dEO                           */
-#define MOE_STAGE_DOWN_DGRAD      8   /* B2  dA = dEO W2, activation backward     */
-#define MOE_STAGE_DOWN_WGRAD      9   /* B3  dW2 = dEO^T A (fused: + SGD on W2)    */
-#define MOE_STAGE_UP_DGRAD       10   /* B4  dXp = dH W1 (+ dH3 W3)               */
-#define MOE_STAGE_UP_WGRAD       11   /* B5  dW1 (| dW3) = dH^T Xp (fused: + SGD)  */
-#define MOE_STAGE_SHARED_BWD     12   /*     shared branch dgrad and wgrad (fused: + SGD) */
-#define MOE_STAGE_BIAS_GRADS     13   /*     db1, db2 (MLP kinds)                 */
-#define MOE_STAGE_ROUTER_BWD     14   /* B7  dlogits                              */
-#define MOE_STAGE_ROUTER_DWG     15   /* B8  dWg = dl^T X                         */
-#define MOE_STAGE_ROUTER_DX      16   /* B8  router part of dX = dl Wg            */
-#define MOE_STAGE_SCATTER        17   /* B6  dX = sum of dXp rows + router part (+ shared) */
-#define MOE_STAGE_SGD            18   /* S1  masters and working copies (fused:
-                                           Wg and the biases only)                  */
+#define MOE_STAGE_ROUTER_LOGITS   0   /* l = X Wg^T                               */
+#define MOE_STAGE_ROUTE           1   /* top-k, gates, histogram, scan, slots, aux */
+#define MOE_STAGE_GATHER          2   /* Xp = X[token_of]                         */
+#define MOE_STAGE_UP_FWD          3   /* H = Xp W1^T (|W3^T), A = act(H)          */
+#define MOE_STAGE_DOWN_FWD        4   /* EO = A W2^T (+ b2)                       */
+#define MOE_STAGE_SHARED_FWD      5   /* shared branch Ys = SwiGLU(X) (n_shared > 0) */
+#define MOE_STAGE_COMBINE_LOSS    6   /* Y (+ Ys), MSE, dY, loss scalars          */
+#define MOE_STAGE_COMBINE_BWD     7   /* dgate, dEO                               */
+#define MOE_STAGE_DOWN_DGRAD      8   /* dA = dEO W2, activation backward         */
+#define MOE_STAGE_DOWN_WGRAD      9   /* dW2 = dEO^T A (fused: + SGD on W2)        */
+#define MOE_STAGE_UP_DGRAD       10   /* dXp = dH W1 (+ dH3 W3)                   */
+#define MOE_STAGE_UP_WGRAD       11   /* dW1 (| dW3) = dH^T Xp (fused: + SGD)      */
+#define MOE_STAGE_SHARED_BWD     12   /* shared branch dgrad and wgrad (fused: + SGD) */
+#define MOE_STAGE_BIAS_GRADS     13   /* db1, db2 (MLP kinds)                     */
+#define MOE_STAGE_ROUTER_BWD     14   /* dlogits                                  */
+#define MOE_STAGE_ROUTER_DWG     15   /* dWg = dl^T X                             */
+#define MOE_STAGE_ROUTER_DX      16   /* router part of dX = dl Wg                */
+#define MOE_STAGE_SCATTER        17   /* dX = sum of dXp rows + router part (+ shared) */
+#define MOE_STAGE_SGD            18   /* masters and working copies (fused: Wg and
+                                         the biases only)                          */
 #define MOE_NUM_STAGES           19
 
 /*

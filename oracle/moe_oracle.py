@@ -17,8 +17,9 @@ reader to check against the pages by eye:
              "Numerical contracts".
 
 Where the pages leave a step open, the reading taken is named in the
-docstring (R1..R12 below); every reading is also listed with its reasons in
-the design notes of the repository.
+docstring of the function that applies it (R1..R12 and R17..R20 below; the
+numbers in between concern the workloads, i.e. how inputs are drawn, the
+learning rates and the empty case, rather than a step of the layer).
 
   R1  group score = largest member logit (group-limited selection).
   R2  selection compares router logits (same order as the scores, since
