@@ -148,7 +148,7 @@ def resolve_routing(l64, gpu_idx, w, eps, e_bias=None):
 WEIGHT_NAMES = ("Wg", "W1", "b1", "W2", "b2", "W3", "Ws1", "Ws3", "Ws2")
 
 
-class GpuRun:
+class LayerRun:
     """Buffers and results of one moe_forward (+ moe_backward) on the GPU."""
 
     def __init__(self, w, inp, device=DEV):
@@ -198,7 +198,7 @@ def check_routing_tables(r_gpu, resolved, w):
 def full_parity(w, inp, dY, aux_coef, check_saved=True, label=""):
     """Forward + backward on the GPU against the whole-layer oracle."""
     t0 = time.time()
-    run = GpuRun(w, inp)
+    run = LayerRun(w, inp)
     run.forward()
     torch.cuda.synchronize()
     saved = {b: run.saved(b).cpu() for b in ("XP", "H", "A", "EO")} if check_saved else None

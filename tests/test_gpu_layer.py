@@ -12,7 +12,7 @@ import torch
 from oracle import moe_oracle as O
 from sparse_mixture_experts_gate_amd import _lib as L
 from sparse_mixture_experts_gate_amd import workloads as W
-from tests.gpu_harness import (TOL, EPS, GpuRun, assert_close, full_parity, oracle_params,
+from tests.gpu_harness import (TOL, EPS, LayerRun, assert_close, full_parity, oracle_params,
                                resolve_routing, check_routing_tables, say, shape_of, to64)
 
 pytestmark = pytest.mark.gpu
@@ -120,7 +120,7 @@ def test_empty_experts_get_zero_gradients():
 def test_no_tokens():
     w = wl("f32_no_tokens", T=0)
     inp = _inputs(w)
-    run = GpuRun(w, inp)
+    run = LayerRun(w, inp)
     run.forward()
     run.backward(torch.empty(0, w.d, device="cuda"), 0.5)
     torch.cuda.synchronize()
@@ -137,7 +137,7 @@ def test_bitwise_deterministic(w):
     dY = W.make_upstream_grad(w).cuda()
     outs = []
     for _ in range(2):
-        run = GpuRun(w, inp)
+        run = LayerRun(w, inp)
         run.forward()
         run.backward(dY, 0.2)
         torch.cuda.synchronize()
@@ -150,7 +150,7 @@ def test_bitwise_deterministic(w):
 def test_inputs_unchanged_and_calls_repeatable():
     w = BF16_CASES[0]
     inp = _inputs(w)
-    run = GpuRun(w, inp)
+    run = LayerRun(w, inp)
     before = {n: v.clone() for n, v in run.weights.items() if v is not None}
     X0 = run.X.clone()
     dY = W.make_upstream_grad(w).cuda()

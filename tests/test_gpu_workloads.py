@@ -22,7 +22,7 @@ import torch
 from oracle import moe_oracle as O
 from sparse_mixture_experts_gate_amd import _lib as L
 from sparse_mixture_experts_gate_amd import workloads as W
-from tests.gpu_harness import (EPS, TOL, GpuRun, assert_close, check_routing_tables, full_parity,
+from tests.gpu_harness import (EPS, TOL, LayerRun, assert_close, check_routing_tables, full_parity,
                                resolve_routing, say, shape_of, to64)
 from tests.test_gpu_layer import train_step_parity
 
@@ -108,7 +108,7 @@ def _sampled_parity(w, n_tokens, n_experts_checked, seed=0):
     mask = torch.zeros(w.T, dtype=torch.bool)
     mask[torch.from_numpy(S)] = True
     dY = W.make_upstream_grad(w, seed=seed, device=dev, scale=1e-3, token_mask=mask)
-    run = GpuRun(w, inp, device=dev)
+    run = LayerRun(w, inp, device=dev)
     run.forward()
     run.backward(dY, w.aux_coef)
     torch.cuda.synchronize()
