@@ -20,7 +20,7 @@ MFMA utilisation and clock per GEMM stage, from one counter run:
 
     rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 \\
         SQ_INSTS_MFMA SQ_CYCLES GRBM_GUI_ACTIVE -d OUT/mfma -o mfma --output-format csv -- \\
-        python3 bench.py --steps 1 --warmup 0 --gemm-steps 0 --api-steps 0 --no-cpu-baseline
+        python3 bench.py --steps 1 --warmup 2 --gemm-steps 0 --api-steps 0 --no-cpu-baseline
     python -m sparse_mixture_experts_gate_amd.profile_summary --mfma OUT/mfma/mfma_counter_collection.csv \\
         --markdown M --command "..."
 
@@ -263,8 +263,9 @@ PEAK_BF16_TFLOPS, PEAK_CLOCK_GHZ = 2500.0, 2.4
 
 
 def mfma_markdown(path, title, command):
-    """Per GEMM stage of the first traced step: executed MFMA flops (MOPS x 512), the
-    fraction of SIMD-cycles the MFMA pipe is busy, and the clock the chip held.
+    """Per GEMM stage of the last traced training step (run with warm-up steps, so the
+    clock is the one the chip holds in steady state): executed MFMA flops (MOPS x 512),
+    the fraction of SIMD-cycles the MFMA pipe is busy, and the clock the chip held.
 
     SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of every SIMD (it equals the number
     of 32x32x16 MFMAs times their 32 cycles); SQ_BUSY_CU_CYCLES sums the busy cycles of
@@ -276,16 +277,15 @@ def mfma_markdown(path, title, command):
         d = per.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
                                                    "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
         d[r["Counter_Name"]] = float(r["Counter_Value"])
+    # dispatches of the last traced step: from its router GEMM on
+    ids = sorted(per)
+    starts = [i for i, did in enumerate(ids) if _starts_step(per[did]["name"])]
     state = {"stage": None, "wgrad": 0}
-    rows, started = [], False
-    for did in sorted(per):
+    rows = []
+    for did in ids[starts[-1]:] if starts else []:
         d = per[did]
-        if _starts_step(d["name"]):
-            if started:
-                break
-            started = True
         st = _stage_of(d["name"], state)
-        if not started or st is None:
+        if st is None:
             continue
         state["stage"] = st
         if "gemm_bf16_kernel" not in d["name"]:
