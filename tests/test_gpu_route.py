@@ -138,3 +138,19 @@ def test_bias_changes_picks_but_not_the_gates_of_unchanged_picks():
     same = np.all(a["topk_idx"].numpy() == b["topk_idx"].numpy(), axis=1)
     assert 0 < same.sum() < 2000, "the bias should change some picks and leave others"
     assert torch.equal(a["gates"][same], b["gates"][same])
+
+
+def test_src_k_is_optional():
+    """With src_k NULL every other routing output is the same as with it."""
+    w = _workload(777, 64, 6, 8, 4, "sigmoid")
+    logits = W.make_router_logits(777, 64, "normal", seed=5)
+    full = _route(w, logits)
+    cfg = L.config(w)
+    ws = L.alloc_workspace(cfg, "cuda")
+    r = L.alloc_routing(w, "cuda")
+    r.pop("src_k")
+    L.moe_route(cfg, logits.cuda(), r, ws)
+    torch.cuda.synchronize()
+    for n, v in r.items():
+        if n != "logits":
+            assert torch.equal(v.cpu(), full[n]), n
