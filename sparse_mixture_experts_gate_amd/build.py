@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
 ARCH = "gfx950"
-SOURCES = ["moe_api.cpp", "routing.hip", "dispatch.hip", "gemm_simple.hip", "gemm_mfma.hip"]
+SOURCES = ["moe_api.cpp", "routing.hip", "dispatch.hip", "gemm_simple.hip", "gemm_mfma.hip",
+           "gemm_mfma_kt64.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -60,10 +60,21 @@
 #include "kernels.hpp"
 
 namespace moe {
+#ifdef MOE_GEMM_KT64
+namespace kt64 {
+#endif
 
+#ifdef MOE_GEMM_KT64
+// the second build of this file (gemm_mfma_kt64.hip): 64-deep k-tiles, so a K-contiguous
+// operand row of a k-tile is one whole 128-byte line, with loads staged through registers
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NS = 2;                           // LDS stages
+constexpr int DIST = 1;
+#else
 constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int NS = 4;                           // LDS stages (ring)
 constexpr int DIST = 2;                         // k-tiles loaded ahead of the one in use
+#endif
 constexpr int NTHR = 256;
 constexpr int KSTEPS = BK / 16;                 // MFMA k-steps per k-tile
 constexpr int TILE_ELEMS = 256 * BK;            // one operand tile in LDS (bf16)
@@ -190,6 +201,35 @@ __device__ __forceinline__ void dma_one(const OpPlan& o, int i, uint32_t t, int 
         dma16(r, t + j * 1024, o.vo[i & 1], (uint32_t)rowbase * o.ld_bytes + (uint32_t)k0 * 2u);
     }
 }
+
+#ifdef MOE_GEMM_KT64
+typedef unsigned int nu4r __attribute__((ext_vector_type(4)));
+// The 16 bytes a lane's dma_one would bring, loaded into registers instead.
+template <bool STRIDED, int W = 256>
+__device__ __forceinline__ nu4r load_one(const OpPlan& o, int i, int k0, int wave) {
+    if (STRIDED) {
+        constexpr int RPL = 512 / W;
+        constexpr int IPW = BK / RPL / 4;
+        const int j = wave * IPW + i;
+        rsrc_t r = o.r0;
+        int kk = k0;
+        if (k0 >= o.kswitch) { r = o.r1; kk = k0 - o.kswitch; }
+        return __builtin_bit_cast(nu4r, __builtin_amdgcn_raw_buffer_load_b128(
+            r, o.vo[i & 1], (uint32_t)(kk + RPL * j) * o.ld_bytes, 0));
+    } else {
+        const int j = wave * DIRECT_IPW + i;
+        const int row0 = DIRECT_ROWS * j;
+        int rowbase = row0;
+        rsrc_t r = o.r0;
+        if (o.paired) {
+            rowbase = ((row0 >> 6) << 5) + (row0 & 31);
+            if ((row0 >> 5) & 1) r = o.r1;
+        }
+        return __builtin_bit_cast(nu4r, __builtin_amdgcn_raw_buffer_load_b128(
+            r, o.vo[i & 1], (uint32_t)rowbase * o.ld_bytes + (uint32_t)k0 * 2u, 0));
+    }
+}
+#endif
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
@@ -487,6 +527,85 @@ gemm_bf16_kernel(GemmParams p) {
             prefetch(1, mb[1]);
         }
 
+#ifdef MOE_GEMM_KT64
+        if (nk > 0) {
+            // Loads staged through registers.  rb holds the k-tile after the next: in the
+            // slots of the first half of k-tile kt, vector q of k-tile kt+1 goes from rb[q] to
+            // its LDS stage and rb[q] is reloaded with k-tile kt+2 (the LDS write reads rb[q]
+            // when it issues), so each load has about one k-tile to arrive.  The barrier at
+            // the end of k-tile kt publishes k-tile kt+1.  The vectors of a step are spread
+            // over all its MFMA slots, so every wave layout (4, 8 or 16 slots) moves them all.
+            nu4r rb[LPW];
+            auto ldsoff = [&](int q, int kt) -> uint32_t {
+                const uint32_t st = (uint32_t)(kt % NSt) * (STAGE * 2);
+                const uint32_t o = (q < IPW_A) ? st + (uint32_t)(wave * IPW_A + q) * 1024u
+                                               : st + TILE_A * 2 + (uint32_t)(wave * IPW_B + q - IPW_A) * 1024u;
+                return o + (uint32_t)lane * 16u;
+            };
+            auto load = [&](int q, int kt) {
+                rb[q] = (q < IPW_A) ? load_one<AT, TM>(pa, q, kt * BK, wave)
+                                    : load_one<BT>(pb, q - IPW_A, kt * BK, wave);
+            };
+            auto put = [&](int q, int kt) {
+                *reinterpret_cast<nu4r*>(reinterpret_cast<char*>(lds) + ldsoff(q, kt)) = rb[q];
+            };
+#pragma unroll
+            for (int q = 0; q < LPW; ++q) load(q, 0);
+#pragma unroll
+            for (int q = 0; q < LPW; ++q) { put(q, 0); load(q, 1); }
+            __syncthreads();
+            Frags fa, fb;
+#pragma unroll
+            for (int idx = 0; idx < NR; ++idx) read_one(lds, lds + TILE_A, 0, fa, idx);
+            constexpr int HALF = KSTEPS / 2;
+            static_assert(LPW % HALF == 0, "register-staged load parts");
+            constexpr int PPS = LPW / HALF;                  // vectors moved per k-step
+            for (int kt = 0; kt < nk; ++kt) {
+                const int st = kt % NSt;
+                const bf16* As = lds + st * STAGE;
+                const bf16* Bs = lds + st * STAGE + TILE_A;
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s) {
+                    Frags& cur = (s & 1) ? fb : fa;
+                    Frags& nxt = (s & 1) ? fa : fb;
+                    if (s + 1 < KSTEPS) {
+#pragma unroll
+                        for (int i = 0; i < NMF; ++i) {
+                            mfma_one(cur, i);
+                            if (i < NR) read_one(As, Bs, s + 1, nxt, i);
+                            if (s < HALF) {
+#pragma unroll
+                                for (int q = s * PPS + i * PPS / NMF; q < s * PPS + (i + 1) * PPS / NMF; ++q) {
+                                    put(q, kt + 1);
+                                    load(q, kt + 2);
+                                }
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    } else {
+                        // last step: publish k-tile kt+1, read its first fragments under the
+                        // second half of the MFMAs
+                        constexpr int h1 = NMF / 2;
+#pragma unroll
+                        for (int i = 0; i < h1; ++i) {
+                            mfma_one(cur, i);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        __syncthreads();
+                        const int sn = (kt + 1) % NSt;
+#pragma unroll
+                        for (int i = h1; i < NMF; ++i) {
+                            mfma_one(cur, i);
+#pragma unroll
+                            for (int idx = (i - h1) * NR / (NMF - h1); idx < (i - h1 + 1) * NR / (NMF - h1); ++idx)
+                                read_one(lds + sn * STAGE, lds + sn * STAGE + TILE_A, 0, nxt, idx);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                }
+            }
+        }
+#else
         if (nk > 0) {
 #pragma unroll
             for (int t = 0; t < DIST; ++t)
@@ -544,6 +663,7 @@ gemm_bf16_kernel(GemmParams p) {
             }
             wait_vm<0>();
         }
+#endif
 
         // ---- epilogue ------------------------------------------------------------------
         if constexpr (EPI == EPI_SGD) {
@@ -935,6 +1055,7 @@ hipError_t mfma_up_fwd(const ExpertGemmArgs& a, hipStream_t s) {
     return run<MODE_ROWS, false, false, EPI_UP_GELU, false>(p, p.mtiles_ub * NT, s);
 }
 
+#ifndef MOE_GEMM_KT64     // the second build holds the up projection only
 hipError_t mfma_down_fwd(const ExpertGemmArgs& a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
     GemmParams p = base_rows(a);
@@ -1115,4 +1236,8 @@ hipError_t mfma_router_dwg(const RouterGemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+#endif  // MOE_GEMM_KT64
+#ifdef MOE_GEMM_KT64
+}  // namespace kt64
+#endif
 }  // namespace moe

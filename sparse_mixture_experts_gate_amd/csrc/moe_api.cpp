@@ -290,7 +290,7 @@ int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_
     TRY(launch_gather(ga, c->dtype, x.s));
     ExpertGemmArgs ea = expert_args(x, w, r);
     TRY(x.mark(MOE_STAGE_UP_FWD));
-    TRY(f32 ? simple_up_fwd(ea, x.s) : mfma_up_fwd(ea, x.s));
+    TRY(f32 ? simple_up_fwd(ea, x.s) : kt64::mfma_up_fwd(ea, x.s));
     TRY(x.mark(MOE_STAGE_DOWN_FWD));
     TRY(f32 ? simple_down_fwd(ea, x.s) : mfma_down_fwd(ea, x.s));
     TRY(x.mark(MOE_STAGE_SHARED_FWD));
@@ -298,7 +298,7 @@ int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_
     if (shared) {
         TRY(launch_shared_table(x.buf<int32_t>(B_STAB), c->T, x.s));
         ExpertGemmArgs sa = shared_args(x, X, w);
-        TRY(f32 ? simple_up_fwd(sa, x.s) : mfma_up_fwd(sa, x.s));
+        TRY(f32 ? simple_up_fwd(sa, x.s) : kt64::mfma_up_fwd(sa, x.s));
         TRY(f32 ? simple_down_fwd(sa, x.s) : mfma_down_fwd(sa, x.s));
     }
     TRY(x.mark(MOE_STAGE_COMBINE_LOSS));
