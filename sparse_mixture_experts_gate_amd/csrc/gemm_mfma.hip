@@ -21,7 +21,9 @@
 //   * every operand goes straight from global memory into LDS (buffer loads
 //     with an LDS destination, bounds checked by the buffer descriptor so
 //     ragged rows and k tails read as zero) through a ring of 4 LDS stages,
-//     k-tiles loaded 2 ahead of the one in use; K-contiguous operands are kept
+//     k-tiles loaded 2 ahead of the one in use; the second build of this file
+//     (gemm_mfma_kt64.hip, used for the up projection) takes 64-deep k-tiles
+//     in 2 LDS stages instead, with the k-tile after next held in registers; K-contiguous operands are kept
 //     as [rows][32] (64-byte rows of four 16-byte chunks, chunk XOR-swizzled by
 //     (row >> 2) & 3: the LDS has 64 four-byte banks and the 16 lanes served
 //     together by a ds_read_b128 read 16 consecutive rows, which then hit 16
