@@ -111,8 +111,8 @@ def _stage_of(name, state):
         return "route" if state["stage"] in ("route",) else "combine_loss"
     if "gather_kernel" in name:
         return "gather"
-    if "gemm_bf16_kernel<0, false, false, 0" in name:
-        return "down_fwd"
+    if "gemm_bf16_kernel<0, false, false, 0" in name or "gemm_bf16_kernel<0, false, false, 8" in name:
+        return "down_fwd"          # plain store (SwiGLU) or store + bias (MLP)
     if "gemm_bf16_kernel<0, false, false" in name:
         return "up_fwd"
     if "combine_kernel" in name:

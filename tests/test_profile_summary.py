@@ -39,6 +39,29 @@ def test_stage_of_one_step():
         state["stage"] = st
 
 
+def test_stage_of_mlp_step():
+    """The bias + activation MLP: its down projection stores with a bias (epilogue 8), its
+    bias gradients are column sums."""
+    K = "void moe::kt64::gemm_bf16_kernel<{}>(moe::kt64::GemmParams)"
+    step = [(G.format("2, false, false, 0, true, 256"), "router_logits"),
+            ("moe::route_topk_kernel(moe::RouteArgs)", "route"),
+            ("_ZN3moe13gather_kernelIDF16bLi8EEEvNS_10GatherArgsE", "gather"),
+            (K.format("0, false, false, 3, false, 256"), "up_fwd"),
+            (G.format("0, false, false, 8, false, 256"), "down_fwd"),
+            ("_ZN3moe14combine_kernelIDF16bLb1ELi8EEEvNS_11CombineArgsE", "combine_loss"),
+            ("_ZN3moe18combine_bwd_kernelIDF16bLi8EEEvNS_14CombineBwdArgsE", "combine_bwd"),
+            (G.format("0, false, true, 6, false, 256"), "down_dgrad"),
+            (G.format("1, true, true, 7, true, 256"), "down_wgrad"),
+            (G.format("0, false, true, 0, false, 256"), "up_dgrad"),
+            (G.format("1, true, true, 7, true, 128"), "up_wgrad"),
+            ("_ZN3moe13colsum_kernelIDF16bEEvNS_10ColSumArgsE", "bias_grads")]
+    state = {"stage": None, "wgrad": 0}
+    for name, want in step:
+        st = S._stage_of(name, state)
+        assert st == want, (name, st, want)
+        state["stage"] = st
+
+
 def test_stage_durations_count_steps_at_the_router_gemm(tmp_path):
     path = tmp_path / "trace.csv"
     with open(path, "w", newline="") as f:
