@@ -527,3 +527,82 @@ def train_step(X, Yt, P, shp: Shape, lr, aux_coef, topk_idx=None):
     for n in PARAM_NAMES:
         newP[n] = None if P.get(n) is None else sgd(P[n], grads["d" + n], lr)
     return {"fw": fw, "grads": grads, "mse": m, "loss": loss, "params": newP, "dY": dY}
+
+
+def train_step_streamed(X, Yt, Wg, get_expert, shp: Shape, lr, aux_coef, topk_idx=None,
+                        e_bias=None, keep=(), dY=None, progress=None):
+    """train_step for a layer whose expert weights do not fit in memory at once.
+
+    The steps and their order are those of train_step (route, experts, combine,
+    MSE + aux_coef * aux, backward, SGD), with two differences of bookkeeping
+    only: the expert weights are fetched one expert at a time, by
+    get_expert(e) -> {"W1", "W2", "W3" (SwiGLU), "b1", "b2" (MLP)} in float64,
+    once for the forward and once for the backward; and the combine backward
+    is taken per expert segment (dg_ti = <dY_t, EO[slot]> and
+    dEO[slot] = g_ti dY_t for the rows of that segment), so that dEO never
+    exists as a whole.  dX is summed in pick order as in scatter_rows.
+    With dY given, the backward starts from it instead of the MSE gradient
+    (the loss is still reported).  Returns the loss parts, Y, dY, dX, dWg, the
+    routing, and for each expert in `keep` its gradients and updated weights;
+    the router weight's update is Wg - lr * dWg.  progress, if given, is called
+    with a short text after every 32 experts of each pass.
+    """
+    fw = route(X, Wg, shp, topk_idx, e_bias)
+    r = fw["routing"]
+    T, d = X.shape
+    k, E = shp.k, shp.E
+    gates = fw["gates"]
+    gate_row = gates.reshape(-1)[r.token_of * k + r.src_k]      # g of each expert-major row
+    EO = np.zeros((T * k, d))
+    saved = {}
+    for e in range(E):
+        lo, hi = r.offsets[e], r.offsets[e + 1]
+        if hi == lo:
+            continue
+        p = get_expert(e)
+        s = expert_forward(shp.expert, gather_rows(X, r.token_of[lo:hi]), p["W1"], p.get("b1"),
+                           p["W2"], p.get("b2"), p.get("W3"))
+        EO[lo:hi] = s.pop("EO")
+        saved[e] = s
+        if progress and (e + 1) % 32 == 0:
+            progress(f"oracle forward: {e + 1} of {E} experts")
+    Y = combine(EO, r.slot_of, gates)
+    aux, f, Pm = aux_loss(r.counts, fw["q"], k)
+    m, dY_mse = mse(Y, Yt)
+    if dY is None:
+        dY = dY_mse
+    dgate = np.zeros((T, k))
+    dXp = np.zeros((T * k, d))
+    out = {"experts": {}}
+    for e in range(E):
+        lo, hi = r.offsets[e], r.offsets[e + 1]
+        if hi == lo and e not in keep:
+            continue
+        p = get_expert(e)
+        tok = r.token_of[lo:hi]
+        EOe = EO[lo:hi]
+        dgate[tok, r.src_k[lo:hi]] = (dY[tok] * EOe).sum(axis=1)
+        dEO = gate_row[lo:hi, None] * dY[tok]
+        if hi == lo:
+            s = {"A": np.zeros((0, p["W2"].shape[1])), "H": np.zeros((0, p["W1"].shape[0])),
+                 "H1": np.zeros((0, p["W1"].shape[0])), "H3": np.zeros((0, p["W1"].shape[0]))}
+        else:
+            s = saved.pop(e)
+        g = expert_backward(shp.expert, gather_rows(X, tok), p["W1"], p["W2"], p.get("W3"), s, dEO)
+        dXp[lo:hi] = g["dXp"]
+        if e in keep:
+            ge = {n: g[n] for n in ("dW1", "dW2", "dW3", "db1", "db2") if n in g}
+            new = {n[1:]: sgd(p[n[1:]], ge[n], lr) for n in ge}
+            out["experts"][e] = {"grads": ge, "params": new}
+        if progress and (e + 1) % 32 == 0:
+            progress(f"oracle backward: {e + 1} of {E} experts")
+    del EO, saved
+    dX = scatter_rows(dXp, r.slot_of)
+    del dXp
+    dw = renorm_backward(dgate, gates, fw["w"], shp.route_scale)
+    dq = aux_grad_q(r.counts, T, k, E, aux_coef)
+    dl = router_backward(fw["logits"], r.topk_idx, dw, dq, shp.score)
+    out.update({"mse": m, "aux": aux, "loss": m + aux_coef * aux, "Y": Y, "dY": dY,
+                "dX": dX + dl @ Wg, "dWg": dl.T @ X, "dgate": dgate, "dlogits": dl,
+                "logits": fw["logits"], "gates": gates, "routing": r})
+    return out

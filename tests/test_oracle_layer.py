@@ -310,3 +310,50 @@ def test_expert_relabel_metamorphic():
     b = O.layer_forward(X, Q, shp)
     assert np.allclose(a["Y"], b["Y"], rtol=1e-12, atol=1e-14)
     assert np.array_equal(perm[b["topk_idx"]], a["topk_idx"])
+
+
+@pytest.mark.parametrize("expert,score,G,TG", [("swiglu", "sigmoid", 4, 2), ("relu", "softmax", 1, 1),
+                                               ("gelu", "softmax", 2, 1)])
+def test_streamed_step_equals_train_step(expert, score, G, TG):
+    """The per-expert streamed step (used where the expert weights do not fit in host
+    memory at once) gives train_step's loss, Y, dX, dWg and expert updates, with an
+    expert left empty so that its zero gradients come out of the empty segment."""
+    rng = np.random.default_rng(11)
+    T, d, E, ffn, k = 40, 12, 8, 10, 2
+    P = _rand_params(rng, E, d, ffn, expert)
+    X = np.abs(rng.normal(size=(T, d)))
+    P["Wg"][E - 1] = -10.0 * np.abs(P["Wg"][E - 1])   # far below every other logit: never picked
+    Yt = rng.normal(size=(T, d))
+    shp = O.Shape(E=E, k=k, n_groups=G, topk_groups=TG, score=score, expert=expert)
+    ref = O.train_step(X, Yt, P, shp, lr=0.05, aux_coef=0.01)
+    assert ref["fw"]["routing"].counts[E - 1] == 0
+
+    def get(e):
+        return {n: P[n][e] for n in ("W1", "W2", "W3", "b1", "b2") if P[n] is not None}
+
+    keep = (0, 3, E - 1)
+    st = O.train_step_streamed(X, Yt, P["Wg"], get, shp, lr=0.05, aux_coef=0.01, keep=keep)
+    tol = dict(rtol=1e-12, atol=1e-14)
+    assert np.array_equal(st["routing"].topk_idx, ref["fw"]["topk_idx"])
+    for a, b in ((st["mse"], ref["mse"]), (st["aux"], ref["fw"]["aux"]), (st["loss"], ref["loss"])):
+        assert abs(a - b) <= 1e-13 * max(1.0, abs(b))
+    assert np.allclose(st["Y"], ref["fw"]["Y"], **tol)
+    assert np.allclose(st["dY"], ref["dY"], **tol)
+    assert np.allclose(st["dgate"], ref["grads"]["dgate"], **tol)
+    assert np.allclose(st["dX"], ref["grads"]["dX"], **tol)
+    assert np.allclose(st["dWg"], ref["grads"]["dWg"], **tol)
+    for e in keep:
+        for n, g in st["experts"][e]["grads"].items():
+            assert np.allclose(g, ref["grads"][n][e], **tol), (e, n)
+        for n, v in st["experts"][e]["params"].items():
+            assert np.allclose(v, ref["params"][n][e], **tol), (e, n)
+    assert all(np.all(g == 0) for g in st["experts"][E - 1]["grads"].values())
+    # a caller-supplied dY replaces the MSE gradient in the backward
+    dY = rng.normal(size=(T, d))
+    sd = O.train_step_streamed(X, Yt, P["Wg"], get, shp, lr=0.05, aux_coef=0.01, keep=keep, dY=dY)
+    gr = O.layer_backward(X, P, shp, ref["fw"], dY, 0.01)
+    assert np.allclose(sd["dX"], gr["dX"], **tol)
+    assert np.allclose(sd["dWg"], gr["dWg"], **tol)
+    for e in keep:
+        for n, g in sd["experts"][e]["grads"].items():
+            assert np.allclose(g, gr[n][e], **tol), (e, n)
