@@ -8,8 +8,8 @@ Prints one JSON line.  `value` is tokens per second of the whole training
 step.  Per-stage times come from HIP events recorded by the library between
 its launches on the bench stream (moe_train_step_profiled) inside the timed
 region; `roofline` is the dominant stage's algorithmic work over its average
-duration.  `cpu_baseline` times the float64 oracle on the host on a bounded
-sample of the same workload.
+duration.  `cpu_baseline` times the float64 oracle on the host: one whole
+forward + loss + backward of the same workload, streamed one expert at a time.
 """
 from __future__ import annotations
 
@@ -163,13 +163,17 @@ def measured_traffic(stage: str, workload: str, sgd: str):
     return ent["hbm_bytes"]
 
 
-def cpu_baseline(w, inp, budget_s: float):
-    """The oracle, as it stands, on a bounded sample of the workload (host cores).
+def cpu_baseline(w, inp, max_experts: int = 0):
+    """The oracle, as it stands, on the host cores: one whole forward + loss + backward.
 
-    Sample: routing of every token (logits, group-limited top-k, gates, dispatch
-    tables, aux), then the expert forward and backward of whole expert segments
-    (experts 0, 1, 2, ...) until the time budget is used; the expert part is
-    scaled to all T*k rows by row count.
+    The float64 oracle's streamed step: router logits, group-limited top-k,
+    gates, dispatch tables and aux for every token; gather, expert forward,
+    combine, MSE and aux; combine backward, expert backward, scatter, router
+    backward and router GEMMs, with the expert weights fetched one expert at a
+    time.  Not timed: copying the inputs to the host and decoding each expert's
+    bf16 weights to float64.  max_experts > 0 bounds the run to that many
+    experts' rows (for quick runs; the result is then scaled by row count and
+    labelled extrapolated).
     """
     import numpy as np
     import torch
@@ -178,49 +182,53 @@ def cpu_baseline(w, inp, budget_s: float):
     from oracle import moe_oracle as O
 
     X64 = inp["X"].double().cpu().numpy()
+    Yt64 = inp["Yt"].double().cpu().numpy()
     Wg64 = inp["Wg_w"].double().cpu().numpy()
+    names = [n for n in ("W1", "W2", "W3", "b1", "b2") if inp.get(n + "_w") is not None]
+    host = {n: inp[n + "_w"].cpu() for n in names}
     shp = O.Shape(E=w.E, k=w.k, n_groups=w.n_groups, topk_groups=w.topk_groups, score=w.score,
                   expert=w.expert)
+    t_fetch = [0.0]
+    buf = {n: torch.empty(host[n].shape[1:], dtype=torch.float64) for n in names}
+
+    def get(e):
+        # decoded into the same float64 buffers each call: the streamed step is done
+        # with one expert's weights before it asks for the next
+        t = time.perf_counter()
+        out = {n: buf[n].copy_(host[n][e]).numpy() for n in names}
+        t_fetch[0] += time.perf_counter() - t
+        return out
+
+    topk = None
+    rows_run = w.T * w.k
+    if max_experts > 0:
+        # route once untimed, then keep only the tokens whose picks all fall in the first
+        # max_experts experts' segments: the timed run is the oracle on that sub-batch
+        fw = O.route(X64, Wg64, shp)
+        sel = np.all(fw["topk_idx"] < max_experts, axis=1)
+        X64, Yt64 = X64[sel], Yt64[sel]
+        rows_run = int(sel.sum()) * w.k
     t0 = time.perf_counter()
-    fw = O.route(X64, Wg64, shp)
-    aux, _, _ = O.aux_loss(fw["routing"].counts, fw["q"], w.k)
-    t_route = time.perf_counter() - t0
-    r = fw["routing"]
-    rng = np.random.default_rng(0)
-    t_exp = 0.0
-    rows = 0
-    n_exp = 0
-    for e in range(w.E):
-        lo, hi = int(r.offsets[e]), int(r.offsets[e + 1])
-        if hi == lo:
-            continue
-        W1 = inp["W1_w"][e].double().cpu().numpy()
-        W2 = inp["W2_w"][e].double().cpu().numpy()
-        W3 = inp["W3_w"][e].double().cpu().numpy() if inp.get("W3_w") is not None else None
-        b1 = inp["b1_w"][e].double().cpu().numpy() if inp.get("b1_w") is not None else None
-        b2 = inp["b2_w"][e].double().cpu().numpy() if inp.get("b2_w") is not None else None
-        dEO = rng.standard_normal((hi - lo, w.d))
-        t1 = time.perf_counter()
-        Xp = O.gather_rows(X64, r.token_of[lo:hi])
-        s = O.expert_forward(w.expert, Xp, W1, b1, W2, b2, W3)
-        O.expert_backward(w.expert, Xp, W1, W2, W3, s, dEO)
-        t_exp += time.perf_counter() - t1
-        rows += hi - lo
-        n_exp += 1
-        if t_route + t_exp >= budget_s:
-            break
-    full = t_route + t_exp * (w.T * w.k / max(rows, 1))
+    O.train_step_streamed(X64, Yt64, Wg64, get, shp, w.lr, w.aux_coef, topk_idx=topk,
+                          progress=lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True))
+    t_all = time.perf_counter() - t0 - t_fetch[0]
+    full = t_all * (w.T * w.k) / max(rows_run, 1)
     pools = threadpool_info()
     threads = max([i.get("num_threads", 1) for i in pools] or [1])
     blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
             for i in pools if i.get("user_api") == "blas"]
+    what = ("float64 oracle, one whole step of forward + MSE + aux + backward (routing, gather, "
+            "experts, combine, loss, combine backward, scatter, router backward, router GEMMs; "
+            "no SGD) streamed one expert at a time")
+    if rows_run == w.T * w.k:
+        sample = f"{what}: all {w.T} tokens and {w.E} experts, {t_all:.1f} s (weight decoding excluded)"
+    else:
+        sample = (f"{what}: the {rows_run // w.k} tokens routed only to experts < {max_experts} "
+                  f"({t_all:.1f} s), scaled by row count to all {w.T * w.k} rows: {full:.0f} s, "
+                  f"extrapolated")
     return {"value": w.T / full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "blas": ", ".join(blas) or None, "host_cpus": os.cpu_count(),
-            "sample": (f"float64 oracle: routing of all {w.T} tokens ({t_route:.1f} s) + expert "
-                       f"forward/backward of {n_exp} whole expert segments ({rows} of {w.T * w.k} "
-                       f"rows, {t_exp:.1f} s), expert part extrapolated to all rows by row count: "
-                       f"{full:.0f} s per step, extrapolated"),
-            "seconds_measured": round(t_route + t_exp, 2)}
+            "blas": ", ".join(blas) or None, "host_cpus": os.cpu_count(), "sample": sample,
+            "seconds_measured": round(t_all, 2), "seconds_weight_decoding": round(t_fetch[0], 2)}
 
 
 def main(argv=None) -> int:
@@ -229,7 +237,9 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="grouped_sigmoid_t32768_d7168_e256")
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-experts", type=int, default=0,
+                    help="time the oracle on the tokens routed to the first N experts only and "
+                         "scale by row count (0: the whole step, about a minute on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sgd", choices=("fused", "stored"), default="fused",
                     help="fused: the expert weight-gradient GEMMs apply the SGD step themselves "
@@ -458,7 +468,7 @@ def main(argv=None) -> int:
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_experts)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

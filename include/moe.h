@@ -94,7 +94,8 @@ extern "C" {
  * multiples of 4; bfloat16: d and ffn multiples of 64, E a multiple of 8, and
  * T * max(d, hcols, 2 Hs) * 2 < 2^31 (hcols = 2 ffn for SwiGLU, else ffn): an
  * expert's rows of a k-strided GEMM operand, up to T of them, must span less
- * than 2 GiB.
+ * than 2 GiB; and max(ffn, Hs) * d * 4 < 2^31: one expert's (or the shared
+ * branch's) weight matrix, as float32 masters, must span less than 2 GiB.
  */
 typedef struct moe_config {
     int32_t T;            /* tokens */

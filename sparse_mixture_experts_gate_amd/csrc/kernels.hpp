@@ -35,7 +35,7 @@ struct SlotArgs {
     int32_t* tile_prefix;  // [3][MOE_MAX_EXPERTS+1]: m-tile prefix for 64/128/256-row tiles
     int32_t* slot_of;      // [T,k]
     int32_t* token_of;     // [T*k]
-    float* gate_of;        // [T*k]
+    float* gate_of;        // [T*k] gate of each expert-major row, or NULL
     int32_t* src_k;        // [T*k] pick index of each row, or NULL
     int T, E, k, nchunk;
 };

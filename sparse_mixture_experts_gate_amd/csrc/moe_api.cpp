@@ -85,6 +85,10 @@ int supported(const moe_config* c) {
                                                   c->expert == MOE_EXPERT_SWIGLU ? 2 * (int64_t)c->ffn : c->ffn,
                                                   2 * (int64_t)c->n_shared * c->ffn});
         if ((int64_t)c->T * widest * 2 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+        // One expert's weight block (and the shared branch's) is addressed through one
+        // descriptor too, as fp32 masters in the fused SGD step: ffn x d (Hs x d) floats.
+        const int64_t wrows = std::max<int64_t>(c->ffn, (int64_t)c->n_shared * c->ffn);
+        if (wrows * c->d * 4 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
     }
     return MOE_OK;
 }
@@ -221,23 +225,35 @@ struct Ctx {
         if (_e != hipSuccess) return MOE_ERR_HIP; \
     } while (0)
 
-// Routing from logits: top-k, gates, histogram, scan, slots, aux.
-int run_routing(const Ctx& x, const float* logits, const float* e_bias, moe_routing* r) {
-    const moe_config* c = x.c;
-    RouteArgs ra = {logits, r->topk_idx, r->gates, x.buf<int32_t>(B_HIST), x.buf<float>(B_QPART),
+// Scratch of the routing kernels: per-chunk histograms, their scan bases, per-chunk aux
+// partial sums, the GEMM tile prefixes, and (optionally) the gate of each expert-major row.
+struct RouteScratch {
+    int32_t* hist; int32_t* cbase; float* qpart; int32_t* tprefix; float* gate_of;
+};
+
+// Routing from logits: top-k, gates, histogram, scan, slots, aux.  Every scratch entry
+// the kernels read was written earlier in the same sequence, so nothing needs clearing.
+int run_routing(const moe_config* c, hipStream_t s, const RouteScratch& sc, const float* logits,
+                const float* e_bias, moe_routing* r) {
+    RouteArgs ra = {logits, r->topk_idx, r->gates, sc.hist, sc.qpart,
                     c->T, c->E, c->k, c->n_groups, c->topk_groups, c->score, nchunk(c),
                     e_bias, c->group_score, route_scale(c)};
-    TRY(launch_route_topk(ra, x.s));
-    ScanArgs sa = {x.buf<int32_t>(B_HIST), x.buf<int32_t>(B_CBASE), r->counts, nchunk(c)};
-    TRY(launch_expert_scan(sa, c->E, x.s));
-    SlotArgs sl = {r->counts, x.buf<int32_t>(B_CBASE), r->topk_idx, r->gates, r->offsets,
-                   x.buf<int32_t>(B_TPREFIX), r->slot_of, r->token_of, x.buf<float>(B_GATEOF),
-                   r->src_k, c->T, c->E, c->k, nchunk(c)};
-    TRY(launch_slot_assign(sl, x.s));
-    FinalizeArgs fa = {x.buf<float>(B_QPART), r->counts, nullptr, 0, r->aux, nullptr, 0.f,
+    TRY(launch_route_topk(ra, s));
+    ScanArgs sa = {sc.hist, sc.cbase, r->counts, nchunk(c)};
+    TRY(launch_expert_scan(sa, c->E, s));
+    SlotArgs sl = {r->counts, sc.cbase, r->topk_idx, r->gates, r->offsets, sc.tprefix,
+                   r->slot_of, r->token_of, sc.gate_of, r->src_k, c->T, c->E, c->k, nchunk(c)};
+    TRY(launch_slot_assign(sl, s));
+    FinalizeArgs fa = {sc.qpart, r->counts, nullptr, 0, r->aux, nullptr, 0.f,
                        c->T, c->d, c->E, c->k, nchunk(c)};
-    TRY(launch_finalize(fa, x.s));
+    TRY(launch_finalize(fa, s));
     return MOE_OK;
+}
+
+int run_routing(const Ctx& x, const float* logits, const float* e_bias, moe_routing* r) {
+    RouteScratch sc = {x.buf<int32_t>(B_HIST), x.buf<int32_t>(B_CBASE), x.buf<float>(B_QPART),
+                       x.buf<int32_t>(B_TPREFIX), x.buf<float>(B_GATEOF)};
+    return run_routing(x.c, x.s, sc, logits, e_bias, r);
 }
 
 ExpertGemmArgs expert_args(const Ctx& x, const moe_weights* w, const moe_routing* r) {

@@ -132,6 +132,51 @@ __device__ __forceinline__ void score_token(const float (&l)[EPL], int E, int sc
     }
 }
 
+// Wave-wide float64 sum: the same DPP row moves on the two 32-bit halves, then the four row
+// results in a fixed order.
+template <int C> __device__ __forceinline__ double dpp_d(double v) {
+    const long long b = __builtin_bit_cast(long long, v);
+    const int lo = dpp_i<C>((int)(b & 0xffffffffll)), hi = dpp_i<C>((int)(b >> 32));
+    return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ double lane_d(double v, int l) {
+    const long long b = __builtin_bit_cast(long long, v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), l);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ double wv_sum_d(double v) {
+    v += dpp_d<DPP_QXOR1>(v);
+    v += dpp_d<DPP_QXOR2>(v);
+    v += dpp_d<DPP_HALF_MIRROR>(v);
+    v += dpp_d<DPP_MIRROR>(v);
+    return (lane_d(v, 0) + lane_d(v, 16)) + (lane_d(v, 32) + lane_d(v, 48));
+}
+
+// Selection scores of the router variants: each score evaluated in float64 and rounded
+// once to fp32, so that it is the fp32 rounding of the score up to the last bit of the
+// float64 exponential (the "Numerical contracts" gate ranks scores plus the bias).  The
+// fp32 max of the logits is exact, and so is the float64 difference l - max.
+__device__ __forceinline__ void selection_scores(const float (&l)[EPL], int E, int score, float mx,
+                                                 float (&v)[EPL]) {
+    const int lane = threadIdx.x & 63;
+    if (score == MOE_SCORE_SOFTMAX) {
+        double z[EPL], zs = 0.0;
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) {
+            const int e = lane + 64 * m;
+            z[m] = (e < E) ? exp((double)l[m] - (double)mx) : 0.0;
+            zs += z[m];
+        }
+        zs = wv_sum_d(zs);
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) v[m] = (float)(z[m] / zs);
+    } else {
+#pragma unroll
+        for (int m = 0; m < EPL; ++m) v[m] = (float)(1.0 / (1.0 + exp(-(double)l[m])));
+    }
+}
+
 // Score of expert e (owned by some lane) without a shuffle: recompute from its logit.
 __device__ __forceinline__ float selected_score(float l, const TokenScores& ts, int score) {
     if (score == MOE_SCORE_SOFTMAX) return expf(l - ts.mx) / ts.z;
@@ -176,11 +221,12 @@ route_topk_kernel(RouteArgs a) {
         // selection values
         const bool on_scores = a.bias != nullptr || a.group_score == MOE_GROUP_TOP2_SUM;
         float v[EPL];
+        if (on_scores) selection_scores(ts.l, E, a.score, ts.mx, v);   // wave-uniform
 #pragma unroll
         for (int m = 0; m < EPL; ++m) {
             int e = lane + 64 * m;
             if (!on_scores) v[m] = ts.l[m];
-            else v[m] = (e < E) ? ts.s[m] + (a.bias ? a.bias[e] : 0.f) : -INFINITY;
+            else v[m] = (e < E) ? v[m] + (a.bias ? a.bias[e] : 0.f) : -INFINITY;
             if (e < E) { s_l[wave][e] = ts.l[m]; s_v[wave][e] = v[m]; }
         }
         __builtin_amdgcn_wave_barrier();
@@ -386,7 +432,7 @@ slot_assign_kernel(SlotArgs a) {
             const int slot = s_off[e] + base[i] + __popcll(s_mask[e] & below);
             a.slot_of[(size_t)t * k + i] = slot;
             a.token_of[slot] = t;
-            a.gate_of[slot] = gt[i];
+            if (a.gate_of) a.gate_of[slot] = gt[i];
             if (a.src_k) a.src_k[slot] = i;
         }
     }

@@ -156,6 +156,16 @@ def test_bf16_shape_rules(lib):
     assert _call_forward(L.config(w.replace(T=(1 << 31) // (2 * widest) + 1))) == -5
     wg = w.replace(expert="swiglu", ffn=2048)                    # hcols 4096 > d
     assert _call_forward(L.config(wg.replace(T=(1 << 30) // 4096 + 1))) == -5
+    # one expert's weight matrix as float32 masters must span less than 2 GiB: ffn * d * 4
+    # (a shape that passes this rule is shown by the next check in line, the workspace
+    # size: nothing is launched)
+    wide = w.replace(T=64, d=16384, ffn=32768)               # 2^29 floats: exactly 2 GiB
+    assert _call_forward(L.config(wide), ws_bytes=1) == -5
+    assert _call_forward(L.config(wide.replace(ffn=32768 - 64)), ws_bytes=1) == -4
+    # the shared branch's Hs x d block counts too (Hs = n_shared * ffn)
+    sh = w.replace(T=64, d=8192, ffn=4096, expert="swiglu")
+    assert _call_forward(L.config(sh.replace(n_shared=15)), ws_bytes=1) == -4
+    assert _call_forward(L.config(sh.replace(n_shared=16)), ws_bytes=1) == -5
 
 
 def test_pointer_and_workspace_errors(lib):
@@ -209,3 +219,4 @@ def test_one_hip_runtime_per_process(lib):
     maps = open("/proc/self/maps").read()
     hips = sorted(set(re.findall(r"\S*libamdhip64\S*", maps)))
     assert len(hips) == 1, hips
+

@@ -12,8 +12,8 @@ import torch
 from oracle import moe_oracle as O
 from sparse_mixture_experts_gate_amd import _lib as L
 from sparse_mixture_experts_gate_amd import workloads as W
-from tests.gpu_harness import (TOL, EPS, LayerRun, assert_close, full_parity, oracle_params,
-                               resolve_routing, check_routing_tables, say, shape_of, to64)
+from tests.gpu_harness import (TOL, LayerRun, assert_close, check_routing, full_parity, oracle_params,
+                               say, shape_of, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -199,8 +199,7 @@ def train_step_parity(w, inp, label, fused=False):
     X64 = to64(inp["X"])
     P = oracle_params(inp)
     l64 = X64 @ P["Wg"].T
-    resolved, n_amb = resolve_routing(l64, r["topk_idx"].cpu().numpy(), w, EPS[w.dtype], P["e_bias"])
-    check_routing_tables(r, resolved, w)
+    resolved, _, _ = check_routing(r, l64, w, P["e_bias"], label)
     st = O.train_step(X64, to64(inp["Yt"]), P, shape_of(w), w.lr, w.aux_coef, topk_idx=resolved)
     say(f"[{label}] loss gpu {loss.tolist()} oracle {[st['mse'], st['fw']['aux'], st['loss']]}")
     assert_close("loss", to64(loss), [st["mse"], st["fw"]["aux"], st["loss"]], rtol, atol)
