@@ -62,6 +62,8 @@ extern "C" {
 #define MOE_ERR_WORKSPACE     -4  /* workspace NULL or smaller than moe_workspace_bytes() */
 #define MOE_ERR_UNSUPPORTED   -5  /* valid layer, but outside what the kernels support */
 #define MOE_ERR_HIP           -6  /* a HIP launch failed */
+#define MOE_ERR_SCRATCH       -7  /* moe_route_noalloc: the shape needs more scratch than
+                                     MOE_ROUTE_SCRATCH_BYTES */
 
 /* ---- enums ------------------------------------------------------------- */
 #define MOE_SCORE_SOFTMAX   0
@@ -233,6 +235,26 @@ int64_t moe_workspace_offset(const moe_config* cfg, int32_t which);
  */
 int moe_route(const moe_config* cfg, const float* logits, const float* e_bias,
               moe_routing* r, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and outputs as moe_route, minus the workspace:
+ * the kernels' scratch (per-64-token-chunk histograms, scan bases and aux
+ * partial sums, and the GEMM tile prefixes) lives in one static device array
+ * of MOE_ROUTE_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends.  Nothing is allocated or freed, and no scratch entry needs
+ * clearing (each is written before it is read within the call).
+ * Limit: 3 * align256(E * ceil(T / 64) * 4) + align256(3 * 257 * 4) bytes must
+ * fit in MOE_ROUTE_SCRATCH_BYTES (T up to 174,656 tokens at E = 256), else
+ * MOE_ERR_SCRATCH before any launch.  Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (other streams or host threads) race
+ * and must be serialised by the caller.  The first call on a device resolves
+ * the array's address there (MOE_ERR_HIP if that fails).
+ */
+#define MOE_ROUTE_SCRATCH_BYTES  (8u << 20)
+int moe_route_noalloc(const moe_config* cfg, const float* logits, const float* e_bias,
+                      moe_routing* r, void* stream);
 
 /*
  * Forward of the layer: router GEMM, routing, gather, expert up and down

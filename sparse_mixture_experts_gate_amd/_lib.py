@@ -22,9 +22,9 @@ GROUP = {"max": 0, "top2": 1}
 WS = {"XP": 0, "H": 1, "A": 2, "EO": 3}
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_NULL_PTR", -3: "MOE_ERR_MISALIGNED",
-          -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_UNSUPPORTED", -6: "MOE_ERR_HIP"}
+          -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_UNSUPPORTED", -6: "MOE_ERR_HIP", -7: "MOE_ERR_SCRATCH"}
 
-EXPORTS = ["moe_workspace_bytes", "moe_workspace_offset", "moe_route", "moe_forward",
+EXPORTS = ["moe_workspace_bytes", "moe_workspace_offset", "moe_route", "moe_route_noalloc", "moe_forward",
            "moe_backward", "moe_train_step", "moe_train_step_profiled", "moe_status_string",
            "moe_abi_version"]
 
@@ -89,6 +89,8 @@ def load() -> ctypes.CDLL:
         lib.moe_workspace_offset.restype = ctypes.c_int64
         lib.moe_route.argtypes = [P(moe_config), ctypes.c_void_p, ctypes.c_void_p, P(moe_routing),
                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        lib.moe_route_noalloc.argtypes = [P(moe_config), ctypes.c_void_p, ctypes.c_void_p, P(moe_routing),
+                                          ctypes.c_void_p]
         lib.moe_forward.argtypes = [P(moe_config), ctypes.c_void_p, P(moe_weights), ctypes.c_void_p,
                                     P(moe_routing), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         lib.moe_backward.argtypes = [P(moe_config), ctypes.c_void_p, P(moe_weights), P(moe_routing),
@@ -99,7 +101,7 @@ def load() -> ctypes.CDLL:
                                        P(moe_grads), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p]
         lib.moe_train_step_profiled.argtypes = lib.moe_train_step.argtypes + [ctypes.c_void_p]
-        for f in ("moe_route", "moe_forward", "moe_backward", "moe_train_step",
+        for f in ("moe_route", "moe_route_noalloc", "moe_forward", "moe_backward", "moe_train_step",
                   "moe_train_step_profiled"):
             getattr(lib, f).restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -184,6 +186,13 @@ def moe_route(cfg: moe_config, logits: torch.Tensor, routing: dict, workspace: t
     r = routing_struct(routing)
     _check(load().moe_route(ctypes.byref(cfg), _p(logits), _p(e_bias), ctypes.byref(r), _p(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream)), "moe_route")
+
+
+def moe_route_noalloc(cfg: moe_config, logits: torch.Tensor, routing: dict, stream=None,
+                      e_bias: Optional[torch.Tensor] = None) -> None:
+    r = routing_struct(routing)
+    _check(load().moe_route_noalloc(ctypes.byref(cfg), _p(logits), _p(e_bias), ctypes.byref(r),
+                                    _stream(stream)), "moe_route_noalloc")
 
 
 def moe_forward(cfg: moe_config, X: torch.Tensor, weights: dict, Y: torch.Tensor, routing: dict,

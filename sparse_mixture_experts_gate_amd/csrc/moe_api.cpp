@@ -16,11 +16,19 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "kernels.hpp"
 
 using namespace moe;
+
+// The scratch of moe_route_noalloc: one static device array, which each GPU the library
+// runs on holds until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory; its device address on each GPU comes from hipGetSymbolAddress (taken
+// once per device, with that device current, in scratch_ptr below) and only that address
+// is ever passed on.
+static __device__ __align__(256) unsigned char scratch[MOE_ROUTE_SCRATCH_BYTES];
 
 namespace {
 
@@ -256,6 +264,38 @@ int run_routing(const Ctx& x, const float* logits, const float* e_bias, moe_rout
     return run_routing(x.c, x.s, sc, logits, e_bias, r);
 }
 
+// ---- routing with no workspace -------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Bytes of scratch a routing call needs: histograms, scan bases and aux partials of every
+// 64-token chunk, and the tile prefixes (each part 256-byte aligned).
+size_t route_scratch_bytes(const moe_config* c, size_t* off) {
+    const size_t ne = (size_t)c->E * (size_t)nchunk(c) * 4;
+    const size_t sz[4] = {ne, ne, ne, (size_t)3 * (MOE_MAX_EXPERTS + 1) * 4};
+    size_t o = 0;
+    for (int i = 0; i < 4; ++i) {
+        if (off) off[i] = o;
+        o += align256(sz[i] > 0 ? sz[i] : 1);
+    }
+    return o;
+}
+
+// Device address of this GPU's scratch array, resolved on the first call on the device.
+int scratch_ptr(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 ExpertGemmArgs expert_args(const Ctx& x, const moe_weights* w, const moe_routing* r) {
     const moe_config* c = x.c;
     ExpertGemmArgs a = {};
@@ -422,6 +462,7 @@ const char* moe_status_string(int st) {
         case MOE_ERR_WORKSPACE: return "workspace missing or smaller than moe_workspace_bytes()";
         case MOE_ERR_UNSUPPORTED: return "shape outside what the gfx950 kernels support";
         case MOE_ERR_HIP: return "a HIP kernel launch failed";
+        case MOE_ERR_SCRATCH: return "the call needs more scratch than the library's static buffer holds";
         default: return "unknown status";
     }
 }
@@ -455,6 +496,28 @@ int moe_route(const moe_config* cfg, const float* logits, const float* e_bias, m
     if ((st = P.check(cfg->T)) != MOE_OK) return st;
     Ctx x{cfg, (char*)workspace, layout(cfg), (hipStream_t)stream};
     return run_routing(x, logits, e_bias, r);
+}
+
+int moe_route_noalloc(const moe_config* cfg, const float* logits, const float* e_bias,
+                      moe_routing* r, void* stream) {
+    if (!shape_ok(cfg)) return MOE_ERR_INVALID_ARG;
+    int st = supported(cfg);
+    if (st != MOE_OK) return st;
+    if ((st = check_bias(cfg, e_bias)) != MOE_OK) return st;
+    if (!r) return MOE_ERR_NULL_PTR;
+    size_t off[4];
+    if (route_scratch_bytes(cfg, off) > (size_t)MOE_ROUTE_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    Ptrs P;
+    P.add(logits, true);
+    add_routing(P, r, false);
+    if ((st = P.check(cfg->T)) != MOE_OK) return st;
+    void* base = nullptr;
+    if ((st = scratch_ptr(&base)) != MOE_OK) return st;
+    char* b = static_cast<char*>(base);
+    RouteScratch sc = {reinterpret_cast<int32_t*>(b + off[0]), reinterpret_cast<int32_t*>(b + off[1]),
+                       reinterpret_cast<float*>(b + off[2]), reinterpret_cast<int32_t*>(b + off[3]),
+                       nullptr};
+    return run_routing(cfg, (hipStream_t)stream, sc, logits, e_bias, r);
 }
 
 int moe_forward(const moe_config* cfg, const void* X, const moe_weights* w, void* Y,

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings_and_version(lib):
     assert L.abi_version() == 4
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert L.status_string(code) and L.status_string(code) != "unknown status"
     assert L.status_string(12345) == "unknown status"
 
@@ -220,3 +220,17 @@ def test_one_hip_runtime_per_process(lib):
     hips = sorted(set(re.findall(r"\S*libamdhip64\S*", maps)))
     assert len(hips) == 1, hips
 
+
+def test_route_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """moe_route_noalloc's static scratch holds 3 x E x ceil(T/64) int32/float chunk
+    entries plus the tile prefixes: T = 174,656 fits at E = 256, one more token does not.
+    Both calls stop before any launch (the second at its NULL logits)."""
+    w = W.WORKLOADS[0].replace(E=256, k=8, n_groups=8, topk_groups=4, score="sigmoid")
+    r = L.moe_routing(*([4096] * 8))
+    big = L.config(w.replace(T=174657))
+    assert lib.moe_route_noalloc(ctypes.byref(big), ctypes.c_void_p(4096), None, ctypes.byref(r), None) == -7
+    fits = L.config(w.replace(T=174656))
+    assert lib.moe_route_noalloc(ctypes.byref(fits), None, None, ctypes.byref(r), None) == -2
+    assert lib.moe_route_noalloc(ctypes.byref(fits), ctypes.c_void_p(4096), None, None, None) == -2
+    bad = L.config(w.replace(k=300))
+    assert lib.moe_route_noalloc(ctypes.byref(bad), ctypes.c_void_p(4096), None, ctypes.byref(r), None) == -1
