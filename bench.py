@@ -35,7 +35,10 @@ def stage_work(w, fused=False):
     Bytes count each operand read once and each output written once.  fused: the
     weight-gradient stages apply the SGD step to the expert weights (read and write
     the fp32 master, write the working copy) instead of writing the fp32 gradient,
-    and the SGD stage covers the router weight and the biases only."""
+    and the SGD stage covers the router weight and the biases only.  With fused
+    dispatch (w.fused_dispatch) there is no gather and no combine backward: the
+    contractions read the same expert rows straight from X and dY (counted in their
+    own operand bytes, as before) and the down dgrad applies the gates."""
     s = 2 if w.dtype == "bf16" else 4
     T, d, E, k, ffn = w.T, w.d, w.E, w.k, w.ffn
     R = T * k
@@ -53,11 +56,12 @@ def stage_work(w, fused=False):
 
     def by(n):
         return {"flop": 0, "byte": n}
+    fd = getattr(w, "fused_dispatch", 0) == 1
     return {
         "router_logits": {"flop": 2.0 * T * d * E, "byte": T * d * s + E * d * s + T * E * 4},
         "route": by(T * E * 4 + T * k * 8 + R * 12),
         # read X once, write k rows, read the slot indices
-        "gather": by((T * d + R * d) * s + R * 4),
+        "gather": by(0 if fd else (T * d + R * d) * s + R * 4),
         # Xp, W1|W3 in; H and A out
         "up_fwd": {"flop": 2.0 * R * d * hid, "byte": (R * d + n_up + R * hid + R * ffn) * s},
         # A, W2 in; EO out
@@ -68,7 +72,7 @@ def stage_work(w, fused=False):
         # read k rows, gates, slots (and Ys); write Y; read Y_target; write dY
         "combine_loss": by((R * d + 3 * T * d + (T * d if hs else 0)) * s + R * 8),
         # read dY and k rows of EO, write k rows of dEO; slots, gates, dgate
-        "combine_bwd": by((T * d + 2 * R * d) * s + R * 12),
+        "combine_bwd": by(0 if fd else (T * d + 2 * R * d) * s + R * 12),
         # dEO, W2, H in; dH out
         "down_dgrad": {"flop": 2.0 * R * d * ffn, "byte": (R * d + n_dn + 2 * R * hid) * s},
         # dEO, A in; dW2 out (or the SGD step on W2)
@@ -142,17 +146,17 @@ STAGE_SOURCE.update({s: "routing.hip" for s in ("route", "router_bwd")})
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_train_step_t32768_d7168_e256.json")
 
 
-def measured_traffic(stage: str, workload: str, sgd: str):
+def measured_traffic(stage: str, workload: str, sgd: str, dispatch: str = "staged"):
     """HBM bytes per step of a stage from the committed counter summary, or None when
-    there is none, it was taken in the other SGD mode, or the kernel source has
-    changed since the counters were taken."""
+    there is none, it was taken in the other SGD or dispatch mode, or the kernel
+    source has changed since the counters were taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     if rec.get("workload") != workload or stage not in rec.get("stages", {}):
         return None
-    if rec.get("sgd", "stored") != sgd:
+    if rec.get("sgd", "stored") != sgd or rec.get("dispatch", "staged") != dispatch:
         return None
     src = os.path.join(ROOT, "sparse_mixture_experts_gate_amd", "csrc", STAGE_SOURCE[stage])
     from sparse_mixture_experts_gate_amd.profile_summary import code_sha256
@@ -244,6 +248,13 @@ def main(argv=None) -> int:
     ap.add_argument("--sgd", choices=("fused", "stored"), default="fused",
                     help="fused: the expert weight-gradient GEMMs apply the SGD step themselves "
                          "(no expert gradients stored); stored: gradients written, then one SGD pass")
+    ap.add_argument("--dispatch", choices=("auto", "staged", "fused"), default="auto",
+                    help="staged: gather into expert-major copies and a combine backward; fused: "
+                         "the expert contractions read X and dY through token_of and apply the "
+                         "gates themselves (bf16 SwiGLU only); auto: fused where supported")
+    ap.add_argument("--dispatch-probe-steps", type=int, default=2,
+                    help="with fused dispatch: profiled steps of the staged path after the timed "
+                         "region, so that the gather and combine-backward kernels are measured too")
     ap.add_argument("--shared-experts", type=int, default=0,
                     help="add the shared-experts branch: one SwiGLU of hidden N * ffn over every "
                          "token, timed as its own stages")
@@ -273,6 +284,8 @@ def main(argv=None) -> int:
     w = W.BY_NAME[a.workload]
     if a.shared_experts:
         w = w.replace(n_shared=a.shared_experts)
+    if a.dispatch == "fused" or (a.dispatch == "auto" and w.expert == "swiglu" and w.dtype == "bf16"):
+        w = w.replace(fused_dispatch=1)
     dev = "cuda"
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
@@ -352,7 +365,7 @@ def main(argv=None) -> int:
     stages = stage_table(avg, work)
     dom = max(L.STAGES, key=lambda s: avg[s])
     roof = roof_of(work[dom], avg[dom], peak_tf)
-    roof["traffic"] = measured_traffic(dom, w.name, a.sgd)
+    roof["traffic"] = measured_traffic(dom, w.name, a.sgd, "fused" if w.fused_dispatch else "staged")
     roof["kernel"] = dom
 
     graph = None
@@ -414,6 +427,24 @@ def main(argv=None) -> int:
         gemm_mode = "stored"
         stages_stored = stage_table(gemm_avg, stage_work(w, False))
         del gs
+    # with fused dispatch there is no gather and no combine backward in the step: a few
+    # profiled steps of the staged path (own workspace, after the timed region) measure them
+    probe = None
+    if w.fused_dispatch and a.dispatch_probe_steps > 0:
+        ws_stage = w.replace(fused_dispatch=0)
+        cfg_s = L.config(ws_stage)
+        ws_s = L.alloc_workspace(cfg_s, dev)
+        ev3 = [L.StageEvents() for _ in range(a.dispatch_probe_steps)]
+        with torch.cuda.stream(stream):
+            for i in range(a.dispatch_probe_steps):
+                L.moe_train_step_profiled(cfg_s, X, Yt, params, w.lr, w.aux_coef, Y, r, g, loss, ws_s,
+                                          ev3[i], stream=stream)
+            stream.synchronize()
+        _, avg_s = collect(ev3)
+        tab_s = stage_table(avg_s, stage_work(ws_stage, fused))
+        probe = {"steps": a.dispatch_probe_steps, "stages": {s_: tab_s[s_] for s_ in ("gather", "combine_bwd")},
+                 "step_ms": round(sum(avg_s.values()), 3)}
+        del ws_s
     gemm_ms = sum(gemm_avg[s] for s in GEMM_STAGES)
     gemm_flop = sum(work[s]["flop"] for s in GEMM_STAGES)
     counts = r["counts"].cpu().tolist()
@@ -440,6 +471,7 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "ffn": w.ffn, "k": w.k,
                    "n_groups": w.n_groups, "topk_groups": w.topk_groups, "score": w.score,
                    "expert": w.expert, "n_shared": w.n_shared, "step": "forward+loss+backward+sgd",
+                   "dispatch": "fused: no gather, no combine backward" if w.fused_dispatch else "staged",
                    "sgd": "fused into the expert weight-gradient GEMMs" if fused
                    else "one pass over stored gradients"},
         "roofline": roof,
@@ -457,7 +489,10 @@ def main(argv=None) -> int:
             gemm_flop / sum(exec_flop.values()), 4)),
         "step_gpu_ms": {"median": round(pct(step_gpu, 0.5), 3), "p90": round(pct(step_gpu, 0.9), 3)},
         "fwd_bwd_gpu_ms": {"median": round(pct(fb_gpu, 0.5), 3), "p90": round(pct(fb_gpu, 0.9), 3)},
-        "dispatch_gbps": stages["gather"].get("gbs"),
+        "dispatch_gbps": (probe["stages"]["gather"].get("gbs") if probe else stages["gather"].get("gbs")),
+        "dispatch_probe": (None if probe is None else dict(probe, note=(
+            "fused dispatch has no gather or combine-backward kernel; dispatch_gbps is the gather "
+            "kernel of the staged path, measured in these profiled steps after the timed region"))),
         "combine_gbps": stages["combine_loss"].get("gbs"),
         "stages": stages,
         "stages_stored_gradients": stages_stored,

@@ -92,6 +92,20 @@ extern "C" {
  * probabilities or sigmoid values) plus the correction bias, added in fp32.
  * n_shared >= 0 and n_shared * ffn <= 2^24: the shared-experts branch, one
  * SwiGLU over every token with hidden width Hs = n_shared * ffn (0 = none).
+ * fused_dispatch is 0 or 1 ("AI Infra Kernel Lab" README, "Project status": the
+ * fused native path, whose private histogram/scan/scatter pack and weighted
+ * down-projection epilogue cut the intermediate bytes; "Validation evidence":
+ * its byte inventory).  0, the staged path: the token rows are gathered into
+ * expert-major copies (Xp), the expert outputs are combined with their gates,
+ * and the combine backward writes dEO = gate * dY rows.  1, fused: the up
+ * projection and both weight gradients read the token rows of X and dY through
+ * token_of (no Xp, no dEO); the up projection stores each row's A scaled by its
+ * gate, so the down projection's outputs come gate-weighted and the combine is
+ * a plain sum; the down-projection dgrad applies the gate to dY W2 and computes
+ * the gate gradient <dY_t, EO> there as <dY_t W2, silu(H1) * H3>.  Same
+ * results within rounding; bf16 SwiGLU only (else MOE_ERR_UNSUPPORTED).  In the
+ * fused path the saved A and EO hold the gate-scaled rows and MOE_WS_XP has no
+ * buffer.
  * Kernel limits (MOE_ERR_UNSUPPORTED): E <= 256, k <= 16; float32: d and ffn
  * multiples of 4; bfloat16: d and ffn multiples of 64, E a multiple of 8, and
  * T * max(d, hcols, 2 Hs) * 2 < 2^31 (hcols = 2 ffn for SwiGLU, else ffn): an
@@ -113,6 +127,7 @@ typedef struct moe_config {
     int32_t group_score;  /* MOE_GROUP_* */
     float   route_scale;  /* gate multiplier after renormalisation; 0 = 1 */
     int32_t n_shared;     /* shared experts (hidden Hs = n_shared * ffn); 0 = none */
+    int32_t fused_dispatch; /* 0: staged dispatch; 1: fused dispatch (below) */
 } moe_config;
 
 /*
@@ -206,7 +221,7 @@ typedef struct moe_params {
 
 /* Workspace buffers whose byte offsets moe_workspace_offset() reports.
  * They hold the forward's saved activations, read back by moe_backward:
- *   XP    dtype [T*k, d]    gathered expert-major rows
+ *   XP    dtype [T*k, d]    gathered expert-major rows (none with fused dispatch)
  *   H     dtype [T*k, hcols] pre-activations; hcols = 2*ffn for SwiGLU
  *                           ([H1 | H3] per row), ffn for the MLP kinds
  *   A     dtype [T*k, ffn]  activations fed to the down projection
@@ -223,7 +238,8 @@ typedef struct moe_params {
 size_t moe_workspace_bytes(const moe_config* cfg);
 
 /* Byte offset of a saved-activation buffer (MOE_WS_*) inside the workspace,
- * or -1 for an invalid shape or buffer id.  For inspection only. */
+ * or -1 for an invalid shape or buffer id, and for MOE_WS_XP with fused
+ * dispatch.  For inspection only. */
 int64_t moe_workspace_offset(const moe_config* cfg, int32_t which);
 
 /*

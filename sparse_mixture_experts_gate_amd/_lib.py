@@ -42,7 +42,8 @@ class MoeError(RuntimeError):
 class moe_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "d", "E", "ffn", "k", "n_groups", "topk_groups", "score", "expert", "dtype",
-                 "group_score")] + [("route_scale", ctypes.c_float), ("n_shared", ctypes.c_int32)]
+                 "group_score")] + [("route_scale", ctypes.c_float), ("n_shared", ctypes.c_int32),
+                                    ("fused_dispatch", ctypes.c_int32)]
 
 
 WEIGHTS = ("Wg", "W1", "b1", "W2", "b2", "W3", "e_bias", "Ws1", "Ws3", "Ws2")
@@ -71,7 +72,7 @@ class moe_params(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 4                 # the structs above, as include/moe.h declares them
+ABI_VERSION = 5                 # the structs above, as include/moe.h declares them
 
 
 def load() -> ctypes.CDLL:
@@ -129,7 +130,7 @@ def config(w, group_score=None, route_scale=None) -> moe_config:
     rs = route_scale if route_scale is not None else getattr(w, "route_scale", 1.0)
     return moe_config(w.T, w.d, w.E, w.ffn, w.k, w.n_groups, w.topk_groups, code(SCORE, w.score),
                       code(EXPERT, w.expert), code(DTYPE, w.dtype), code(GROUP, gs), float(rs),
-                      int(getattr(w, "n_shared", 0)))
+                      int(getattr(w, "n_shared", 0)), int(getattr(w, "fused_dispatch", 0)))
 
 
 def _p(t: Optional[torch.Tensor]):
@@ -324,5 +325,7 @@ def workspace_view(ws: torch.Tensor, cfg: moe_config, which: str, rows: int, col
                    dtype: torch.dtype) -> torch.Tensor:
     """A [rows, cols] view of a saved-activation buffer inside the workspace."""
     off = workspace_offset(cfg, which)
+    if off < 0:
+        raise ValueError(f"no {which} buffer in this layer's workspace")
     nbytes = rows * cols * torch.tensor([], dtype=dtype).element_size()
     return ws[off:off + nbytes].view(dtype).view(rows, cols)

@@ -58,7 +58,8 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
         float g[MOE_MAX_K];
         load_slots(a.slot_of, t, k, sl);
 #pragma unroll
-        for (int i = 0; i < MOE_MAX_K; ++i) g[i] = (i < k) ? a.gates[(size_t)t * k + i] : 0.f;
+        for (int i = 0; i < MOE_MAX_K; ++i)     // gates NULL: EO rows come gate-weighted already
+            g[i] = (i < k) ? (a.gates ? a.gates[(size_t)t * k + i] : 1.f) : 0.f;
         const uint4* eo = reinterpret_cast<const uint4*>(a.EO);
         for (int v = lane; v < a.vec; v += 64) {
             float acc[N];

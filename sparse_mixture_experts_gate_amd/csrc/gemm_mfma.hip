@@ -109,7 +109,18 @@ struct GemmParams {
     void* W; void* W2; float lr;  // EPI_SGD: C/C2 are fp32 masters, W/W2 their bf16 copies
     const bf16* bias; long bias_es;
     const bf16* H; long ldh; int ffn;
+    // gathered operand rows (fused dispatch): token index of each expert-major row
+    const int32_t* rows_tok;      // GA_ROWS: rows of A; GA_KA / GA_KB: k-rows of A / B
+    int src_rows;                 // rows of the token-major source the gathered rows come from
+    const float* row_scale;       // EPI_UP_SWIGLU_G / EPI_DN_SWIGLU_G: gate of each expert-major row
+    float* dot_part;              // EPI_DN_SWIGLU_G: [N-tiles][rows] partial <dA, A> of each row
+    long dot_ld;                  // rows of dot_part per N-tile
 };
+// Gathered operands.  GA_ROWS: the K-contiguous A operand of a row-mode contraction is
+// read from rows rows_tok[p] of a token-major source instead of rows p of an expert-major
+// one.  GA_KA / GA_KB: the k-strided A / B operand of a weight gradient takes its k-row p
+// (a row of the expert's segment) from row rows_tok[p] of a token-major source.
+enum { GA_NONE = 0, GA_ROWS = 1, GA_KA = 2, GA_KB = 3 };
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, long bytes) {
@@ -128,6 +139,24 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
+// Sum over each half (32 lanes) of the wavefront, the same value on every lane of the half:
+// DPP quad swaps and row mirrors leave each 16-lane row holding its sum, then the two rows
+// of each half are added in a fixed order.
+template <int C> __device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), C, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float half_wave_sum(float v) {
+    v += dpp_f<0xB1>(v);          // quad lane ^ 1
+    v += dpp_f<0x4E>(v);          // quad lane ^ 2
+    v += dpp_f<0x141>(v);         // half-row mirror
+    v += dpp_f<0x140>(v);         // row mirror
+    const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (threadIdx.x & 32) ? hi : lo;
+}
+
 // One wave load: 64 lanes x 16 bytes from a buffer straight into LDS at lds_addr + lane * 16.
 // Issued through inline assembly so that the compiler's wait-count insertion does not
 // turn every later LDS read into a full drain of the load queue: the kernel counts
@@ -138,6 +167,11 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+}
+// The same for 4 bytes a lane (the k-row token indices of a gathered weight-gradient operand).
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                  :: "s"(lds_addr), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -303,15 +337,25 @@ __device__ __forceinline__ void grouped(int q, int mt, int nt, int& tm, int& tn)
 // TM: tile rows.  256: one workgroup per CU, a 4-stage ring; 128 (the SGD epilogue of the
 // weight gradients): two workgroups per CU, 128 accumulators a lane and a 3-stage ring,
 // so that one workgroup's epilogue runs under the other's main loop.
-template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256>
+template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256, int GA = GA_NONE>
 __global__ void __launch_bounds__(NTHR, TM == 128 ? 2 : 1)
 __attribute__((amdgpu_waves_per_eu(TM == 128 ? 2 : 1, TM == 128 ? 2 : 1)))
 gemm_bf16_kernel(GemmParams p) {
     static_assert(TM == 256 || (TM == 128 && MODE == MODE_KSEG && EPI == EPI_SGD), "128-row tiles: SGD epilogue");
+    static_assert(GA == GA_NONE || (GA == GA_ROWS && MODE == MODE_ROWS && !AT) ||
+                  (GA == GA_KA && MODE == MODE_KSEG && AT && TM == 256) ||
+                  (GA == GA_KB && MODE == MODE_KSEG && BT), "gathered operand");
+    constexpr bool KGATHER = GA == GA_KA || GA == GA_KB;
+#ifdef MOE_GEMM_KT64
+    static_assert(!KGATHER, "k-row gathers run in the 32-deep build");
+#endif
     constexpr int NSt = TM == 128 ? 3 : NS;
     constexpr int TILE_A = TM * BK, STAGE = TILE_A + TILE_ELEMS;
     static_assert(DIST <= NSt - 1, "prefetch distance");
-    __shared__ __attribute__((aligned(1024))) bf16 lds[NSt * STAGE];
+    // KGATHER: after the stages, a ring of NSt slots of k-row token indices, 256 bytes per
+    // wavefront (its 8 k-rows of a k-tile, in the order it reads them)
+    constexpr int IDX_ELEMS = KGATHER ? NSt * 512 : 0;
+    __shared__ __attribute__((aligned(1024))) bf16 lds[NSt * STAGE + IDX_ELEMS];
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
@@ -401,18 +445,40 @@ gemm_bf16_kernel(GemmParams p) {
     const bf16* Be = p.B + (long)e * p.bes;
     const bf16* B2e = p.B2 ? p.B2 + (long)e * p.bes : nullptr;
 
+    constexpr uint32_t OUTB = 0x80000000u;         // a byte offset past every buffer bound
     OpPlan pa, pb;
+    // GA_ROWS: lane offset of each of this wave's A loads, the gathered row's start plus the
+    // swizzled chunk (OUTB for rows past the tile: they read zeros)
+    uint32_t gvo[GA == GA_ROWS ? DIRECT_IPW : 1];
     if (AT) {   // A[k][m]
-        const bf16* base = p.A + row_base * p.lda + m0;
-        rsrc_t r = make_rsrc(base, ((long)K * p.lda - m0) * 2);
-        pa = plan_strided<TM>(r, r, (uint32_t)(p.lda * 2), 0x7fffffff);
+        if constexpr (GA == GA_KA) {      // k-row p is row rows_tok[p] of the source
+            rsrc_t r = make_rsrc(p.A + m0, ((long)p.src_rows * p.lda - m0) * 2);
+            pa = plan_strided<TM>(r, r, (uint32_t)(p.lda * 2), 0x7fffffff);
+        } else {
+            const bf16* base = p.A + row_base * p.lda + m0;
+            rsrc_t r = make_rsrc(base, ((long)K * p.lda - m0) * 2);
+            pa = plan_strided<TM>(r, r, (uint32_t)(p.lda * 2), 0x7fffffff);
+        }
+    } else if constexpr (GA == GA_ROWS) {   // A[m][k], row m of the tile = source row rows_tok[m]
+        rsrc_t r = make_rsrc(p.A, (long)p.src_rows * p.lda * 2);
+        pa = plan_direct(r, r, (uint32_t)(p.lda * 2), 0);
+        const int lr = lane / CHUNKS;
+#pragma unroll
+        for (int i = 0; i < DIRECT_IPW; ++i) {
+            const int row = DIRECT_ROWS * (wave * DIRECT_IPW + i) + lr;
+            const uint32_t chunk = pa.vo[i & 1] - (uint32_t)lr * pa.ld_bytes;
+            gvo[i] = row < rows_valid ? (uint32_t)p.rows_tok[row_base + m0 + row] * pa.ld_bytes + chunk : OUTB;
+        }
     } else {    // A[m][k]
         const bf16* base = p.A + (row_base + m0) * p.lda + kbase;
         rsrc_t r = make_rsrc(base, ((long)rows_valid * p.lda - kbase) * 2);
         pa = plan_direct(r, r, (uint32_t)(p.lda * 2), 0);
     }
     if (BT) {   // B[k][n]
-        if (MODE == MODE_KSEG) {
+        if (GA == GA_KB) {                // k-row p is row rows_tok[p] of the source
+            rsrc_t r = make_rsrc(p.B + n0, ((long)p.src_rows * p.ldb - n0) * 2);
+            pb = plan_strided(r, r, (uint32_t)(p.ldb * 2), 0x7fffffff);
+        } else if (MODE == MODE_KSEG) {
             const bf16* base = p.B + row_base * p.ldb + n0;
             rsrc_t r = make_rsrc(base, ((long)K * p.ldb - n0) * 2);
             pb = plan_strided(r, r, (uint32_t)(p.ldb * 2), 0x7fffffff);
@@ -455,10 +521,44 @@ gemm_bf16_kernel(GemmParams p) {
     const int nk = (K + BK - 1) / BK;
     // load q (0 .. LPW-1) of k-tile kt; tiles past the end load harmless data (the buffer
     // bounds make them zeros or rows of this operand) into a stage nobody reads again
+    // KGATHER: the token indices of k-tile kt's k-rows reach LDS one k-tile before that
+    // k-tile's operand loads are issued (ring slot kt % NSt; wave w's 8 k-rows 8w..8w+7 of
+    // the k-tile, stored so that lane half h reads the indices of its k-rows 8w + 2i + h,
+    // i = 0..3, as one 16-byte vector); tk holds those of the k-tile being loaded
+    uint32_t tk[KGATHER ? STRIDED_IPW : 1];
+    const uint32_t idx_base = lds_base + (uint32_t)(NSt * STAGE * 2);
+    const rsrc_t ridx = make_rsrc(KGATHER ? p.rows_tok + row_base : nullptr, KGATHER ? (long)K * 4 : 0);
+    auto idx_dma = [&](int kt) {
+        const int l = lane & 7;
+        dma4(ridx, idx_base + (uint32_t)(kt % NSt) * 1024u + (uint32_t)wave * 256u,
+             (uint32_t)(2 * (l & 3) + ((l >> 2) & 1)) * 4u, (uint32_t)(kt * BK + 8 * wave) * 4u);
+    };
+    auto idx_read = [&](int kt) {
+        const nu4 v = *reinterpret_cast<const nu4*>(reinterpret_cast<const char*>(lds) + NSt * STAGE * 2 +
+                                                    (kt % NSt) * 1024 + wave * 256 + (lane >> 5) * 16);
+#pragma unroll
+        for (int i = 0; i < (KGATHER ? STRIDED_IPW : 1); ++i) tk[i] = v[i];
+    };
+    // load i of a gathered k-strided operand: k-row kt BK + 2 (wave IPW + i) + h of the
+    // segment, read from its source row (k-rows past the segment read zeros)
+    auto dma_gathered = [&](const OpPlan& o, int i, uint32_t t, int kt) {
+        const int h = lane >> 5;
+        const int j = wave * STRIDED_IPW + i;
+        const uint32_t chunk = o.vo[i & 1] - (uint32_t)h * o.ld_bytes;
+        const uint32_t voff = (kt * BK + 2 * j + h < K) ? tk[i] * o.ld_bytes + chunk : OUTB;
+        dma16(o.r0, t + (uint32_t)j * 1024u, voff, 0);
+    };
     auto dma = [&](int q, int kt) {
         const uint32_t st = (uint32_t)(kt % NSt) * (STAGE * 2);
-        if (q < IPW_A) dma_one<AT, TM>(pa, q, lds_base + st, kt * BK, wave);
-        else dma_one<BT>(pb, q - IPW_A, lds_base + st + TILE_A * 2, kt * BK, wave);
+        if (q < IPW_A) {
+            if constexpr (GA == GA_ROWS)
+                dma16(pa.r0, lds_base + st + (uint32_t)(wave * DIRECT_IPW + q) * 1024u, gvo[q], (uint32_t)(kt * BK) * 2u);
+            else if constexpr (GA == GA_KA) dma_gathered(pa, q, lds_base + st, kt);
+            else dma_one<AT, TM>(pa, q, lds_base + st, kt * BK, wave);
+        } else {
+            if constexpr (GA == GA_KB) dma_gathered(pb, q - IPW_A, lds_base + st + TILE_A * 2, kt);
+            else dma_one<BT>(pb, q - IPW_A, lds_base + st + TILE_A * 2, kt * BK, wave);
+        }
     };
     const int rr = lane & 31, hk = lane >> 5;
 
@@ -545,6 +645,13 @@ gemm_bf16_kernel(GemmParams p) {
                 return o + (uint32_t)lane * 16u;
             };
             auto load = [&](int q, int kt) {
+                if constexpr (GA == GA_ROWS) {
+                    if (q < IPW_A) {
+                        rb[q] = __builtin_bit_cast(nu4r, __builtin_amdgcn_raw_buffer_load_b128(
+                            pa.r0, gvo[q], (uint32_t)(kt * BK) * 2u, 0));
+                        return;
+                    }
+                }
                 rb[q] = (q < IPW_A) ? load_one<AT, TM>(pa, q, kt * BK, wave)
                                     : load_one<BT>(pb, q - IPW_A, kt * BK, wave);
             };
@@ -609,10 +716,17 @@ gemm_bf16_kernel(GemmParams p) {
         }
 #else
         if (nk > 0) {
+            if constexpr (KGATHER) {
 #pragma unroll
-            for (int t = 0; t < DIST; ++t)
+                for (int t = 0; t <= DIST; ++t) idx_dma(t);
+                wait_vm<0>();
+            }
+#pragma unroll
+            for (int t = 0; t < DIST; ++t) {
+                if constexpr (KGATHER) idx_read(t);
 #pragma unroll
                 for (int q = 0; q < LPW; ++q) dma(q, t);
+            }
             wait_vm<LPW * (DIST - 1)>();
             __syncthreads();
             Frags fa, fb;
@@ -623,6 +737,12 @@ gemm_bf16_kernel(GemmParams p) {
                 const bf16* As = lds + st * STAGE;
                 const bf16* Bs = lds + st * STAGE + TILE_A;
                 const int pf = kt + DIST;
+                if constexpr (KGATHER) {
+                    // the indices of k-tile pf + 1 go out before k-tile pf's operand loads, so
+                    // the wait at the end of this k-tile (all but the last LPW loads) covers them
+                    idx_dma(pf + 1);
+                    idx_read(pf);
+                }
 #pragma unroll
                 for (int s = 0; s < KSTEPS; ++s) {
                     Frags& cur = (s & 1) ? fb : fa;
@@ -777,7 +897,8 @@ gemm_bf16_kernel(GemmParams p) {
             }
             return;
         }
-        if constexpr ((EPI == EPI_STORE || EPI == EPI_STORE_BIAS || EPI == EPI_UP_SWIGLU) && !OUT_F32) {
+        if constexpr ((EPI == EPI_STORE || EPI == EPI_STORE_BIAS || EPI == EPI_UP_SWIGLU ||
+                       EPI == EPI_UP_SWIGLU_G) && !OUT_F32) {
             // bf16 tile written out through LDS: 512-byte rows of 32 chunks, chunk q of row r
             // at q ^ (r & 31); each lane puts its 4 consecutive columns (8 bytes) in place,
             // then the 256 threads store whole rows with 16-byte vectors
@@ -846,6 +967,16 @@ gemm_bf16_kernel(GemmParams p) {
                             put(rb + i * 32 + rr, c, h1);
                             put(rb + i * 32 + rr, 128 + c, h3);
                         }
+                // EPI_UP_SWIGLU_G: the gates of this lane's accumulator rows, in flight while
+                // the H rows drain
+                float gsc[EPI == EPI_UP_SWIGLU_G ? NI : 1];
+                if constexpr (EPI == EPI_UP_SWIGLU_G) {
+#pragma unroll
+                    for (int i = 0; i < NI; ++i) {
+                        const int row = rb + i * 32 + rr;
+                        gsc[i] = row < rows_valid ? p.row_scale[row_base + m0 + row] : 0.f;
+                    }
+                }
                 __syncthreads();
                 bf16* H = reinterpret_cast<bf16*>(p.C2);
                 drain(256, [&](int r, int c, uint4 x) {
@@ -864,7 +995,10 @@ gemm_bf16_kernel(GemmParams p) {
                         for (int g = 0; g < 4; ++g) {
                             float a[4];
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) a[q] = silu_fast_(acc[i][j][g * 4 + q]) * acc[i][j + 1][g * 4 + q];
+                            for (int q = 0; q < 4; ++q) {
+                                a[q] = silu_fast_(acc[i][j][g * 4 + q]) * acc[i][j + 1][g * 4 + q];
+                                if constexpr (EPI == EPI_UP_SWIGLU_G) a[q] *= gsc[i];
+                            }
                             put(rb + i * 32 + rr, ((cb + j * 32) >> 6) * 32 + g * 8 + hk * 4, a);
                         }
                 __syncthreads();
@@ -878,8 +1012,8 @@ gemm_bf16_kernel(GemmParams p) {
             }
             return;
         }
-        if constexpr (EPI == EPI_DN_SWIGLU || EPI == EPI_DN_RELU || EPI == EPI_DN_GELU ||
-                      EPI == EPI_UP_RELU || EPI == EPI_UP_GELU) {
+        if constexpr (EPI == EPI_DN_SWIGLU || EPI == EPI_DN_SWIGLU_G || EPI == EPI_DN_RELU ||
+                      EPI == EPI_DN_GELU || EPI == EPI_UP_RELU || EPI == EPI_UP_GELU) {
             // Row-pass epilogue of the MLP forward (bias + activation: H and A out) and of the
             // activation backward (H in, dH out).  The fp32 accumulators go out in passes of
             // 32 rows through LDS (1 KB rows, 16-byte chunk c of row r at c ^ r, two buffers,
@@ -890,8 +1024,13 @@ gemm_bf16_kernel(GemmParams p) {
             // rows and is issued unconditionally (a lane outside the tile gets an offset past the
             // bound: its store is dropped, its load reads zeros), so the waits for H count
             // exactly and never cover the stores of the two passes before.
+            // EPI_DN_SWIGLU_G: the accumulator is D = dY_t W2 for the row's token t, and
+            // dA = g D with g the row's gate; each row's partial sum of D * silu(H1) * H3
+            // over the tile's columns (its share of the gate gradient <dY_t, EO>) is added up
+            // over the row's 32 threads in a fixed order and stored per N-tile.
             constexpr bool UP = EPI == EPI_UP_RELU || EPI == EPI_UP_GELU;
-            constexpr bool GLU = EPI == EPI_DN_SWIGLU;
+            constexpr bool GLU = EPI == EPI_DN_SWIGLU || EPI == EPI_DN_SWIGLU_G;
+            constexpr bool GATED = EPI == EPI_DN_SWIGLU_G;
             constexpr int NH = GLU ? 2 : 1;                    // H vectors per 8 columns (backward)
             constexpr uint32_t OUT = 0x80000000u;              // past every bound
             float* stage = reinterpret_cast<float*>(lds);   // 2 x 32 rows x 1 KB
@@ -914,7 +1053,11 @@ gemm_bf16_kernel(GemmParams p) {
                 if (col_ok) unpack8(*reinterpret_cast<const nu4*>(p.bias + (long)e * p.bias_es + n), bias8);
             }
             nu4 hb[3][4][NH];
-            auto prefetch = [&](int q, nu4 (*dst)[NH]) {
+            float gb[3][4];                                    // GATED: gates of the rows, same passes
+            const rsrc_t rg = make_rsrc(GATED ? p.row_scale + rowg : nullptr, GATED ? (long)rows_valid * 4 : 0);
+            const rsrc_t rdot = make_rsrc(GATED ? p.dot_part + (long)n_t * p.dot_ld + rowg : nullptr,
+                                          GATED ? (long)rows_valid * 4 : 0);
+            auto prefetch = [&](int q, int b) {
                 if constexpr (!UP) {
 #pragma unroll
                     for (int it = 0; it < 4; ++it) {
@@ -922,18 +1065,21 @@ gemm_bf16_kernel(GemmParams p) {
                         const bool ok = r < rows_valid && col_ok;
 #pragma unroll
                         for (int h = 0; h < NH; ++h)
-                            dst[it][h] = __builtin_bit_cast(nu4, __builtin_amdgcn_raw_buffer_load_b128(
+                            hb[b][it][h] = __builtin_bit_cast(nu4, __builtin_amdgcn_raw_buffer_load_b128(
                                 rh, ok ? (uint32_t)(r * ldh + n + h * ffn) * 2 : OUT, 0, 0));
+                        if constexpr (GATED)
+                            gb[b][it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                rg, r < rows_valid ? (uint32_t)r * 4 : OUT, 0, 0));
                     }
                 }
             };
-            prefetch(0, hb[0]);
-            if (npass > 1) prefetch(1, hb[1]);
+            prefetch(0, 0);
+            if (npass > 1) prefetch(1, 1);
             __syncthreads();                                   // every wave is past its last LDS read
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 if (q >= npass) break;                         // uniform
-                if (q + 2 < npass) prefetch(q + 2, hb[(q + 2) % 3]);
+                if (q + 2 < npass) prefetch(q + 2, (q + 2) % 3);
                 float* S = stage + (q & 1) * (32 * 256);
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
@@ -973,6 +1119,18 @@ gemm_bf16_kernel(GemmParams p) {
                         if constexpr (GLU) {
                             float h3[8], o3[8];
                             unpack8(hb[q % 3][it][NH - 1], h3);
+                            if constexpr (GATED) {
+                                float dot = 0.f;
+#pragma unroll
+                                for (int k = 0; k < 8; ++k) dot = fmaf(v[k], silu_fast_(h1[k]) * h3[k], dot);
+                                dot = half_wave_sum(dot);              // this thread's row
+                                const float g = gb[q % 3][it];
+#pragma unroll
+                                for (int k = 0; k < 8; ++k) v[k] *= g;
+                                __builtin_amdgcn_raw_buffer_store_b32(
+                                    __builtin_bit_cast(int, dot), rdot,
+                                    (c8 == 0 && rt < rows_valid) ? (uint32_t)rt * 4 : OUT, 0, 0);
+                            }
 #pragma unroll
                             for (int k = 0; k < 8; ++k) {
                                 o1[k] = v[k] * h3[k] * silu_grad_fast_(h1[k]);
@@ -1003,7 +1161,7 @@ gemm_bf16_kernel(GemmParams p) {
 }
 
 // ---- host side -------------------------------------------------------------------------------
-template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256>
+template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256, int GA = GA_NONE>
 static hipError_t run(GemmParams p, int grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
     // Whole XCD rounds; surplus workgroups exit at once. A multiple of 8 is a multiple of
@@ -1021,7 +1179,7 @@ static hipError_t run(GemmParams p, int grid, hipStream_t s) {
         if (grid <= 0) return hipSuccess;
     }
     grid = (grid + 7) & ~7;
-    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, AT, BT, EPI, OUT_F32, TM>), dim3(grid), dim3(NTHR), 0, s, p);
+    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, AT, BT, EPI, OUT_F32, TM, GA>), dim3(grid), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
 
@@ -1047,8 +1205,13 @@ hipError_t mfma_up_fwd(const ExpertGemmArgs& a, hipStream_t s) {
         p.B2 = (const bf16*)a.W3; p.paired = 1; p.N = 2 * a.ffn;
         p.C = a.A; p.C2 = a.H;
         const int NT = (a.ffn + 127) / 128;
+        if (a.token_of) {       // fused dispatch: rows of X through token_of, A gate-scaled
+            p.A = (const bf16*)a.X; p.rows_tok = a.token_of; p.src_rows = a.T; p.row_scale = a.gate_of;
+            return run<MODE_ROWS, false, false, EPI_UP_SWIGLU_G, false, 256, GA_ROWS>(p, p.mtiles_ub * NT, s);
+        }
         return run<MODE_ROWS, false, false, EPI_UP_SWIGLU, false>(p, p.mtiles_ub * NT, s);
     }
+    if (a.token_of) return hipErrorInvalidValue;      // fused dispatch: SwiGLU only
     p.N = a.ffn; p.C = a.A; p.C2 = a.H; p.ldc = a.ffn;
     p.bias = (const bf16*)a.b1; p.bias_es = a.ffn;
     const int NT = (a.ffn + BN - 1) / BN;
@@ -1084,6 +1247,12 @@ hipError_t mfma_down_dgrad(const ExpertGemmArgs& a, hipStream_t s) {
     p.C = a.dH; p.ldc = hcols;
     p.H = (const bf16*)a.H; p.ldh = hcols;
     const int grid = p.mtiles_ub * ((a.ffn + BN - 1) / BN);
+    if (a.token_of) {           // fused dispatch: rows of dY through token_of, gate applied here
+        if (!glu) return hipErrorInvalidValue;
+        p.A = (const bf16*)a.dY; p.rows_tok = a.token_of; p.src_rows = a.T; p.row_scale = a.gate_of;
+        p.dot_part = a.dgate_part; p.dot_ld = a.rows;
+        return run<MODE_ROWS, false, true, EPI_DN_SWIGLU_G, false, 256, GA_ROWS>(p, grid, s);
+    }
     if (glu) return run<MODE_ROWS, false, true, EPI_DN_SWIGLU, false>(p, grid, s);
     if (a.expert == MOE_EXPERT_RELU) return run<MODE_ROWS, false, true, EPI_DN_RELU, false>(p, grid, s);
     return run<MODE_ROWS, false, true, EPI_DN_GELU, false>(p, grid, s);
@@ -1112,6 +1281,14 @@ hipError_t mfma_down_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     p.C = a.dW2; p.ldc = a.ffn; p.ces = (long)a.d * a.ffn;
     const int grid = a.E * ((a.d + BM - 1) / BM) * ((a.ffn + BN - 1) / BN);
     p.xcd_group = 2;
+    if (a.token_of) {           // fused dispatch: k-rows of dY through token_of; A is gate-scaled
+        p.A = (const bf16*)a.dY; p.rows_tok = a.token_of; p.src_rows = a.T;
+        if (a.W2m) {
+            p.C = a.W2m; p.W = a.W2w; p.lr = a.lr;
+            return run<MODE_KSEG, true, true, EPI_SGD, true, 256, GA_KA>(p, grid, s);
+        }
+        return run<MODE_KSEG, true, true, EPI_STORE, true, 256, GA_KA>(p, grid, s);
+    }
     if (a.W2m) {    // SGD step on W2 in place of storing dW2
         p.C = a.W2m; p.W = a.W2w; p.lr = a.lr;
         return run<MODE_KSEG, true, true, EPI_SGD, true>(p, grid, s);
@@ -1131,13 +1308,23 @@ hipError_t mfma_up_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     p.C = a.dW1; p.ldc = a.d; p.ces = (long)a.ffn * a.d;
     if (glu) { p.C2 = a.dW3; p.c2_mstart = a.ffn; }
     const int grid = a.E * ((hcols + BM - 1) / BM) * ((a.d + BN - 1) / BN);
+    const int grid128 = a.E * ((hcols + 127) / 128) * ((a.d + BN - 1) / BN);
     p.xcd_group = 2;
+    if (a.token_of) {           // fused dispatch: k-rows of X through token_of
+        p.B = (const bf16*)a.X; p.rows_tok = a.token_of; p.src_rows = a.T;
+        if (a.W1m) {
+            p.C = a.W1m; p.W = a.W1w; p.lr = a.lr;
+            if (glu) { p.C2 = a.W3m; p.W2 = a.W3w; }
+            return run<MODE_KSEG, true, true, EPI_SGD, true, 128, GA_KB>(p, grid128, s);
+        }
+        return run<MODE_KSEG, true, true, EPI_STORE, true, 256, GA_KB>(p, grid, s);
+    }
     if (a.W1m) {    // SGD step on W1 (and W3) in place of storing dW1 (dW3)
         p.C = a.W1m; p.W = a.W1w; p.lr = a.lr;
         if (glu) { p.C2 = a.W3m; p.W2 = a.W3w; }
         // 128-row tiles, two workgroups per CU: one's SGD epilogue runs under the other's
         // main loop (measured 3-4% faster here; the same for dW2 brought nothing)
-        return run<MODE_KSEG, true, true, EPI_SGD, true, 128>(p, a.E * ((hcols + 127) / 128) * ((a.d + BN - 1) / BN), s);
+        return run<MODE_KSEG, true, true, EPI_SGD, true, 128>(p, grid128, s);
     }
     return run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
 }

@@ -53,7 +53,10 @@ struct RouterBwdArgs {
     const float* logits;
     const int32_t* topk_idx;
     const float* gates;
-    const float* dgate;
+    const float* dgate;    // [T,k], or NULL: the gate gradient is summed from dgate_part
+    const float* dgate_part;  // [nparts][rows] partial gate gradients of the expert-major rows
+    const int32_t* slot_of;   // [T,k] (with dgate_part)
+    int nparts; long part_ld;
     const int32_t* counts;
     void* dlogits;         // [T,E] dtype
     float aux_coef;
@@ -73,7 +76,9 @@ struct GatherArgs {
     int T, k, vec;         // vec = 16-byte vectors per row
 };
 struct CombineArgs {
-    const void* EO; const int32_t* slot_of; const float* gates; void* Y;
+    const void* EO; const int32_t* slot_of;
+    const float* gates;    // [T,k], or NULL when EO rows already carry their gates
+    void* Y;
     const void* Ys;        // shared-branch output [T, d] added to Y, or NULL
     const void* Yt;        // NULL: no loss
     void* dY;              // written when Yt != NULL: 2 (Y - Yt) / (T d)
@@ -132,6 +137,9 @@ enum GemmEpi {
     EPI_SGD = 7,           // weight gradient applied as an SGD step instead of stored:
                            // master = fma(-lr, acc, master), working copy = bf16(master)
     EPI_STORE_BIAS = 8,    // bf16 C = acc + bias per column (MLP down projection)
+    EPI_UP_SWIGLU_G = 9,   // EPI_UP_SWIGLU with A scaled by the gate of its row
+    EPI_DN_SWIGLU_G = 10,  // EPI_DN_SWIGLU from dA = gate * acc, plus the row partials
+                           // of <acc, silu(H1) * H3> (the gate gradient)
 };
 
 // Expert contractions of the layer.  All row-major; see each field.
@@ -152,6 +160,16 @@ struct ExpertGemmArgs {
     float* W1m; float* W3m; float* W2m;
     void* W1w; void* W3w; void* W2w;
     float lr;
+    // Fused dispatch (SwiGLU, bf16), when token_of is set: the expert-major rows of the
+    // layer input and of dY are read from the token-major X and dY through token_of
+    // instead of from gathered copies; A is stored scaled by each row's gate (so EO
+    // comes out gate-weighted); the down dgrad takes dA = gate * (dY W2) and writes each
+    // row's partial gate gradient per 256-column tile into dgate_part [tiles][rows].
+    const int32_t* token_of;         // [rows] token of each expert-major row
+    const float* gate_of;            // [rows] gate of each expert-major row
+    const void* X;                   // [T, d] layer input
+    const void* dY;                  // [T, d] gradient of Y
+    float* dgate_part;               // [ceil(ffn / 256)][rows]
 };
 // float32 layer (gemm_simple.hip): one thread per output element, fp32 accumulate.
 hipError_t simple_up_fwd(const ExpertGemmArgs& a, hipStream_t s);

@@ -35,7 +35,7 @@ namespace {
 constexpr int kChunk = 64;
 
 enum WsBuf {
-    B_XP = 0, B_H, B_A, B_EO, B_DEO, B_DH, B_DXP, B_DY, B_DXR, B_DL, B_DGATE, B_GATEOF,
+    B_XP = 0, B_H, B_A, B_EO, B_DEO, B_DH, B_DXP, B_DY, B_DXR, B_DL, B_DGATE, B_GATEOF, B_DGPART,
     B_HIST, B_CBASE, B_QPART, B_LPART, B_TPREFIX, B_DWGPART, B_LOGPART,
     // shared-experts branch: [H1 | H3] [T, 2 Hs], A [T, Hs], Ys [T, d], dH [T, 2 Hs],
     // dX part [T, d], and its one-segment tables (offsets {0, T}, tile prefixes)
@@ -67,8 +67,13 @@ bool shape_ok(const moe_config* c) {
     if (c->group_score == MOE_GROUP_TOP2_SUM && c->n_groups > 1 && c->E / c->n_groups < 2) return false;
     if (!std::isfinite(c->route_scale) || c->route_scale < 0.f) return false;
     if (c->n_shared < 0 || (int64_t)c->n_shared * c->ffn > (int64_t(1) << 24)) return false;
+    if (c->fused_dispatch != 0 && c->fused_dispatch != 1) return false;
     return true;
 }
+
+inline bool fused(const moe_config* c) { return c->fused_dispatch == 1; }
+// tiles of 256 columns of the down-projection dgrad: partial gate gradients per row
+inline int dgate_parts(const moe_config* c) { return (c->ffn + 255) / 256; }
 
 inline int shared_hidden(const moe_config* c) { return c->n_shared * c->ffn; }
 
@@ -83,6 +88,8 @@ int check_bias(const moe_config* c, const float* e_bias) {
 
 int supported(const moe_config* c) {
     if (c->E > MOE_MAX_EXPERTS || c->k > MOE_MAX_K || c->n_groups > 128) return MOE_ERR_UNSUPPORTED;
+    // fused dispatch: the bf16 SwiGLU contractions only
+    if (fused(c) && (c->dtype != MOE_DTYPE_BF16 || c->expert != MOE_EXPERT_SWIGLU)) return MOE_ERR_UNSUPPORTED;
     if (c->dtype == MOE_DTYPE_F32) {
         if (c->d % 4 || c->ffn % 4) return MOE_ERR_UNSUPPORTED;
     } else {
@@ -110,11 +117,12 @@ Layout layout(const moe_config* c) {
     const size_t s = esize(c), T = c->T, rows = (size_t)c->T * c->k, d = c->d, E = c->E;
     const size_t nc = nchunk(c);
     size_t sz[B_COUNT];
-    sz[B_XP] = rows * d * s;
+    // fused dispatch: no gathered rows and no dEO (read through token_of from X and dY)
+    sz[B_XP] = fused(c) ? 0 : rows * d * s;
     sz[B_H] = rows * hcols(c) * s;
     sz[B_A] = rows * c->ffn * s;
     sz[B_EO] = rows * d * s;
-    sz[B_DEO] = rows * d * s;
+    sz[B_DEO] = fused(c) ? 0 : rows * d * s;
     sz[B_DH] = rows * hcols(c) * s;
     sz[B_DXP] = rows * d * s;
     sz[B_DY] = T * d * s;
@@ -122,6 +130,7 @@ Layout layout(const moe_config* c) {
     sz[B_DL] = T * E * s;
     sz[B_DGATE] = T * c->k * 4;
     sz[B_GATEOF] = rows * 4;
+    sz[B_DGPART] = fused(c) ? (size_t)dgate_parts(c) * rows * 4 : 0;
     sz[B_HIST] = E * nc * 4;
     sz[B_CBASE] = E * nc * 4;
     sz[B_QPART] = nc * E * 4;
@@ -312,6 +321,16 @@ ExpertGemmArgs expert_args(const Ctx& x, const moe_weights* w, const moe_routing
     return a;
 }
 
+// Fused dispatch: the expert contractions read X and dY through token_of, apply the gates
+// themselves, and leave the gate gradient in per-tile partials.
+void set_fused(const Ctx& x, ExpertGemmArgs& a, const void* X, const moe_routing* r, const void* dY) {
+    a.token_of = r->token_of;
+    a.gate_of = x.buf<float>(B_GATEOF);
+    a.X = X;
+    a.dY = dY;
+    a.dgate_part = x.buf<float>(B_DGPART);
+}
+
 // The shared-experts branch as one expert segment of all T rows: the expert
 // contractions run it with E = 1 and the token rows themselves in place of the
 // gathered rows.  Its tables (offsets {0, T}, tile prefixes) are in B_STAB.
@@ -341,10 +360,13 @@ int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_
     TRY(x.mark(MOE_STAGE_ROUTE));
     int st = run_routing(x, r->logits, w->e_bias, r);
     if (st != MOE_OK) return st;
-    GatherArgs ga = {X, r->slot_of, x.buf<void>(B_XP), c->T, c->k, vec};
     TRY(x.mark(MOE_STAGE_GATHER));
-    TRY(launch_gather(ga, c->dtype, x.s));
+    if (!fused(c)) {                // fused dispatch: the up projection reads X through token_of
+        GatherArgs ga = {X, r->slot_of, x.buf<void>(B_XP), c->T, c->k, vec};
+        TRY(launch_gather(ga, c->dtype, x.s));
+    }
     ExpertGemmArgs ea = expert_args(x, w, r);
+    if (fused(c)) set_fused(x, ea, X, r, nullptr);
     TRY(x.mark(MOE_STAGE_UP_FWD));
     TRY(f32 ? simple_up_fwd(ea, x.s) : kt64::mfma_up_fwd(ea, x.s));
     TRY(x.mark(MOE_STAGE_DOWN_FWD));
@@ -358,7 +380,7 @@ int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_
         TRY(f32 ? simple_down_fwd(sa, x.s) : mfma_down_fwd(sa, x.s));
     }
     TRY(x.mark(MOE_STAGE_COMBINE_LOSS));
-    CombineArgs ca = {x.buf<void>(B_EO), r->slot_of, r->gates, Y,
+    CombineArgs ca = {x.buf<void>(B_EO), r->slot_of, fused(c) ? nullptr : r->gates, Y,
                       shared ? x.buf<void>(B_YS) : nullptr, Yt, x.buf<void>(B_DY),
                       x.buf<float>(B_LPART), c->T > 0 ? 2.0f / ((float)c->T * (float)c->d) : 0.f,
                       c->T, c->k, vec};
@@ -380,11 +402,14 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
     const moe_config* c = x.c;
     const bool f32 = c->dtype == MOE_DTYPE_F32;
     const int vec = c->d * esize(c) / 16;
-    CombineBwdArgs cb = {dY, x.buf<void>(B_EO), r->slot_of, r->gates, x.buf<float>(B_DGATE),
-                         x.buf<void>(B_DEO), c->T, c->k, vec};
     TRY(x.mark(MOE_STAGE_COMBINE_BWD));
-    TRY(launch_combine_bwd(cb, c->dtype, x.s));
+    if (!fused(c)) {                // fused dispatch: the down dgrad applies the gates itself
+        CombineBwdArgs cb = {dY, x.buf<void>(B_EO), r->slot_of, r->gates, x.buf<float>(B_DGATE),
+                             x.buf<void>(B_DEO), c->T, c->k, vec};
+        TRY(launch_combine_bwd(cb, c->dtype, x.s));
+    }
     ExpertGemmArgs ea = expert_args(x, w, r);
+    if (fused(c)) set_fused(x, ea, X, r, dY);
     ea.dW1 = g->dW1; ea.dW2 = g->dW2; ea.dW3 = g->dW3;
     if (sgd) {
         const bool glu = c->expert == MOE_EXPERT_SWIGLU;
@@ -429,8 +454,10 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
         ColSumArgs b1 = {x.buf<void>(B_DH), c->ffn, r->offsets, g->db1, c->ffn, c->E};
         TRY(launch_colsum(b1, c->dtype, x.s));
     }
-    RouterBwdArgs rb = {r->logits, r->topk_idx, r->gates, x.buf<float>(B_DGATE), r->counts,
-                        x.buf<void>(B_DL), aux_coef, c->T, c->E, c->k, c->score, route_scale(c)};
+    RouterBwdArgs rb = {r->logits, r->topk_idx, r->gates, fused(c) ? nullptr : x.buf<float>(B_DGATE),
+                        x.buf<float>(B_DGPART), r->slot_of, dgate_parts(c), (long)c->T * c->k,
+                        r->counts, x.buf<void>(B_DL), aux_coef, c->T, c->E, c->k, c->score,
+                        route_scale(c)};
     TRY(x.mark(MOE_STAGE_ROUTER_BWD));
     TRY(launch_router_bwd(rb, c->dtype, x.s));
     RouterGemmArgs rg = {c->T, c->d, c->E, X, w->Wg, x.buf<void>(B_DL), nullptr,
@@ -451,7 +478,7 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 4; }
+int32_t moe_abi_version(void) { return 5; }
 
 const char* moe_status_string(int st) {
     switch (st) {
@@ -476,7 +503,7 @@ int64_t moe_workspace_offset(const moe_config* cfg, int32_t which) {
     if (!shape_ok(cfg)) return -1;
     Layout L = layout(cfg);
     switch (which) {
-        case MOE_WS_XP: return (int64_t)L.off[B_XP];
+        case MOE_WS_XP: return fused(cfg) ? -1 : (int64_t)L.off[B_XP];
         case MOE_WS_H: return (int64_t)L.off[B_H];
         case MOE_WS_A: return (int64_t)L.off[B_A];
         case MOE_WS_EO: return (int64_t)L.off[B_EO];

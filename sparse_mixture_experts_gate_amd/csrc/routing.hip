@@ -521,7 +521,12 @@ router_bwd_kernel(RouterBwdArgs a) {
     if (lane < k) {
         e_i = a.topk_idx[(size_t)t * k + lane];
         g_i = a.gates[(size_t)t * k + lane];
-        dg_i = a.dgate[(size_t)t * k + lane];
+        if (a.dgate) {
+            dg_i = a.dgate[(size_t)t * k + lane];
+        } else {            // the row's partial sums over the down-projection column tiles, in order
+            const long p = a.slot_of[(size_t)t * k + lane];
+            for (int j = 0; j < a.nparts; ++j) dg_i += a.dgate_part[(long)j * a.part_ld + p];
+        }
         w_i = selected_score(a.logits[(size_t)t * E + e_i], ts, a.score);
     }
     const float S = wv_sum(w_i);

@@ -51,6 +51,7 @@ class Workload:
     route_scale: float = 1.0
     e_bias: float = 0.0           # std of the seeded correction bias; 0 = no bias
     n_shared: int = 0             # shared experts: one SwiGLU of hidden n_shared * ffn; 0 = none
+    fused_dispatch: int = 0       # 1: expert contractions read X / dY through token_of (SwiGLU bf16)
 
     @property
     def torch_dtype(self) -> torch.dtype:

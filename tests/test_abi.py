@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert L.abi_version() == 4
+    assert L.abi_version() == 5
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert L.status_string(code) and L.status_string(code) != "unknown status"
     assert L.status_string(12345) == "unknown status"
@@ -234,3 +234,18 @@ def test_route_noalloc_rejects_shapes_beyond_its_scratch(lib):
     assert lib.moe_route_noalloc(ctypes.byref(fits), ctypes.c_void_p(4096), None, None, None) == -2
     bad = L.config(w.replace(k=300))
     assert lib.moe_route_noalloc(ctypes.byref(bad), ctypes.c_void_p(4096), None, ctypes.byref(r), None) == -1
+
+
+def test_fused_dispatch_rules(lib):
+    w = W.BY_NAME["grouped_sigmoid_t16384_e64"]
+    assert L.workspace_bytes(L.config(w.replace(fused_dispatch=2))) == 0
+    assert _call_forward(L.config(w.replace(fused_dispatch=2))) == -1
+    # bf16 SwiGLU only
+    assert _call_forward(L.config(w.replace(fused_dispatch=1, expert="gelu"))) == -5
+    assert _call_forward(L.config(W.WORKLOADS[0].replace(fused_dispatch=1))) == -5
+    # no gathered copy of X and no dEO: the workspace shrinks by two [T k, d] buffers
+    staged = L.workspace_bytes(L.config(w))
+    fused = L.workspace_bytes(L.config(w.replace(fused_dispatch=1)))
+    assert staged - fused >= 2 * w.T * w.k * w.d * 2 - 8 * w.T * w.k * 4
+    assert L.workspace_offset(L.config(w.replace(fused_dispatch=1)), "XP") == -1
+    assert L.workspace_offset(L.config(w), "XP") >= 0

@@ -110,8 +110,9 @@ def _dense_parity(w, label):
     return run, fw
 
 
-def test_skewed_swiglu_full():
-    w = W.BY_NAME["skewed_swiglu_t8192_e32"]
+@pytest.mark.parametrize("dispatch", [0, 1], ids=["staged", "fused-dispatch"])
+def test_skewed_swiglu_full(dispatch):
+    w = W.BY_NAME["skewed_swiglu_t8192_e32"].replace(fused_dispatch=dispatch)
     run, fw = _dense_parity(w, w.name)
     # identical gate rows give identical logits; ties leave experts 29..31 empty
     lg = run.routing["logits"]
@@ -122,20 +123,21 @@ def test_skewed_swiglu_full():
     assert counts[29] == counts[30] == counts[31] == 0
 
 
-def test_grouped_sigmoid_e64_full():
-    w = W.BY_NAME["grouped_sigmoid_t16384_e64"]
+@pytest.mark.parametrize("dispatch", [0, 1], ids=["staged", "fused-dispatch"])
+def test_grouped_sigmoid_e64_full(dispatch):
+    w = W.BY_NAME["grouped_sigmoid_t16384_e64"].replace(fused_dispatch=dispatch)
     _dense_parity(w, w.name)
 
 
 @pytest.mark.timeout(900)
 def test_benchmarked_train_step_e256_d7168(capsys):
-    """The step the benchmark times (T=32768, d=7168, E=256, k=8; SGD fused into the
-    weight-gradient GEMMs) against the oracle's training step, streamed one expert at
+    """The step the benchmark times (T=32768, d=7168, E=256, k=8; fused dispatch; SGD
+    fused into the weight-gradient GEMMs) against the oracle's training step, streamed one expert at
     a time: the loss triple, Y, dX and dWg on every token, and the master updates and
     bf16 working copies of eight experts, the most and the least loaded among them.
     lr is 100 so that the update moves the float32 masters (at 1e-3 it is below
     their resolution); dY is the step's own MSE gradient."""
-    w = W.BY_NAME["grouped_sigmoid_t32768_d7168_e256"]
+    w = W.BY_NAME["grouped_sigmoid_t32768_d7168_e256"].replace(fused_dispatch=1)
     lr = 100.0
     t0 = time.time()
 
@@ -247,7 +249,8 @@ def _train_once(w, lr, fused):
     return out
 
 
-def test_fused_sgd_step_full_size_equals_stored():
+@pytest.mark.parametrize("dispatch", [0, 1], ids=["staged", "fused-dispatch"])
+def test_fused_sgd_step_full_size_equals_stored(dispatch):
     """The launch configuration the benchmark times: the T=32768, d=7168, E=256
     training step with the SGD step fused into the weight-gradient GEMMs gives
     bitwise the outputs and parameters of the step that stores the gradients
@@ -256,7 +259,7 @@ def test_fused_sgd_step_full_size_equals_stored():
     covers the stored-gradient step too.  lr is raised from 1e-3 to 100 so that
     the step moves the float32 masters (at 1e-3 the update is below their
     resolution)."""
-    w = W.BY_NAME["grouped_sigmoid_t32768_d7168_e256"]
+    w = W.BY_NAME["grouped_sigmoid_t32768_d7168_e256"].replace(fused_dispatch=dispatch)
     say(f"[{w.name}] stored-gradient step")
     a = _train_once(w, 100.0, fused=False)
     say(f"[{w.name}] fused step")
