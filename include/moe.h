@@ -261,7 +261,7 @@ int moe_route(const moe_config* cfg, const float* logits, const float* e_bias,
  * of MOE_ROUTE_SCRATCH_BYTES that each GPU the library runs on holds until the
  * process ends.  Nothing is allocated or freed, and no scratch entry needs
  * clearing (each is written before it is read within the call).
- * Limit: 3 * align256(E * ceil(T / 64) * 4) + align256(3 * 257 * 4) bytes must
+ * Limit: 3 * align256(E * ceil(T / 64) * 4) + align256(4 * 257 * 4) bytes must
  * fit in MOE_ROUTE_SCRATCH_BYTES (T up to 174,656 tokens at E = 256), else
  * MOE_ERR_SCRATCH before any launch.  Every call on a GPU shares that GPU's
  * array: calls that overlap on one GPU (other streams or host threads) race

@@ -331,6 +331,7 @@ __global__ void shared_table_kernel(int32_t* tab, int T) {
         tp[0] = 0;
         tp[1] = (T + bm - 1) / bm;
     }
+    tab[2 + 3 * (MOE_MAX_EXPERTS + 1)] = 0;     // segment order: the one segment
 }
 
 // ---- host launchers ------------------------------------------------------------

@@ -14,10 +14,8 @@
 //     with fp32 accumulators; the last m-tile of an expert with at most 128
 //     (64) valid rows puts the 4 wavefronts side by side on 64 columns each,
 //     4 x 2 (2 x 2) MFMA tiles, so that it costs a fraction of a full tile's
-//     MFMA work; the up-projection weight gradient with the SGD step runs
-//     128 x 256 tiles (2 x 4 MFMA tiles a wavefront, a 3-stage ring) with two
-//     workgroups per CU, so that one's SGD epilogue runs under the other's
-//     main loop;
+//     MFMA work (the template also holds a 128-row tile with two workgroups per
+//     CU for the SGD epilogue, which the persistent form below replaced);
 //   * every operand goes straight from global memory into LDS (buffer loads
 //     with an LDS destination, bounds checked by the buffer descriptor so
 //     ragged rows and k tails read as zero) through a ring of 4 LDS stages,
@@ -55,7 +53,14 @@
 //     deals workgroups round-robin to the 8 XCDs; the kernel groups the XCDs
 //     (G per group) and gives each group a contiguous, equal share of the
 //     tiles (in KSEG mode, of each segment's tiles, since a tile's cost there
-//     follows its segment's row count), dealt round-robin among its members.
+//     follows its segment's row count), dealt round-robin among its members;
+//   * the weight gradients with the SGD step run persistent: one workgroup per CU
+//     loops over tiles taken from its XCD group's queue (one integer atomic per
+//     tile), segments with the most rows first;
+//   * gathered operands (fused dispatch): A rows of a row-mode contraction, or the
+//     k-rows of a weight gradient's operand, come from a token-major source
+//     through token_of; a weight gradient's k-row indices reach LDS through a
+//     small ring two k-tiles ahead of the operand loads that use them.
 #include <algorithm>
 
 #include "common.hpp"
@@ -115,6 +120,10 @@ struct GemmParams {
     const float* row_scale;       // EPI_UP_SWIGLU_G / EPI_DN_SWIGLU_G: gate of each expert-major row
     float* dot_part;              // EPI_DN_SWIGLU_G: [N-tiles][rows] partial <dA, A> of each row
     long dot_ld;                  // rows of dot_part per N-tile
+    // persistent weight gradients: one tile counter per XCD group (zeroed before the launch),
+    // and the segments in the order their tiles are handed out (most rows first)
+    int32_t* queue;
+    const int32_t* seg_order;
 };
 // Gathered operands.  GA_ROWS: the K-contiguous A operand of a row-mode contraction is
 // read from rows rows_tok[p] of a token-major source instead of rows p of an expert-major
@@ -337,10 +346,11 @@ __device__ __forceinline__ void grouped(int q, int mt, int nt, int& tm, int& tn)
 // TM: tile rows.  256: one workgroup per CU, a 4-stage ring; 128 (the SGD epilogue of the
 // weight gradients): two workgroups per CU, 128 accumulators a lane and a 3-stage ring,
 // so that one workgroup's epilogue runs under the other's main loop.
-template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256, int GA = GA_NONE>
+template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256, int GA = GA_NONE, bool PER = false>
 __global__ void __launch_bounds__(NTHR, TM == 128 ? 2 : 1)
 __attribute__((amdgpu_waves_per_eu(TM == 128 ? 2 : 1, TM == 128 ? 2 : 1)))
 gemm_bf16_kernel(GemmParams p) {
+    static_assert(!PER || MODE == MODE_KSEG, "persistent: weight gradients");
     static_assert(TM == 256 || (TM == 128 && MODE == MODE_KSEG && EPI == EPI_SGD), "128-row tiles: SGD epilogue");
     static_assert(GA == GA_NONE || (GA == GA_ROWS && MODE == MODE_ROWS && !AT) ||
                   (GA == GA_KA && MODE == MODE_KSEG && AT && TM == 256) ||
@@ -365,8 +375,25 @@ gemm_bf16_kernel(GemmParams p) {
     else if (MODE == MODE_KSEG) nreal = p.E * ((p.M + TM - 1) / TM) * NT;
     else nreal = ((p.M + BM - 1) / BM) * NT * (p.kchunk > 0 ? (p.K + p.kchunk - 1) / p.kchunk : 1);
     nreal = uni(nreal);
+    // The persistent form (PER) takes its tiles from its XCD group's queue instead of its
+    // block index: a grid of one workgroup per resident slot, each looping until the
+    // group's tiles are handed out (an integer atomic per tile; which workgroup computes a
+    // tile does not change its result).  Tickets walk the segments most rows first, so the
+    // longest tiles go first and the short ones fill the tail.
+    __shared__ int s_ticket;
     int L = blockIdx.x;
-    {
+    int ticket = 0, per_total = 0, per_cg = 1, per_s0 = 0, per_tps = 1, per_g = 0;
+    if constexpr (PER) {
+        const int G = p.xcd_group, ng = 8 / G;
+        per_g = uni((int)(blockIdx.x & 7) / G);
+        per_tps = uni(nreal / p.E);
+        per_s0 = (per_g * per_tps) / ng;
+        per_cg = ((per_g + 1) * per_tps) / ng - per_s0;
+        per_total = uni(p.E * per_cg);
+        if (tid == 0) s_ticket = atomicAdd(p.queue + per_g, 1);
+        __syncthreads();
+        ticket = uni(s_ticket);
+    } else {
         // Workgroups are dealt to the 8 XCDs round-robin by blockIdx. The XCDs form 8/G groups
         // of G; each group takes a contiguous, equal share of the tiles (of each segment's
         // tiles, for the weight gradients) and deals it round-robin to its members. G = 8 spreads neighbouring tiles over every L2 (each operand row is
@@ -389,6 +416,14 @@ gemm_bf16_kernel(GemmParams p) {
             if (li >= q + (g < r ? 1 : 0)) return;
             L = g * q + min(g, r) + li;
         }
+    }
+    for (int it = 0;; ++it) {
+    int next = 0;
+    if constexpr (PER) {
+        if (ticket >= per_total) break;                  // uniform: the group's tiles are all out
+        const int seg = p.seg_order[ticket / per_cg];
+        L = seg * per_tps + per_s0 + ticket % per_cg;
+        if (tid == 0) next = atomicAdd(p.queue + per_g, 1);   // awaited after this tile
     }
 
     int e = 0, m0 = 0, n_t = 0;
@@ -727,7 +762,8 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
                 for (int q = 0; q < LPW; ++q) dma(q, t);
             }
-            wait_vm<LPW * (DIST - 1)>();
+            if constexpr (KGATHER) idx_dma(DIST + 1);     // into k-tile 0's slot, now read
+            wait_vm<LPW * (DIST - 1) + (KGATHER ? 1 : 0)>();
             __syncthreads();
             Frags fa, fb;
 #pragma unroll
@@ -738,9 +774,10 @@ gemm_bf16_kernel(GemmParams p) {
                 const bf16* Bs = lds + st * STAGE + TILE_A;
                 const int pf = kt + DIST;
                 if constexpr (KGATHER) {
-                    // the indices of k-tile pf + 1 go out before k-tile pf's operand loads, so
-                    // the wait at the end of this k-tile (all but the last LPW loads) covers them
-                    idx_dma(pf + 1);
+                    // the indices run two k-tiles ahead of the operand loads: k-tile pf + 2's go
+                    // out now, are complete at the end of the next k-tile, and are read in the
+                    // one after (three ring slots: pf being read, pf + 1 pending, pf + 2)
+                    idx_dma(pf + 2);
                     idx_read(pf);
                 }
 #pragma unroll
@@ -768,7 +805,7 @@ gemm_bf16_kernel(GemmParams p) {
                             for (int q = i * PART / h1; q < (i + 1) * PART / h1; ++q) dma(s * PART + q, pf);
                             __builtin_amdgcn_sched_barrier(0);
                         }
-                        wait_vm<LPW * (DIST - 1)>();
+                        wait_vm<LPW * (DIST - 1) + (KGATHER ? 1 : 0)>();
                         wait_lgkm0();
                         __syncthreads();
                         const int sn = (kt + 1) % NSt;
@@ -1158,12 +1195,50 @@ gemm_bf16_kernel(GemmParams p) {
     } else {
         tile(Layout<TM / 64, 4>{});
     }
+    if constexpr (!PER) break;
+    else {
+        __syncthreads();                                 // the epilogue is done with LDS
+        if (tid == 0) s_ticket = next;
+        __syncthreads();
+        ticket = uni(s_ticket);
+    }
+    }   // tiles
 }
 
+
 // ---- host side -------------------------------------------------------------------------------
-template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256, int GA = GA_NONE>
+__global__ void __launch_bounds__(64) zero_queue_kernel(int32_t* q) {
+    if (threadIdx.x < 8) q[threadIdx.x] = 0;
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256, int GA = GA_NONE, bool PER = false>
 static hipError_t run(GemmParams p, int grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
+    if constexpr (PER) {
+        // one workgroup per resident slot (two per CU with 128-row tiles), whole XCD rounds;
+        // the queues start at zero
+        if (p.xcd_group == 0) p.xcd_group = 8;
+        if (p.xcd_group != 1 && p.xcd_group != 2 && p.xcd_group != 4 && p.xcd_group != 8) return hipErrorInvalidValue;
+        if (!p.queue || !p.seg_order) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(zero_queue_kernel, dim3(1), dim3(64), 0, s, p.queue);
+        const int slots = (device_cus() * (TM == 128 ? 2 : 1) + 7) & ~7;
+        hipLaunchKernelGGL((gemm_bf16_kernel<MODE, AT, BT, EPI, OUT_F32, TM, GA, true>), dim3(slots),
+                           dim3(NTHR), 0, s, p);
+        return hipGetLastError();
+    }
     // Whole XCD rounds; surplus workgroups exit at once. A multiple of 8 is a multiple of
     // every group count, so each group's slots cover its share of the tiles.
     if (p.xcd_group == 0) p.xcd_group = 8;
@@ -1271,10 +1346,15 @@ hipError_t mfma_up_dgrad(const ExpertGemmArgs& a, hipStream_t s) {
     return run<MODE_ROWS, false, true, EPI_STORE, false>(p, p.mtiles_ub * ((a.d + BN - 1) / BN), s);
 }
 
+// With the SGD step in the epilogue, the weight gradients run persistent: one workgroup per
+// CU takes its tiles from its XCD group's queue, segments with the most rows first (measured
+// at T = 32768, E = 256: down 11.7 -> 11.25 ms, up 22.9 -> 22.0-22.5 ms against the block-
+// index deal, with the up projection's 128-row tiles at two workgroups per CU).
 hipError_t mfma_down_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     // dW2[e] (d x ffn) = dEO_e^T A_e: A operand = dEO as [k = row][m = c], B = A as [k][n = j]
     GemmParams p = {};
     p.E = a.E; p.offsets = a.offsets; p.b2_kstart = -1; p.ffn = a.ffn;
+    p.queue = a.queue; p.seg_order = a.tile_prefix + 3 * (MOE_MAX_EXPERTS + 1);
     p.A = (const bf16*)a.dEO; p.lda = a.d;
     p.B = (const bf16*)a.A; p.ldb = a.ffn;
     p.M = a.d; p.N = a.ffn;
@@ -1285,13 +1365,13 @@ hipError_t mfma_down_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
         p.A = (const bf16*)a.dY; p.rows_tok = a.token_of; p.src_rows = a.T;
         if (a.W2m) {
             p.C = a.W2m; p.W = a.W2w; p.lr = a.lr;
-            return run<MODE_KSEG, true, true, EPI_SGD, true, 256, GA_KA>(p, grid, s);
+            return run<MODE_KSEG, true, true, EPI_SGD, true, 256, GA_KA, true>(p, grid, s);
         }
         return run<MODE_KSEG, true, true, EPI_STORE, true, 256, GA_KA>(p, grid, s);
     }
     if (a.W2m) {    // SGD step on W2 in place of storing dW2
         p.C = a.W2m; p.W = a.W2w; p.lr = a.lr;
-        return run<MODE_KSEG, true, true, EPI_SGD, true>(p, grid, s);
+        return run<MODE_KSEG, true, true, EPI_SGD, true, 256, GA_NONE, true>(p, grid, s);
     }
     return run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
 }
@@ -1302,29 +1382,27 @@ hipError_t mfma_up_wgrad(const ExpertGemmArgs& a, hipStream_t s) {
     const int hcols = glu ? 2 * a.ffn : a.ffn;
     GemmParams p = {};
     p.E = a.E; p.offsets = a.offsets; p.b2_kstart = -1; p.ffn = a.ffn;
+    p.queue = a.queue; p.seg_order = a.tile_prefix + 3 * (MOE_MAX_EXPERTS + 1);
     p.A = (const bf16*)a.dH; p.lda = hcols;
     p.B = (const bf16*)a.Xp; p.ldb = a.d;
     p.M = hcols; p.N = a.d;
     p.C = a.dW1; p.ldc = a.d; p.ces = (long)a.ffn * a.d;
     if (glu) { p.C2 = a.dW3; p.c2_mstart = a.ffn; }
     const int grid = a.E * ((hcols + BM - 1) / BM) * ((a.d + BN - 1) / BN);
-    const int grid128 = a.E * ((hcols + 127) / 128) * ((a.d + BN - 1) / BN);
     p.xcd_group = 2;
     if (a.token_of) {           // fused dispatch: k-rows of X through token_of
         p.B = (const bf16*)a.X; p.rows_tok = a.token_of; p.src_rows = a.T;
         if (a.W1m) {
             p.C = a.W1m; p.W = a.W1w; p.lr = a.lr;
             if (glu) { p.C2 = a.W3m; p.W2 = a.W3w; }
-            return run<MODE_KSEG, true, true, EPI_SGD, true, 128, GA_KB>(p, grid128, s);
+            return run<MODE_KSEG, true, true, EPI_SGD, true, 256, GA_KB, true>(p, grid, s);
         }
         return run<MODE_KSEG, true, true, EPI_STORE, true, 256, GA_KB>(p, grid, s);
     }
     if (a.W1m) {    // SGD step on W1 (and W3) in place of storing dW1 (dW3)
         p.C = a.W1m; p.W = a.W1w; p.lr = a.lr;
         if (glu) { p.C2 = a.W3m; p.W2 = a.W3w; }
-        // 128-row tiles, two workgroups per CU: one's SGD epilogue runs under the other's
-        // main loop (measured 3-4% faster here; the same for dW2 brought nothing)
-        return run<MODE_KSEG, true, true, EPI_SGD, true, 128>(p, grid128, s);
+        return run<MODE_KSEG, true, true, EPI_SGD, true, 256, GA_NONE, true>(p, grid, s);
     }
     return run<MODE_KSEG, true, true, EPI_STORE, true>(p, grid, s);
 }

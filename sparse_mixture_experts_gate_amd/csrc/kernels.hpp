@@ -32,7 +32,8 @@ struct SlotArgs {
     const int32_t* topk_idx;
     const float* gates;
     int32_t* offsets;      // [E+1]
-    int32_t* tile_prefix;  // [3][MOE_MAX_EXPERTS+1]: m-tile prefix for 64/128/256-row tiles
+    int32_t* tile_prefix;  // [3][MOE_MAX_EXPERTS+1]: m-tile prefix for 64/128/256-row tiles,
+                           // then [MOE_MAX_EXPERTS+1]: the experts by rows, most first
     int32_t* slot_of;      // [T,k]
     int32_t* token_of;     // [T*k]
     float* gate_of;        // [T*k] gate of each expert-major row, or NULL
@@ -146,7 +147,9 @@ enum GemmEpi {
 struct ExpertGemmArgs {
     int T, d, E, ffn, k, rows;       // rows = T*k
     const int32_t* offsets;          // [E+1]
-    const int32_t* tile_prefix;      // [3][MOE_MAX_EXPERTS+1]
+    const int32_t* tile_prefix;      // [3][MOE_MAX_EXPERTS+1] m-tile prefixes, then the
+                                     // experts by rows, most first [MOE_MAX_EXPERTS+1]
+    int32_t* queue;                  // [8] tile counters of the persistent weight gradients
     const void* Xp; const void* W1; const void* W3; const void* b1;
     const void* W2; const void* b2;
     void* H; void* A; void* EO;      // forward outputs / saved

@@ -36,13 +36,14 @@ constexpr int kChunk = 64;
 
 enum WsBuf {
     B_XP = 0, B_H, B_A, B_EO, B_DEO, B_DH, B_DXP, B_DY, B_DXR, B_DL, B_DGATE, B_GATEOF, B_DGPART,
-    B_HIST, B_CBASE, B_QPART, B_LPART, B_TPREFIX, B_DWGPART, B_LOGPART,
+    B_HIST, B_CBASE, B_QPART, B_LPART, B_TPREFIX, B_QUEUE, B_DWGPART, B_LOGPART,
     // shared-experts branch: [H1 | H3] [T, 2 Hs], A [T, Hs], Ys [T, d], dH [T, 2 Hs],
     // dX part [T, d], and its one-segment tables (offsets {0, T}, tile prefixes)
     B_HS, B_AS, B_YS, B_DHS, B_DXS, B_STAB,
     B_COUNT
 };
-constexpr int kSharedTab = 2 + 3 * (MOE_MAX_EXPERTS + 1);   // int32 entries of B_STAB
+constexpr int kTabs = 4 * (MOE_MAX_EXPERTS + 1);            // m-tile prefixes (3) and segment order
+constexpr int kSharedTab = 2 + kTabs;                       // int32 entries of B_STAB
 
 struct Layout {
     size_t off[B_COUNT];
@@ -135,7 +136,8 @@ Layout layout(const moe_config* c) {
     sz[B_CBASE] = E * nc * 4;
     sz[B_QPART] = nc * E * 4;
     sz[B_LPART] = (size_t)combine_loss_blocks(c->T) * 4;
-    sz[B_TPREFIX] = 3 * (MOE_MAX_EXPERTS + 1) * 4;
+    sz[B_TPREFIX] = kTabs * 4;
+    sz[B_QUEUE] = 8 * 4;
     // split-K partials of the router weight gradient (bf16 path only)
     const int nsplit = c->dtype == MOE_DTYPE_F32 ? 0 : router_dwg_splits(c->T);
     sz[B_DWGPART] = nsplit > 1 ? (size_t)nsplit * E * d * 4 : 0;
@@ -282,7 +284,7 @@ void* g_scratch_ptr[kMaxDevices] = {};
 // 64-token chunk, and the tile prefixes (each part 256-byte aligned).
 size_t route_scratch_bytes(const moe_config* c, size_t* off) {
     const size_t ne = (size_t)c->E * (size_t)nchunk(c) * 4;
-    const size_t sz[4] = {ne, ne, ne, (size_t)3 * (MOE_MAX_EXPERTS + 1) * 4};
+    const size_t sz[4] = {ne, ne, ne, (size_t)kTabs * 4};
     size_t o = 0;
     for (int i = 0; i < 4; ++i) {
         if (off) off[i] = o;
@@ -311,6 +313,7 @@ ExpertGemmArgs expert_args(const Ctx& x, const moe_weights* w, const moe_routing
     a.T = c->T; a.d = c->d; a.E = c->E; a.ffn = c->ffn; a.k = c->k; a.rows = c->T * c->k;
     a.offsets = r->offsets;
     a.tile_prefix = x.buf<int32_t>(B_TPREFIX);
+    a.queue = x.buf<int32_t>(B_QUEUE);
     a.Xp = x.buf<void>(B_XP);
     a.W1 = w->W1; a.W3 = w->W3; a.W2 = w->W2;
     a.b1 = c->expert == MOE_EXPERT_SWIGLU ? nullptr : w->b1;
@@ -340,6 +343,7 @@ ExpertGemmArgs shared_args(const Ctx& x, const void* X, const moe_weights* w) {
     a.T = c->T; a.d = c->d; a.E = 1; a.ffn = shared_hidden(c); a.k = 1; a.rows = c->T;
     a.offsets = x.buf<int32_t>(B_STAB);
     a.tile_prefix = x.buf<int32_t>(B_STAB) + 2;
+    a.queue = x.buf<int32_t>(B_QUEUE);
     a.Xp = X;
     a.W1 = w->Ws1; a.W3 = w->Ws3; a.W2 = w->Ws2;
     a.H = x.buf<void>(B_HS); a.A = x.buf<void>(B_AS); a.EO = x.buf<void>(B_YS);

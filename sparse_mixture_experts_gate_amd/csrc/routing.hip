@@ -414,6 +414,26 @@ slot_assign_kernel(SlotArgs a) {
             }
             if (lane == 63) tp[E] = ti;
         }
+        // the experts by rows, most first (ties: smaller id first): the order in which the
+        // persistent weight-gradient contractions hand out their tiles
+        __shared__ int s_cnt[MOE_MAX_EXPERTS];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (lane * 4 + j < E) s_cnt[lane * 4 + j] = c4[j];
+        __syncthreads();
+        int rank[4] = {0, 0, 0, 0};
+        for (int f = 0; f < E; ++f) {
+            const int cf = s_cnt[f];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = lane * 4 + j;
+                rank[j] += (cf > c4[j] || (cf == c4[j] && f < e)) ? 1 : 0;
+            }
+        }
+        int* order = a.tile_prefix + 3 * (MOE_MAX_EXPERTS + 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (lane * 4 + j < E) order[rank[j]] = lane * 4 + j;
     }
     __syncthreads();
     if (!valid) return;

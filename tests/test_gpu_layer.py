@@ -229,8 +229,15 @@ def test_train_step_parity(w):
     train_step_parity(w, _inputs(w), w.name)
 
 
+# skewed routing (Zipf gate rows, a tie block that leaves experts empty): the persistent
+# weight gradients hand out segments of very different lengths, the longest first
+SKEWED_PERSISTENT = wl("bf16_swiglu_skewed_queue", T=3000, d=256, E=32, ffn=320, k=4, dtype="bf16",
+                       expert="swiglu", gate="zipf_tie")
+
 FUSED_CASES = [F32_CASES[0], F32_CASES[2], BF16_CASES[0], BF16_CASES[1], BF16_CASES[2], BF16_CASES[5],
-               VARIANT_CASES[2], SHARED_CASES[0], SHARED_CASES[2], SHARED_CASES[3], LIMIT_CASES[2]]
+               VARIANT_CASES[2], SHARED_CASES[0], SHARED_CASES[2], SHARED_CASES[3], LIMIT_CASES[2],
+               SKEWED_PERSISTENT, SKEWED_PERSISTENT.replace(name="bf16_swiglu_skewed_queue_fd",
+                                                            fused_dispatch=1)]
 
 
 @pytest.mark.parametrize("w", [SHARED_CASES[1], SHARED_CASES[4]], ids=lambda w: w.name)
@@ -269,11 +276,14 @@ def _one_step(w, inp, fused, Wg_override=None):
 
 
 @pytest.mark.parametrize("w", [F32_CASES[2], BF16_CASES[0], BF16_CASES[1], BF16_CASES[5], SHARED_CASES[0],
-                               SHARED_CASES[2]], ids=lambda w: w.name)
+                               SHARED_CASES[2], LIMIT_CASES[2], SKEWED_PERSISTENT],
+                         ids=lambda w: w.name)
 def test_fused_sgd_equals_stored_gradient_step(w):
     """The fused step and the step through stored gradients give bitwise the same
     parameters, outputs and remaining gradients: the gradient is the same float32
-    sum and each element takes the same fused multiply-add."""
+    sum and each element takes the same fused multiply-add.  (In bf16 the fused
+    step's weight gradients run persistent, from per-XCD-group tile queues, and the
+    stored step's do not: equality also shows that every tile was handed out once.)"""
     inp = _inputs(w)
     a = _one_step(w, inp, fused=False)
     b = _one_step(w, inp, fused=True)
