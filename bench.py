@@ -235,6 +235,50 @@ def cpu_baseline(w, inp, max_experts: int = 0):
             "seconds_measured": round(t_all, 2), "seconds_weight_decoding": round(t_fetch[0], 2)}
 
 
+def hbm_probe(gib: float) -> dict:
+    """Bandwidth of plain library (torch) streams on the device, the ceiling the layer's
+    memory-bound kernels are measured against: a copy, a read-only reduction, a
+    write-only fill, and the read/write mixes of the gather (one read, k = 8 writes:
+    a row block expanded to 8 contiguous copies) and of the combine (8 reads, one
+    write: a sum over 8 row blocks), at the largest workload's row shape (d = 7168, bf16).
+    Each is timed with events over 5 runs after one warm-up; bytes count each operand
+    read once and each output written once."""
+    import torch
+    dev = "cuda"
+    n = int(gib * 2**30) // 2                       # bf16 elements
+    d, k = 7168, 8
+    rows = max(1, n // (k * d))
+    x = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+    xf = x.view(torch.float32)
+    src = torch.ones(rows, d, dtype=torch.bfloat16, device=dev)
+    blk = torch.ones(k, rows, d, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(rows, d, dtype=torch.bfloat16, device=dev)
+    cases = {
+        "copy": (lambda: y.copy_(x), 2 * n * 2),
+        "read": (lambda: torch.sum(xf), n * 2),
+        "write": (lambda: y.fill_(1.0), n * 2),
+        "gather_mix_1r_8w": (lambda: src.unsqueeze(0).expand(k, rows, d).contiguous(), (1 + k) * rows * d * 2),
+        "combine_mix_8r_1w": (lambda: torch.sum(blk, dim=0, out=out), (k + 1) * rows * d * 2),
+    }
+    res = {}
+    for name, (fn, nbytes) in cases.items():
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[2]
+        res[name] = {"bytes": nbytes, "ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        print(f"[hbm] {name}: {res[name]}", file=sys.stderr, flush=True)
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +314,9 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps (outside "
                          "the timed region), a known-size reference for hardware byte counters")
+    ap.add_argument("--hbm-probe", type=float, default=0.0,
+                    help="only measure library streams of this many GiB (copy, read, write, and the "
+                         "gather and combine read/write mixes), print them as one JSON line and exit")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print("bench.py runs on one GPU only: this layer is built and measured on a single "
@@ -277,6 +324,11 @@ def main(argv=None) -> int:
         return 2
 
     import torch
+
+    if a.hbm_probe > 0:
+        print(json.dumps({"hbm_probe_gib": a.hbm_probe, "peak_gbs": PEAK_HBM_GBS,
+                          "streams": hbm_probe(a.hbm_probe)}), flush=True)
+        return 0
 
     from sparse_mixture_experts_gate_amd import _lib as L
     from sparse_mixture_experts_gate_amd import workloads as W

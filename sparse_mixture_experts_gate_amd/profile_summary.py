@@ -105,6 +105,9 @@ def _stage_of(name, state):
     if state.get("shared") and "gemm_bf16_kernel<1, true, true" in name and state["wgrad"] in (2, 3):
         state["wgrad"] += 1
         return "shared_bwd"
+    if "zero_queue_kernel" in name:        # clears the tile queues of the next weight gradient
+        n = state["wgrad"]
+        return {0: "down_wgrad", 1: "up_wgrad"}.get(n, "shared_bwd" if state.get("shared") else "router_dwg")
     if any(k in name for k in ("route_topk", "expert_scan", "slot_assign")):
         return "route"
     if "finalize_kernel" in name:
@@ -191,7 +194,9 @@ def markdown(rec, title, command):
              f"{rec['calibration']['write_scale']}.", "",
              "FETCH_SIZE counts L2 misses (served by the MALL or HBM), WRITE_SIZE the L2 write-back traffic.",
              f"SGD mode of the step: {rec.get('sgd', 'stored')} (fused: the expert weight-gradient GEMMs apply "
-             "the SGD step to the expert weights; the sgd stage covers the router weight and biases).", "",
+             "the SGD step to the expert weights; the sgd stage covers the router weight and biases).",
+             f"Dispatch mode: {rec.get('dispatch', 'staged')} (fused: no gather and no combine backward; the "
+             "expert GEMMs read X and dY rows through token_of).", "",
              "| stage | launches | fabric read (GB) | fabric write (GB) | total (GB) | ms (under counters) |",
              "|---|---|---|---|---|---|"]
     for st, e in rec["stages"].items():
@@ -309,9 +314,46 @@ def mfma_markdown(path, title, command):
     return "\n".join(lines) + "\n"
 
 
+def hbm_markdown(probe_json, stats_csv, command):
+    """The library-stream ceiling: bench.py --hbm-probe's event-timed bandwidths, and the
+    rocprofv3 kernel statistics of the same run."""
+    rec = None
+    for line in open(probe_json):
+        line = line.strip()
+        if line.startswith("{") and "streams" in line:
+            rec = json.loads(line)
+    if rec is None:
+        raise SystemExit("no --hbm-probe JSON line found")
+    peak = rec.get("peak_gbs", 8000.0)
+    lines = ["# HBM ceiling: library streams on one MI355X", "", "Command (repository root):", "", "```",
+             command, "```", "",
+             f"{rec['hbm_probe_gib']} GiB streams (bf16), each timed with HIP events over 5 runs (median) after a "
+             "warm-up; bytes count each operand read once and each output written once.  The gather mix "
+             "expands a [rows, 7168] block into 8 contiguous copies (1 read, 8 writes), the combine mix sums "
+             "8 such blocks (8 reads, 1 write).", "",
+             "| stream | bytes (GB) | ms | GB/s | of 8 TB/s |", "|---|---|---|---|---|"]
+    for name, e in rec["streams"].items():
+        lines.append(f"| {name} | {e['bytes'] / 1e9:.3f} | {e['ms']:.4f} | {e['gbs']:.1f} | {e['gbs'] / peak:.3f} |")
+    lines += ["", "Kernel statistics of the same run (rocprofv3 --kernel-trace --stats):", "",
+              "| kernel | calls | average (ms) | min (ms) | max (ms) |", "|---|---|---|---|---|"]
+    for r in csv.DictReader(open(stats_csv)):
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+                     f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} |")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     if argv is None:
         argv = sys.argv[1:]
+    if argv and argv[0] == "--hbm":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("--hbm", required=True, help="the JSON output of bench.py --hbm-probe")
+        ap.add_argument("--stats", required=True)
+        ap.add_argument("--markdown", required=True)
+        ap.add_argument("--command", default="")
+        a = ap.parse_args(argv)
+        open(a.markdown, "w").write(hbm_markdown(a.hbm, a.stats, a.command))
+        return 0
     if argv and argv[0] == "--mfma":
         ap = argparse.ArgumentParser()
         ap.add_argument("--mfma", required=True)
@@ -344,10 +386,13 @@ def main(argv=None):
     ap.add_argument("--command", default="")
     ap.add_argument("--sgd", choices=("fused", "stored"), default="fused",
                     help="the bench.py --sgd mode the counters were taken in")
+    ap.add_argument("--dispatch", choices=("fused", "staged"), default="fused",
+                    help="the dispatch mode of the step the counters were taken in")
     a = ap.parse_args(argv)
     rec = summarize(a.fetch_csv, a.write_csv, a.calibration_mib)
     rec["workload"] = a.workload
     rec["sgd"] = a.sgd
+    rec["dispatch"] = a.dispatch
     rec["command"] = a.command
     if a.json:
         json.dump(rec, open(a.json, "w"), indent=1)
