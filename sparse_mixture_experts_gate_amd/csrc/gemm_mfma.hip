@@ -643,9 +643,17 @@ gemm_bf16_kernel(GemmParams p) {
         constexpr uint32_t OUT = 0x80000000u;          // past every bound
         // element offset of tile row ml (wave-uniform) at this thread's columns in its
         // half, or OUT
-        auto elem = [&](int ml, bool& sec) -> uint32_t {
-            sec = ml >= n1;
-            const int r = sec ? ml - n1 : ml;
+        // mo: the row's offset in the tile less this wavefront's rs.  The row and its half are
+        // worked out afresh at each use (rs and n1 pass through an empty asm): otherwise the
+        // compiler computes all 64 rows' indices and descriptor choices once, for the load two
+        // passes ahead and for the store, and keeps hundreds of copies live in (and spilled
+        // out of) the scalar registers through the whole epilogue.
+        auto elem = [&](int mo, bool& sec) -> uint32_t {
+            int h = n1, w = rs;
+            asm volatile("" : "+s"(h), "+s"(w));
+            const int ml = mo + w;
+            sec = ml >= h;
+            const int r = sec ? ml - h : ml;
             return (ml < rows_valid && col_ok) ? (uint32_t)((long)r * ldc + n) : OUT;
         };
         constexpr int PD = TM == 128 ? 1 : 2;         // passes of masters loaded ahead
@@ -654,7 +662,7 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
                 bool sec;
-                const uint32_t o = elem(q * 32 + it * 4 + rs, sec);
+                const uint32_t o = elem(q * 32 + it * 4, sec);
                 dst[it] = __builtin_bit_cast(nf4, __builtin_amdgcn_raw_buffer_load_b128(
                     sec ? rm2 : rm1, o == OUT ? OUT : o * 4, 0, 2));
             }
@@ -864,7 +872,7 @@ gemm_bf16_kernel(GemmParams p) {
                         const int r = it * 4 + rs;
                         const nf4 gr = *reinterpret_cast<const nf4*>(S + r * 256 + ((qt ^ r) << 2));
                         bool sec;
-                        const uint32_t o = elem(q * 32 + r, sec);
+                        const uint32_t o = elem(q * 32 + it * 4, sec);
                         const nf4 mv = mb[q % (PD + 1)][it];
                         nf4 w;
                         w.x = __builtin_fmaf(nlr, gr.x, mv.x);
