@@ -607,9 +607,13 @@ gemm_bf16_kernel(GemmParams p) {
         constexpr int NR = NI + NJ;                    // fragment reads per k-step
         const int rb = (NJ == 4) ? wm * (NI * 32) : 0;  // first row / column of the wave
         const int cb = (NJ == 4) ? wn * 128 : wave * 64;
+        // fragment read idx of a k-step, in the order the MFMAs use them: a0, then b0 .. b(NJ-1)
+        // (the first row of MFMAs), then a1 .. a(NI-1), so that each MFMA waits only for
+        // the reads it needs and not for the whole step's
         auto read_one = [&](const bf16* As, const bf16* Bs, int ks, Frags& f, int idx) {
-            if (idx < NI) f.a[idx] = AT ? read_strided<TM>(As, rb + idx * 32, ks) : read_contig(As, rb + idx * 32, ks);
-            else f.b[idx - NI] = BT ? read_strided(Bs, cb + (idx - NI) * 32, ks) : read_contig(Bs, cb + (idx - NI) * 32, ks);
+            const int ia = idx == 0 ? 0 : idx - NJ, ib = idx - 1;
+            if (idx == 0 || idx > NJ) f.a[ia] = AT ? read_strided<TM>(As, rb + ia * 32, ks) : read_contig(As, rb + ia * 32, ks);
+            else f.b[ib] = BT ? read_strided(Bs, cb + ib * 32, ks) : read_contig(Bs, cb + ib * 32, ks);
         };
         auto mfma_one = [&](const Frags& f, int i) {
             const int ii = i / NJ, jj = i % NJ;
