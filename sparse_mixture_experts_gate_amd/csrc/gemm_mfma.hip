@@ -957,14 +957,31 @@ gemm_bf16_kernel(GemmParams p) {
                 const int q = c >> 3;
                 store4(stage + r * 256 + ((q ^ (r & 31)) << 3) + (c & 7), v);
             };
-            // store the first ncols staged columns of every valid row to dst(r, c, 16 bytes)
-            auto drain = [&](int ncols, auto dst) {
+            // store the first ncols staged columns of the tile's rows: tile row r goes to
+            // base + r ld, staged column c to column col_of(c) there (-1: nowhere).  One buffer
+            // descriptor bounds the tile's rows, so every store is issued unconditionally (rows
+            // past the tile fall outside it and are dropped), and the LDS reads of eight rows
+            // go out before their stores instead of each store waiting for its own read.
+            auto drain = [&](int ncols, bf16* base, long ld, auto col_of) {
                 const int cpr = ncols / 8;                       // 16-byte chunks per row
                 const int rows_per_it = 256 / cpr;
                 const int q = tid % cpr;
-                for (int r = tid / cpr; r < rows_valid; r += rows_per_it) {
-                    const uint4 x = *reinterpret_cast<const uint4*>(stage + r * 256 + ((q ^ (r & 31)) << 3));
-                    dst(r, q * 8, x);
+                const int col = col_of(q * 8);
+                const rsrc_t rd = make_rsrc(base, (long)rows_valid * ld * 2);
+                const int nit = min(cpr, ((rows_valid + rows_per_it - 1) / rows_per_it + 7) & ~7);
+                for (int i0 = 0; i0 < nit; i0 += 8) {
+                    uint4 x[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int r = (i0 + u) * rows_per_it + tid / cpr;
+                        x[u] = *reinterpret_cast<const uint4*>(stage + r * 256 + ((q ^ (r & 31)) << 3));
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int r = (i0 + u) * rows_per_it + tid / cpr;
+                        const uint32_t off = col >= 0 ? (uint32_t)((r * ld + col) * 2) : OUTB;
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(nu4, x[u]), rd, off, 0, 0);
+                    }
                 }
             };
             if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_BIAS) {
@@ -992,13 +1009,9 @@ gemm_bf16_kernel(GemmParams p) {
                             put(rb + i * 32 + rr, cb + j * 32 + g * 8 + hk * 4, v);
                         }
                 __syncthreads();
-                drain(256, [&](int r, int c, uint4 x) {
-                    const int n = n0 + c;
-                    if (n < p.N) {
-                        const long row = (MODE == MODE_ROWS) ? row_base + m0 + r : (long)(m0 + r);
-                        *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(p.C) + row * p.ldc + n) = x;
-                    }
-                });
+                const long row0 = (MODE == MODE_ROWS) ? row_base + m0 : (long)m0;
+                drain(256, reinterpret_cast<bf16*>(p.C) + row0 * p.ldc + n0, p.ldc,
+                      [&](int c) { return n0 + c < p.N ? c : -1; });
             } else {
                 // tile columns (B rows) alternate 32 W1 rows and the 32 W3 rows of the same
                 // hidden units, so MFMA blocks j and j+1 (j even) pair H1 with H3.
@@ -1028,12 +1041,9 @@ gemm_bf16_kernel(GemmParams p) {
                 }
                 __syncthreads();
                 bf16* H = reinterpret_cast<bf16*>(p.C2);
-                drain(256, [&](int r, int c, uint4 x) {
-                    const int hc = c & 127, hid = hid0 + hc;
-                    if (hid < p.ffn) {
-                        const long row = row_base + m0 + r;
-                        *reinterpret_cast<uint4*>(H + row * (2L * p.ffn) + (c >= 128 ? p.ffn : 0) + hid) = x;
-                    }
+                drain(256, H + (row_base + m0) * (2L * p.ffn) + hid0, 2L * p.ffn, [&](int c) {
+                    const int hc = c & 127;
+                    return hid0 + hc < p.ffn ? (c >= 128 ? p.ffn : 0) + hc : -1;
                 });
                 __syncthreads();
 #pragma unroll
@@ -1051,13 +1061,8 @@ gemm_bf16_kernel(GemmParams p) {
                             put(rb + i * 32 + rr, ((cb + j * 32) >> 6) * 32 + g * 8 + hk * 4, a);
                         }
                 __syncthreads();
-                drain(128, [&](int r, int c, uint4 x) {
-                    const int hid = hid0 + c;
-                    if (hid < p.ffn) {
-                        const long row = row_base + m0 + r;
-                        *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(p.C) + row * (long)p.ffn + hid) = x;
-                    }
-                });
+                drain(128, reinterpret_cast<bf16*>(p.C) + (row_base + m0) * (long)p.ffn + hid0, p.ffn,
+                      [&](int c) { return hid0 + c < p.ffn ? c : -1; });
             }
             return;
         }
