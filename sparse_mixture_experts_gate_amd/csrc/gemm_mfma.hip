@@ -920,25 +920,33 @@ gemm_bf16_kernel(GemmParams p) {
                         }
                 }
                 __syncthreads();
-                const int n = n0 + qt * 4;
-                // the output halves as locals: a per-lane choice between two kernel-argument
-                // fields compiles to a load of the chosen field and a full wait before the store
-                float* const C1 = reinterpret_cast<float*>(p.C);
-                float* const C2 = reinterpret_cast<float*>(p.C2);
-                const int c2 = C2 ? p.c2_mstart : 0x7fffffff;
-#pragma unroll 4
-                for (int it = 0; it < 32; ++it) {
-                    const int r = it * 4 + wave;                   // a wavefront stores whole rows
-                    const int ml = pass * 128 + r;
-                    const float4 x = *reinterpret_cast<const float4*>(stage + r * 256 + ((qt ^ (r & 63)) << 2));
-                    if (ml < rows_valid && n < p.N) {
-                        const float v[4] = {x.x, x.y, x.z, x.w};
-                        const long row = (MODE == MODE_ROWS) ? row_base + m0 + ml : (long)(m0 + ml);
-                        if (MODE == MODE_KSEG) {
-                            const bool sec = row >= c2;
-                            store4((sec ? C2 : C1) + (long)e * p.ces + (sec ? row - c2 : row) * p.ldc + n, v);
-                        } else {       // DENSE split over K: segment e's partial output
-                            store4(C1 + (MODE == MODE_DENSE ? (long)e * p.ces : 0L) + row * p.ldc + n, v);
+                // eight rows' LDS reads go out before their stores; every store is issued
+                // unconditionally through a descriptor bounded to its output rows (weight
+                // gradients: the two halves of the SGD epilogue's rm1 / rm2, chosen per row by
+                // elem), so a row or column outside the tile gets an offset past the bound
+                const rsrc_t rc = make_rsrc(reinterpret_cast<float*>(p.C) + (MODE == MODE_DENSE ? (long)e * p.ces : 0L) +
+                                                ((MODE == MODE_ROWS) ? row_base + m0 : (long)m0) * p.ldc,
+                                            ((long)(rows_valid - 1) * p.ldc + p.N) * 4);
+                for (int it0 = 0; it0 < 32; it0 += 8) {
+                    if (pass * 128 + it0 * 4 >= rows_valid) break;             // uniform
+                    nf4 x[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int r = (it0 + u) * 4 + wave;               // a wavefront stores whole rows
+                        x[u] = *reinterpret_cast<const nf4*>(stage + r * 256 + ((qt ^ (r & 63)) << 2));
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        if constexpr (MODE == MODE_KSEG) {
+                            bool sec;
+                            const uint32_t o = elem(pass * 128 + (it0 + u) * 4, sec);
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(nu4, x[u]), sec ? rm2 : rm1,
+                                                                   o == OUT ? OUT : o * 4, 0, 0);
+                        } else {
+                            const int ml = pass * 128 + (it0 + u) * 4 + wave;
+                            const int n = n0 + qt * 4;
+                            const uint32_t o = (ml < rows_valid && n < p.N) ? (uint32_t)(((long)ml * p.ldc + n) * 4) : OUT;
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(nu4, x[u]), rc, o, 0, 0);
                         }
                     }
                 }
