@@ -18,6 +18,20 @@ namespace moe {
 
 constexpr int TOK_WAVES = 4;    // tokens per 256-thread workgroup
 
+// 16-byte loads of rows that a kernel reads once (the expert rows of a token, its
+// targets, the router-path gradient) carry the nontemporal hint: a plain read stream
+// measured 5.8 TB/s without it and 6.3 TB/s with it on one MI355X.
+typedef unsigned int vu4 __attribute__((ext_vector_type(4)));
+typedef float vf4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_once(const uint4* p) {
+    const vu4 v = __builtin_nontemporal_load(reinterpret_cast<const vu4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 ld_once(const float4* p) {
+    const vf4 v = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ void load_slots(const int32_t* slot_of, int t, int k, int* sl) {
 #pragma unroll
     for (int i = 0; i < MOE_MAX_K; ++i) sl[i] = (i < k) ? slot_of[(size_t)t * k + i] : 0;
@@ -36,7 +50,7 @@ __global__ void __launch_bounds__(256) gather_kernel(GatherArgs a) {
     const uint4* src = reinterpret_cast<const uint4*>(a.X) + (size_t)t * a.vec;
     uint4* dst = reinterpret_cast<uint4*>(a.Xp);
     for (int v = lane; v < a.vec; v += 64) {
-        uint4 x = src[v];
+        uint4 x = ld_once(src + v);
 #pragma unroll
         for (int i = 0; i < MOE_MAX_K; ++i) {
             if (i >= k) break;
@@ -69,21 +83,21 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
             for (int i = 0; i < MOE_MAX_K; ++i) {
                 if (i >= k) break;
                 float x[N];
-                Vec16<T>::unpack(eo[(size_t)sl[i] * a.vec + v], x);
+                Vec16<T>::unpack(ld_once(eo + (size_t)sl[i] * a.vec + v), x);
 #pragma unroll
                 for (int j = 0; j < N; ++j) acc[j] = fmaf(g[i], x[j], acc[j]);
             }
             const size_t o = (size_t)t * a.vec + v;
             if (a.Ys) {                    // shared branch: added with no gate
                 float ys[N];
-                Vec16<T>::unpack(reinterpret_cast<const uint4*>(a.Ys)[o], ys);
+                Vec16<T>::unpack(ld_once(reinterpret_cast<const uint4*>(a.Ys) + o), ys);
 #pragma unroll
                 for (int j = 0; j < N; ++j) acc[j] += ys[j];
             }
             reinterpret_cast<uint4*>(a.Y)[o] = Vec16<T>::pack(acc);
             if (LOSS) {
                 float yt[N], dy[N];
-                Vec16<T>::unpack(reinterpret_cast<const uint4*>(a.Yt)[o], yt);
+                Vec16<T>::unpack(ld_once(reinterpret_cast<const uint4*>(a.Yt) + o), yt);
 #pragma unroll
                 for (int j = 0; j < N; ++j) {
                     float r = acc[j] - yt[j];
@@ -126,13 +140,13 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(CombineBwdArgs a) {
     uint4* deo = reinterpret_cast<uint4*>(a.dEO);
     for (int v = lane; v < a.vec; v += 64) {
         float dy[N];
-        Vec16<T>::unpack(dy4[v], dy);
+        Vec16<T>::unpack(ld_once(dy4 + v), dy);
 #pragma unroll
         for (int i = 0; i < MOE_MAX_K; ++i) {
             if (i >= k) break;
             float x[N], o[N];
             const size_t r = (size_t)sl[i] * a.vec + v;
-            Vec16<T>::unpack(eo[r], x);
+            Vec16<T>::unpack(ld_once(eo + r), x);
 #pragma unroll
             for (int j = 0; j < N; ++j) {
                 dg[i] = fmaf(dy[j], x[j], dg[i]);
@@ -170,14 +184,14 @@ __global__ void __launch_bounds__(256) scatter_kernel(ScatterArgs a) {
 #pragma unroll
         for (int i = 0; i < MOE_MAX_K; ++i) {
             if (i >= k) break;
-            r[0][i] = dxp[(size_t)sl[i] * a.vec + v0];
-            r[1][i] = dxp[(size_t)sl[i] * a.vec + v1];
+            r[0][i] = ld_once(dxp + (size_t)sl[i] * a.vec + v0);
+            r[1][i] = ld_once(dxp + (size_t)sl[i] * a.vec + v1);
         }
         float4 q[2][N / 4];
 #pragma unroll
         for (int h = 0; h < N / 4; ++h) {
-            q[0][h] = reinterpret_cast<const float4*>(dxr + v0 * N)[h];
-            q[1][h] = reinterpret_cast<const float4*>(dxr + v1 * N)[h];
+            q[0][h] = ld_once(reinterpret_cast<const float4*>(dxr + v0 * N) + h);
+            q[1][h] = ld_once(reinterpret_cast<const float4*>(dxr + v1 * N) + h);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -200,7 +214,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(ScatterArgs a) {
             }
             if (a.dXs) {                       // shared branch
                 float xs[N];
-                Vec16<T>::unpack(reinterpret_cast<const uint4*>(a.dXs)[(size_t)t * a.vec + v], xs);
+                Vec16<T>::unpack(ld_once(reinterpret_cast<const uint4*>(a.dXs) + (size_t)t * a.vec + v), xs);
 #pragma unroll
                 for (int j = 0; j < N; ++j) acc[j] += xs[j];
             }
