@@ -29,6 +29,9 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
+SCATTER_FUSED_K = 8            # k at which the bf16 scatter runs inside the router dX contraction
+
+
 def stage_work(w, fused=False):
     """Algorithmic work of each stage: {"flop": n, "byte": n} (either may be 0).
 
@@ -38,7 +41,10 @@ def stage_work(w, fused=False):
     and the SGD stage covers the router weight and the biases only.  With fused
     dispatch (w.fused_dispatch) there is no gather and no combine backward: the
     contractions read the same expert rows straight from X and dY (counted in their
-    own operand bytes, as before) and the down dgrad applies the gates."""
+    own operand bytes, as before) and the down dgrad applies the gates.  With bf16
+    and k = 8 the scatter runs in the router dX contraction's epilogue: that stage
+    reads the k rows of dXp (and the shared part) and writes dX, with no fp32 router
+    part written or read, and the scatter stage is empty."""
     s = 2 if w.dtype == "bf16" else 4
     T, d, E, k, ffn = w.T, w.d, w.E, w.k, w.ffn
     R = T * k
@@ -57,6 +63,9 @@ def stage_work(w, fused=False):
     def by(n):
         return {"flop": 0, "byte": n}
     fd = getattr(w, "fused_dispatch", 0) == 1
+    fs = w.dtype == "bf16" and k == SCATTER_FUSED_K
+    # read k rows of dXp (and the shared part), write dX, read the slots
+    scatter_rows = R * d * s + T * d * s + (T * d * s if hs else 0) + R * 4
     return {
         "router_logits": {"flop": 2.0 * T * d * E, "byte": T * d * s + E * d * s + T * E * 4},
         "route": by(T * E * 4 + T * k * 8 + R * 12),
@@ -90,9 +99,10 @@ def stage_work(w, fused=False):
         "bias_grads": by((R * d + R * ffn) * s if not glu else 0),
         "router_bwd": by(T * E * (4 + s) + T * k * 16),
         "router_dwg": {"flop": 2.0 * T * E * d, "byte": (T * E + T * d) * s + E * d * 4},
-        "router_dx": {"flop": 2.0 * T * E * d, "byte": (T * E + E * d) * s + T * d * 4},
+        "router_dx": {"flop": 2.0 * T * E * d,
+                      "byte": (T * E + E * d) * s + (scatter_rows if fs else T * d * 4)},
         # read k rows of dXp, the fp32 router part (and the shared part), write dX, read slots
-        "scatter": by(R * d * s + T * d * (4 + s) + (T * d * s if hs else 0) + R * 4),
+        "scatter": by(0 if fs else scatter_rows + T * d * 4),
         # master read + write, gradient read, working copy write
         "sgd": by(sgd_params * (4 + 4 + 4 + s)),
     }

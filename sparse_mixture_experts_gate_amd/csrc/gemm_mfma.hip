@@ -120,6 +120,9 @@ struct GemmParams {
     const float* row_scale;       // EPI_UP_SWIGLU_G / EPI_DN_SWIGLU_G: gate of each expert-major row
     float* dot_part;              // EPI_DN_SWIGLU_G: [N-tiles][rows] partial <dA, A> of each row
     long dot_ld;                  // rows of dot_part per N-tile
+    // EPI_SCATTER: the expert-major rows of dX (slot_of[t k + i] is token t's i-th), and the
+    // shared branch's part [T, d] or NULL
+    const bf16* scat_rows; const int32_t* scat_slot; const bf16* scat_shared;
     // persistent weight gradients: one tile counter per XCD group (zeroed before the launch),
     // and the segments in the order their tiles are handed out (most rows first)
     int32_t* queue;
@@ -365,7 +368,9 @@ gemm_bf16_kernel(GemmParams p) {
     // KGATHER: after the stages, a ring of NSt slots of k-row token indices, 256 bytes per
     // wavefront (its 8 k-rows of a k-tile, in the order it reads them)
     constexpr int IDX_ELEMS = KGATHER ? NSt * 512 : 0;
-    __shared__ __attribute__((aligned(1024))) bf16 lds[NSt * STAGE + IDX_ELEMS];
+    // EPI_SCATTER: after the stages, the slots of the tile's 256 rows (8 KB)
+    constexpr int SCAT_ELEMS = EPI == EPI_SCATTER ? 256 * MOE_SCATTER_FUSED_K * 2 : 0;
+    __shared__ __attribute__((aligned(1024))) bf16 lds[NSt * STAGE + IDX_ELEMS + SCAT_ELEMS];
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
@@ -893,6 +898,110 @@ gemm_bf16_kernel(GemmParams p) {
                     }
                 }
             }
+            return;
+        }
+        if constexpr (EPI == EPI_SCATTER) {
+            // Router dX joined with the scatter: each token's dX is the sum of its k expert
+            // rows of dXp (in pick order), then this tile's fp32 accumulator (dl Wg), then
+            // the shared branch's part, in fp32, rounded once to bf16 -- the scatter kernel's
+            // order, so dX is bitwise what router dX + scatter write.  The tile goes out in
+            // two passes of 128 rows staged in LDS as fp32 (1 KB rows, 16-byte chunk q of
+            // row r at q ^ (r & 63)); a thread then owns one 16-byte output vector (8
+            // columns) of a row, and four rows' loads go out before their sums.
+            static_assert(MODE == MODE_DENSE && !OUT_F32 && NI == 4 && NJ == 4, "scatter epilogue: router dX");
+            constexpr int KS = MOE_SCATTER_FUSED_K;
+            float* stage = reinterpret_cast<float*>(lds);
+            int32_t* sslot = reinterpret_cast<int32_t*>(lds + NSt * STAGE + IDX_ELEMS);
+            {   // thread r brings row r's slots (rows past the tile get slot 0: a valid row)
+                nu4 s0 = {0u, 0u, 0u, 0u}, s1 = {0u, 0u, 0u, 0u};
+                if (tid < rows_valid) {
+                    const nu4* src = reinterpret_cast<const nu4*>(p.scat_slot + (long)(m0 + tid) * KS);
+                    s0 = src[0]; s1 = src[1];
+                }
+                reinterpret_cast<nu4*>(sslot)[2 * tid] = s0;
+                reinterpret_cast<nu4*>(sslot)[2 * tid + 1] = s1;
+            }
+            __syncthreads();                                   // every wave is past its last LDS read
+            const int c = tid & 31;                            // the thread's output vector
+            const bool col_ok = n0 + 8 * c < p.N;
+            const long col = col_ok ? n0 + 8 * c : p.N - 8;    // loads stay inside the row
+            const long ld = p.ldc;
+            const rsrc_t rx = make_rsrc(reinterpret_cast<bf16*>(p.C) + (long)m0 * ld,
+                                        ((long)(rows_valid - 1) * ld + p.N) * 2);
+            const bf16* const rows = p.scat_rows;
+            const bf16* const shared = p.scat_shared;
+            auto body = [&](auto has_shared) {
+                constexpr bool SH = decltype(has_shared)::value;
+                for (int pass = 0; pass < 2; ++pass) {
+                    if (pass * 128 >= rows_valid) break;       // uniform
+#pragma unroll
+                    for (int i = 0; i < NI; ++i) {
+                        const int r = rb + i * 32 + rr - pass * 128;
+                        if ((rb + i * 32) / 128 != pass) continue;   // wave-uniform
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                const int q = (cb + j * 32 + g * 8 + hk * 4) >> 2;
+                                *reinterpret_cast<nf4*>(stage + r * 256 + ((q ^ (r & 63)) << 2)) =
+                                    nf4{acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                                        acc[i][j][g * 4 + 3]};
+                            }
+                    }
+                    __syncthreads();
+                    for (int it0 = 0; it0 < 16; it0 += 4) {
+                        if (pass * 128 + it0 * 8 >= rows_valid) break;         // uniform
+                        nu4 x[4][KS], xs[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int rt = pass * 128 + (it0 + u) * 8 + (tid >> 5);   // row in the tile
+                            const nu4 sa = *reinterpret_cast<const nu4*>(sslot + rt * KS);
+                            const nu4 sb = *reinterpret_cast<const nu4*>(sslot + rt * KS + 4);
+#pragma unroll
+                            for (int q = 0; q < KS; ++q) {
+                                const uint32_t sl = q < 4 ? sa[q] : sb[q - 4];
+                                x[u][q] = __builtin_nontemporal_load(
+                                    reinterpret_cast<const nu4*>(rows + (long)sl * ld + col));
+                            }
+                            if constexpr (SH) {
+                                const int rl = min(rt, rows_valid - 1);
+                                xs[u] = __builtin_nontemporal_load(
+                                    reinterpret_cast<const nu4*>(shared + (long)(m0 + rl) * ld + col));
+                            }
+                        }
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int r = (it0 + u) * 8 + (tid >> 5);          // row in the pass
+                            const int rt = pass * 128 + r;
+                            float a8[8];
+#pragma unroll
+                            for (int v = 0; v < 8; ++v) a8[v] = 0.f;
+#pragma unroll
+                            for (int q = 0; q < KS; ++q) {
+                                float f[8];
+                                unpack8(x[u][q], f);
+#pragma unroll
+                                for (int v = 0; v < 8; ++v) a8[v] += f[v];
+                            }
+                            const nf4 g0 = *reinterpret_cast<const nf4*>(stage + r * 256 + (((2 * c) ^ (r & 63)) << 2));
+                            const nf4 g1 = *reinterpret_cast<const nf4*>(stage + r * 256 + (((2 * c + 1) ^ (r & 63)) << 2));
+                            a8[0] += g0.x; a8[1] += g0.y; a8[2] += g0.z; a8[3] += g0.w;
+                            a8[4] += g1.x; a8[5] += g1.y; a8[6] += g1.z; a8[7] += g1.w;
+                            if constexpr (SH) {
+                                float f[8];
+                                unpack8(xs[u], f);
+#pragma unroll
+                                for (int v = 0; v < 8; ++v) a8[v] += f[v];
+                            }
+                            const uint32_t o = (rt < rows_valid && col_ok) ? (uint32_t)(((long)rt * ld + n0 + 8 * c) * 2) : OUTB;
+                            __builtin_amdgcn_raw_buffer_store_b128(pack8(a8), rx, o, 0, 0);
+                        }
+                    }
+                    __syncthreads();                           // the pass's rows are read
+                }
+            };
+            if (shared) body(std::true_type{});
+            else body(std::false_type{});
             return;
         }
         if constexpr (EPI == EPI_STORE && OUT_F32) {
@@ -1483,6 +1592,20 @@ hipError_t mfma_router_dx(const RouterGemmArgs& a, hipStream_t s) {
     p.C = a.dXr; p.ldc = a.d;
     const int grid = ((a.T + BM - 1) / BM) * ((a.d + BN - 1) / BN);
     return run<MODE_DENSE, false, true, EPI_STORE, true>(p, grid, s);
+}
+
+hipError_t mfma_router_dx_scatter(const RouterGemmArgs& a, const ScatterArgs& sa, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    if (sa.k != MOE_SCATTER_FUSED_K || sa.T != a.T || a.d % 8 != 0) return hipErrorInvalidValue;
+    GemmParams p = {};
+    p.b2_kstart = -1;
+    p.A = (const bf16*)a.dl; p.lda = a.E;
+    p.B = (const bf16*)a.Wg; p.ldb = a.d;        // B[k = e][n = c]
+    p.M = a.T; p.N = a.d; p.K = a.E;
+    p.C = sa.dX; p.ldc = a.d;
+    p.scat_rows = (const bf16*)sa.dXp; p.scat_slot = sa.slot_of; p.scat_shared = (const bf16*)sa.dXs;
+    const int grid = ((a.T + BM - 1) / BM) * ((a.d + BN - 1) / BN);
+    return run<MODE_DENSE, false, true, EPI_SCATTER, false>(p, grid, s);
 }
 
 // dWg (E x d) = dl^T X over K = T tokens.  With a partial buffer the T rows are

@@ -141,6 +141,8 @@ enum GemmEpi {
     EPI_UP_SWIGLU_G = 9,   // EPI_UP_SWIGLU with A scaled by the gate of its row
     EPI_DN_SWIGLU_G = 10,  // EPI_DN_SWIGLU from dA = gate * acc, plus the row partials
                            // of <acc, silu(H1) * H3> (the gate gradient)
+    EPI_SCATTER = 11,      // router dX: bf16 dX = sum of the token's k expert rows + acc
+                           // (+ the shared branch's part), the scatter's order and rounding
 };
 
 // Expert contractions of the layer.  All row-major; see each field.
@@ -207,6 +209,10 @@ hipError_t simple_router_dx(const RouterGemmArgs& a, hipStream_t s);
 hipError_t simple_router_dwg(const RouterGemmArgs& a, hipStream_t s);
 hipError_t mfma_router_logits(const RouterGemmArgs& a, hipStream_t s);
 hipError_t mfma_router_dx(const RouterGemmArgs& a, hipStream_t s);
+// The router dX contraction with the scatter in its epilogue (bf16, k = MOE_SCATTER_FUSED_K):
+// writes sa.dX = sum over the token's k rows of sa.dXp + dl Wg (+ sa.dXs) and no dXr.
+constexpr int MOE_SCATTER_FUSED_K = 8;
+hipError_t mfma_router_dx_scatter(const RouterGemmArgs& a, const ScatterArgs& sa, hipStream_t s);
 hipError_t mfma_router_dwg(const RouterGemmArgs& a, hipStream_t s);
 
 }  // namespace moe

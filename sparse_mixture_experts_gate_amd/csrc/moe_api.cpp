@@ -470,9 +470,15 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
     TRY(x.mark(MOE_STAGE_ROUTER_DWG));
     TRY(f32 ? simple_router_dwg(rg, x.s) : mfma_router_dwg(rg, x.s));
     TRY(x.mark(MOE_STAGE_ROUTER_DX));
-    TRY(f32 ? simple_router_dx(rg, x.s) : mfma_router_dx(rg, x.s));
     ScatterArgs sa = {x.buf<void>(B_DXP), r->slot_of, x.buf<float>(B_DXR), g->dX,
                       shared ? x.buf<void>(B_DXS) : nullptr, c->T, c->k, vec};
+    if (!f32 && c->k == MOE_SCATTER_FUSED_K) {
+        // the scatter runs in the router dX contraction's epilogue (same sums, same order)
+        TRY(mfma_router_dx_scatter(rg, sa, x.s));
+        TRY(x.mark(MOE_STAGE_SCATTER));
+        return MOE_OK;
+    }
+    TRY(f32 ? simple_router_dx(rg, x.s) : mfma_router_dx(rg, x.s));
     TRY(x.mark(MOE_STAGE_SCATTER));
     TRY(launch_scatter(sa, c->dtype, x.s));
     return MOE_OK;

@@ -83,6 +83,11 @@ LIMIT_CASES = [
        dtype="bf16", expert="swiglu", score="sigmoid"),
     wl("bf16_gelu_k6_groups", T=300, d=192, E=16, ffn=256, k=6, n_groups=8, topk_groups=4,
        dtype="bf16", expert="gelu", score="sigmoid"),
+    # k = 8: the router dX contraction with the scatter in its epilogue, over a ragged last row
+    # tile and column tile, with and without the shared branch's part
+    wl("bf16_swiglu_k8_shared_ragged", T=700, d=320, E=16, ffn=192, k=8, dtype="bf16", expert="swiglu",
+       n_shared=1),
+    wl("bf16_gelu_k8_ragged", T=333, d=192, E=16, ffn=256, k=8, dtype="bf16", expert="gelu"),
     # router logits split over K into segments of 320, 320 and 192 columns (a ragged last one)
     wl("bf16_swiglu_router_ragged_split", T=300, d=832, E=8, ffn=128, k=2, dtype="bf16",
        expert="swiglu"),
