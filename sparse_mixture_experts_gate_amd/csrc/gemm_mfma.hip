@@ -345,91 +345,42 @@ __device__ __forceinline__ void grouped(int q, int mt, int nt, int& tm, int& tn)
     tm = rem / gsz;
     tn = ng * gn + (rem - tm * gsz);
 }
+// Shared memory of one tile: the ring of operand stages, then (gathered k-rows) the ring of
+// their token indices, then (scatter epilogue) the slots of the tile's rows.
+template <int EPI, int TM, int GA>
+struct TileLds {
+    static constexpr bool KGATHER = GA == GA_KA || GA == GA_KB;
+    static constexpr int NSt = TM == 128 ? 3 : NS;
+    static constexpr int TILE_A = TM * BK, STAGE = TILE_A + TILE_ELEMS;
+    // KGATHER: after the stages, a ring of NSt slots of k-row token indices, 256 bytes per
+    // wavefront (its 8 k-rows of a k-tile, in the order it reads them)
+    static constexpr int IDX_ELEMS = KGATHER ? NSt * 512 : 0;
+    // EPI_SCATTER: after the stages, the slots of the tile's 256 rows (8 KB)
+    static constexpr int SCAT_ELEMS = EPI == EPI_SCATTER ? 256 * MOE_SCATTER_FUSED_K * 2 : 0;
+    static constexpr int ELEMS = NSt * STAGE + IDX_ELEMS + SCAT_ELEMS;
+};
 
-// TM: tile rows.  256: one workgroup per CU, a 4-stage ring; 128 (the SGD epilogue of the
-// weight gradients): two workgroups per CU, 128 accumulators a lane and a 3-stage ring,
-// so that one workgroup's epilogue runs under the other's main loop.
-template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256, int GA = GA_NONE, bool PER = false>
-__global__ void __launch_bounds__(NTHR, TM == 128 ? 2 : 1)
-__attribute__((amdgpu_waves_per_eu(TM == 128 ? 2 : 1, TM == 128 ? 2 : 1)))
-gemm_bf16_kernel(GemmParams p) {
-    static_assert(!PER || MODE == MODE_KSEG, "persistent: weight gradients");
+// One output tile L of a contraction (L indexes the contraction's tiles as the schedule
+// below lays them out), from its k-loop to its epilogue, with the workgroup's shared
+// memory at lds (TileLds<EPI, TM, GA>::ELEMS elements).  TM: tile rows.  256: one
+// workgroup per CU, a 4-stage ring; 128 (the SGD epilogue of the weight gradients): two
+// workgroups per CU, 128 accumulators a lane and a 3-stage ring.
+template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256, int GA = GA_NONE>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int L, bf16* lds) {
     static_assert(TM == 256 || (TM == 128 && MODE == MODE_KSEG && EPI == EPI_SGD), "128-row tiles: SGD epilogue");
     static_assert(GA == GA_NONE || (GA == GA_ROWS && MODE == MODE_ROWS && !AT) ||
                   (GA == GA_KA && MODE == MODE_KSEG && AT && TM == 256) ||
                   (GA == GA_KB && MODE == MODE_KSEG && BT), "gathered operand");
-    constexpr bool KGATHER = GA == GA_KA || GA == GA_KB;
+    using S = TileLds<EPI, TM, GA>;
+    constexpr bool KGATHER = S::KGATHER;
 #ifdef MOE_GEMM_KT64
     static_assert(!KGATHER, "k-row gathers run in the 32-deep build");
 #endif
-    constexpr int NSt = TM == 128 ? 3 : NS;
-    constexpr int TILE_A = TM * BK, STAGE = TILE_A + TILE_ELEMS;
+    constexpr int NSt = S::NSt, TILE_A = S::TILE_A, STAGE = S::STAGE, IDX_ELEMS = S::IDX_ELEMS;
     static_assert(DIST <= NSt - 1, "prefetch distance");
-    // KGATHER: after the stages, a ring of NSt slots of k-row token indices, 256 bytes per
-    // wavefront (its 8 k-rows of a k-tile, in the order it reads them)
-    constexpr int IDX_ELEMS = KGATHER ? NSt * 512 : 0;
-    // EPI_SCATTER: after the stages, the slots of the tile's 256 rows (8 KB)
-    constexpr int SCAT_ELEMS = EPI == EPI_SCATTER ? 256 * MOE_SCATTER_FUSED_K * 2 : 0;
-    __shared__ __attribute__((aligned(1024))) bf16 lds[NSt * STAGE + IDX_ELEMS + SCAT_ELEMS];
     const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-
     const int NT = p.paired ? (p.ffn + 127) / 128 : (p.N + BN - 1) / BN;
-    int nreal;
-    if (MODE == MODE_ROWS) nreal = p.tile_prefix[p.E] * NT;
-    else if (MODE == MODE_KSEG) nreal = p.E * ((p.M + TM - 1) / TM) * NT;
-    else nreal = ((p.M + BM - 1) / BM) * NT * (p.kchunk > 0 ? (p.K + p.kchunk - 1) / p.kchunk : 1);
-    nreal = uni(nreal);
-    // The persistent form (PER) takes its tiles from its XCD group's queue instead of its
-    // block index: a grid of one workgroup per resident slot, each looping until the
-    // group's tiles are handed out (an integer atomic per tile; which workgroup computes a
-    // tile does not change its result).  Tickets walk the segments most rows first, so the
-    // longest tiles go first and the short ones fill the tail.
-    __shared__ int s_ticket;
-    int L = blockIdx.x;
-    int ticket = 0, per_total = 0, per_cg = 1, per_s0 = 0, per_tps = 1, per_g = 0;
-    if constexpr (PER) {
-        const int G = p.xcd_group, ng = 8 / G;
-        per_g = uni((int)(blockIdx.x & 7) / G);
-        per_tps = uni(nreal / p.E);
-        per_s0 = (per_g * per_tps) / ng;
-        per_cg = ((per_g + 1) * per_tps) / ng - per_s0;
-        per_total = uni(p.E * per_cg);
-        if (tid == 0) s_ticket = atomicAdd(p.queue + per_g, 1);
-        __syncthreads();
-        ticket = uni(s_ticket);
-    } else {
-        // Workgroups are dealt to the 8 XCDs round-robin by blockIdx. The XCDs form 8/G groups
-        // of G; each group takes a contiguous, equal share of the tiles (of each segment's
-        // tiles, for the weight gradients) and deals it round-robin to its members. G = 8 spreads neighbouring tiles over every L2 (each operand row is
-        // fetched into all of them); G = 1 keeps them on one XCD (least fabric traffic, but the
-        // requests of the co-resident tiles crowd one L2).
-        const int G = p.xcd_group;
-        const int x = L & 7, i = L >> 3, g = x / G, u = x - g * G, ng = 8 / G;
-        const int li = i * G + u;
-        if (MODE == MODE_KSEG) {
-            // A weight-gradient tile costs in proportion to its segment's rows (K), so equal
-            // tile counts per group are not equal work once the routing is skewed: every
-            // group takes the same contiguous share of each segment's tiles instead.
-            const int tps = uni(nreal / p.E);
-            const int s0 = (g * tps) / ng, cg = ((g + 1) * tps) / ng - s0;
-            if (cg == 0 || li >= p.E * cg) return;
-            const int seg = li / cg;
-            L = seg * tps + s0 + (li - seg * cg);
-        } else {
-            const int q = nreal / ng, r = nreal - q * ng;
-            if (li >= q + (g < r ? 1 : 0)) return;
-            L = g * q + min(g, r) + li;
-        }
-    }
-    for (int it = 0;; ++it) {
-    int next = 0;
-    if constexpr (PER) {
-        if (ticket >= per_total) break;                  // uniform: the group's tiles are all out
-        const int seg = p.seg_order[ticket / per_cg];
-        L = seg * per_tps + per_s0 + ticket % per_cg;
-        if (tid == 0) next = atomicAdd(p.queue + per_g, 1);   // awaited after this tile
-    }
 
     int e = 0, m0 = 0, n_t = 0;
     long row_base = 0;
@@ -1329,14 +1280,81 @@ gemm_bf16_kernel(GemmParams p) {
     } else {
         tile(Layout<TM / 64, 4>{});
     }
-    if constexpr (!PER) break;
-    else {
-        __syncthreads();                                 // the epilogue is done with LDS
-        if (tid == 0) s_ticket = next;
+}
+
+template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256, int GA = GA_NONE, bool PER = false>
+__global__ void __launch_bounds__(NTHR, TM == 128 ? 2 : 1)
+__attribute__((amdgpu_waves_per_eu(TM == 128 ? 2 : 1, TM == 128 ? 2 : 1)))
+gemm_bf16_kernel(GemmParams p) {
+    static_assert(!PER || MODE == MODE_KSEG, "persistent: weight gradients");
+    __shared__ __attribute__((aligned(1024))) bf16 lds[TileLds<EPI, TM, GA>::ELEMS];
+    const int tid = threadIdx.x;
+    const int NT = p.paired ? (p.ffn + 127) / 128 : (p.N + BN - 1) / BN;
+
+    int nreal;
+    if (MODE == MODE_ROWS) nreal = p.tile_prefix[p.E] * NT;
+    else if (MODE == MODE_KSEG) nreal = p.E * ((p.M + TM - 1) / TM) * NT;
+    else nreal = ((p.M + BM - 1) / BM) * NT * (p.kchunk > 0 ? (p.K + p.kchunk - 1) / p.kchunk : 1);
+    nreal = uni(nreal);
+    // The persistent form (PER) takes its tiles from its XCD group's queue instead of its
+    // block index: a grid of one workgroup per resident slot, each looping until the
+    // group's tiles are handed out (an integer atomic per tile; which workgroup computes a
+    // tile does not change its result).  Tickets walk the segments most rows first, so the
+    // longest tiles go first and the short ones fill the tail.
+    __shared__ int s_ticket;
+    int L = blockIdx.x;
+    int ticket = 0, per_total = 0, per_cg = 1, per_s0 = 0, per_tps = 1, per_g = 0;
+    if constexpr (PER) {
+        const int G = p.xcd_group, ng = 8 / G;
+        per_g = uni((int)(blockIdx.x & 7) / G);
+        per_tps = uni(nreal / p.E);
+        per_s0 = (per_g * per_tps) / ng;
+        per_cg = ((per_g + 1) * per_tps) / ng - per_s0;
+        per_total = uni(p.E * per_cg);
+        if (tid == 0) s_ticket = atomicAdd(p.queue + per_g, 1);
         __syncthreads();
         ticket = uni(s_ticket);
+    } else {
+        // Workgroups are dealt to the 8 XCDs round-robin by blockIdx. The XCDs form 8/G groups
+        // of G; each group takes a contiguous, equal share of the tiles (of each segment's
+        // tiles, for the weight gradients) and deals it round-robin to its members. G = 8 spreads neighbouring tiles over every L2 (each operand row is
+        // fetched into all of them); G = 1 keeps them on one XCD (least fabric traffic, but the
+        // requests of the co-resident tiles crowd one L2).
+        const int G = p.xcd_group;
+        const int x = L & 7, i = L >> 3, g = x / G, u = x - g * G, ng = 8 / G;
+        const int li = i * G + u;
+        if (MODE == MODE_KSEG) {
+            // A weight-gradient tile costs in proportion to its segment's rows (K), so equal
+            // tile counts per group are not equal work once the routing is skewed: every
+            // group takes the same contiguous share of each segment's tiles instead.
+            const int tps = uni(nreal / p.E);
+            const int s0 = (g * tps) / ng, cg = ((g + 1) * tps) / ng - s0;
+            if (cg == 0 || li >= p.E * cg) return;
+            const int seg = li / cg;
+            L = seg * tps + s0 + (li - seg * cg);
+        } else {
+            const int q = nreal / ng, r = nreal - q * ng;
+            if (li >= q + (g < r ? 1 : 0)) return;
+            L = g * q + min(g, r) + li;
+        }
     }
-    }   // tiles
+    for (;;) {
+        int next = 0;
+        if constexpr (PER) {
+            if (ticket >= per_total) break;                  // uniform: the group's tiles are all out
+            const int seg = p.seg_order[ticket / per_cg];
+            L = seg * per_tps + per_s0 + ticket % per_cg;
+            if (tid == 0) next = atomicAdd(p.queue + per_g, 1);   // awaited after this tile
+        }
+        gemm_tile<MODE, AT, BT, EPI, OUT_F32, TM, GA>(p, L, lds);
+        if constexpr (!PER) break;
+        else {
+            __syncthreads();                                 // the epilogue is done with LDS
+            if (tid == 0) s_ticket = next;
+            __syncthreads();
+            ticket = uni(s_ticket);
+        }
+    }
 }
 
 
