@@ -8,7 +8,13 @@ float32 layer and (2e-2, 1e-2) for the bfloat16 layer:
     gradients, which carry the MSE factor 2/(T d) and can be as small as 1e-8,
     get a meaningful bound; for a tensor of range ~1 it is the plain atol);
   * the whole tensor:  ||gpu - ref||_2 <= atol * ||ref||_2
-    (catches a systematic error that the elementwise bound could hide).
+    (catches a systematic error that the elementwise bound could hide);
+  * the bulk of the tensor: at most 0.5% of the elements may exceed
+    rtol * |ref| + atol * rms(ref), the absolute part in units of the tensor's
+    RMS.  Every element cannot be held to that: bf16 storage of the layer's
+    intermediates (unit roundoff 2^-9) puts the largest of ~10^5-10^8 errors at
+    1-1.5% of the RMS; over the whole GPU suite at most 0.12% of a tensor's
+    elements lie outside it.
 
 Routing, two checks (top-k is a discrete function of the logits):
   * exact: the oracle's selection run on the GPU's own fp32 logits must give the
@@ -39,6 +45,7 @@ from sparse_mixture_experts_gate_amd import workloads as W
 TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-2)}
 EPS = {"f32": 1e-5, "bf16": 2e-4}     # logit ambiguity band, see module docstring
 DEV = "cuda"
+RMS_RULE_MAX_OUT = 5e-3   # see the module docstring
 
 
 def say(*a):
@@ -72,6 +79,11 @@ def assert_close(name, got, ref, rtol, atol, extra_abs=0.0):
     nerr = float(np.linalg.norm(got - ref - np.clip(got - ref, -extra_abs, extra_abs)))
     if nerr > atol * nref:
         raise AssertionError(f"{name}: normwise error {nerr / max(nref, 1e-300):.3g} > {atol}")
+    rms = nref / math.sqrt(ref.size)
+    out_rms = float(np.mean(err > rtol * np.abs(ref) + atol * rms + extra_abs))
+    if out_rms > RMS_RULE_MAX_OUT:
+        raise AssertionError(f"{name}: {out_rms:.3g} of the elements outside rtol |ref| + atol rms(ref) "
+                             f"(at most {RMS_RULE_MAX_OUT})")
 
 
 def shape_of(w) -> O.Shape:
