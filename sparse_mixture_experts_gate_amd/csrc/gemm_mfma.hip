@@ -1640,13 +1640,23 @@ __global__ void __launch_bounds__(256) sum_partials_kernel(const float* part, fl
     reinterpret_cast<float4*>(out)[i] = acc;
 }
 
-int router_dwg_splits(int T) {
-    int s = T / 2048;                     // each chunk keeps at least 2048 rows
-    return s < 1 ? 1 : (s > 16 ? 16 : s);
+// dWg's K = T is split into chunks of whole k-tiles until its E x d output tiles about fill
+// the 256 CUs in one round (E = 8, d = 1024 gives 4 tiles: a single K = T tile each would leave
+// the chip idle), keeping at least 128 rows (four k-tiles) a chunk and at most 64 chunks.
+int router_dwg_kchunk(int T, int E, int d) {
+    const int tiles = ((E + BM - 1) / BM) * ((d + BN - 1) / BN);
+    int s = std::max(1, 256 / std::max(tiles, 1));
+    s = std::min(s, std::min(64, T / 128));
+    if (s <= 1) return 0;
+    return ((T + s - 1) / s + BK - 1) / BK * BK;
+}
+int router_dwg_splits(int T, int E, int d) {
+    const int kc = router_dwg_kchunk(T, E, d);
+    return kc > 0 ? (T + kc - 1) / kc : 1;
 }
 
 hipError_t mfma_router_dwg(const RouterGemmArgs& a, hipStream_t s) {
-    const int nsplit = a.dwg_part ? router_dwg_splits(a.T) : 1;
+    const int nsplit = a.dwg_part ? router_dwg_splits(a.T, a.E, a.d) : 1;
     GemmParams p = {};
     p.b2_kstart = -1;
     p.A = (const bf16*)a.dl; p.lda = a.E;
@@ -1655,7 +1665,7 @@ hipError_t mfma_router_dwg(const RouterGemmArgs& a, hipStream_t s) {
     p.ldc = a.d;
     p.E = nsplit;
     if (nsplit > 1) {
-        p.kchunk = ((a.T + nsplit - 1) / nsplit + BK - 1) / BK * BK;
+        p.kchunk = router_dwg_kchunk(a.T, a.E, a.d);
         p.C = a.dwg_part; p.ces = (long)a.E * a.d;
     } else {
         p.C = a.dWg; p.ces = 0;

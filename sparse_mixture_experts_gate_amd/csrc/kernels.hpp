@@ -199,10 +199,11 @@ struct RouterGemmArgs {
     int T, d, E;
     const void* X; const void* Wg; const void* dl;
     float* logits; float* dXr; float* dWg;
-    float* dwg_part;       // bf16 path: router_dwg_splits(T) x [E,d] fp32 partials, or NULL
+    float* dwg_part;       // bf16 path: router_dwg_splits(T, E, d) x [E,d] fp32 partials, or NULL
     float* logit_part;     // bf16 path: router_logit_splits(T, E, d) x [T,E] fp32 partials, or NULL
 };
-int router_dwg_splits(int T);
+int router_dwg_splits(int T, int E, int d);
+int router_dwg_kchunk(int T, int E, int d);
 int router_logit_splits(int T, int E, int d);
 hipError_t simple_router_logits(const RouterGemmArgs& a, hipStream_t s);
 hipError_t simple_router_dx(const RouterGemmArgs& a, hipStream_t s);

@@ -139,7 +139,7 @@ Layout layout(const moe_config* c) {
     sz[B_TPREFIX] = kTabs * 4;
     sz[B_QUEUE] = 8 * 4;
     // split-K partials of the router weight gradient (bf16 path only)
-    const int nsplit = c->dtype == MOE_DTYPE_F32 ? 0 : router_dwg_splits(c->T);
+    const int nsplit = c->dtype == MOE_DTYPE_F32 ? 0 : router_dwg_splits(c->T, c->E, c->d);
     sz[B_DWGPART] = nsplit > 1 ? (size_t)nsplit * E * d * 4 : 0;
     // split-K partials of the router logits (bf16 path only)
     const int lsplit = c->dtype == MOE_DTYPE_F32 ? 0 : router_logit_splits(c->T, c->E, c->d);
@@ -466,7 +466,7 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
     TRY(launch_router_bwd(rb, c->dtype, x.s));
     RouterGemmArgs rg = {c->T, c->d, c->E, X, w->Wg, x.buf<void>(B_DL), nullptr,
                          x.buf<float>(B_DXR), g->dWg,
-                         router_dwg_splits(c->T) > 1 ? x.buf<float>(B_DWGPART) : nullptr};
+                         router_dwg_splits(c->T, c->E, c->d) > 1 ? x.buf<float>(B_DWGPART) : nullptr};
     TRY(x.mark(MOE_STAGE_ROUTER_DWG));
     TRY(f32 ? simple_router_dwg(rg, x.s) : mfma_router_dwg(rg, x.s));
     TRY(x.mark(MOE_STAGE_ROUTER_DX));

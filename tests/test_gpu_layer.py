@@ -44,7 +44,7 @@ BF16_CASES = [
        dtype="bf16", expert="swiglu", score="sigmoid"),
     wl("bf16_swiglu_k1", T=257, d=128, E=8, ffn=128, k=1, dtype="bf16", expert="swiglu"),
     wl("bf16_swiglu_tall", T=1500, d=192, E=8, ffn=320, k=4, dtype="bf16", expert="swiglu"),
-    # T >= 4096: the router weight gradient is split over token chunks (2080 + 2020 rows)
+    # the router weight gradient split over 26 token chunks of 160 rows, the last one 100 rows
     wl("bf16_swiglu_router_split", T=4100, d=128, E=8, ffn=128, k=2, dtype="bf16", expert="swiglu"),
 ]
 
