@@ -345,6 +345,7 @@ __device__ __forceinline__ void grouped(int q, int mt, int nt, int& tm, int& tn)
     tm = rem / gsz;
     tn = ng * gn + (rem - tm * gsz);
 }
+
 // Shared memory of one tile: the ring of operand stages, then (gathered k-rows) the ring of
 // their token indices, then (scatter epilogue) the slots of the tile's rows.
 template <int EPI, int TM, int GA>
