@@ -237,8 +237,8 @@ __device__ __forceinline__ void dma_one(const OpPlan& o, int i, uint32_t t, int 
         int kk = k0;
         if (k0 >= o.kswitch) { r = o.r1; kk = k0 - o.kswitch; }
         dma16(r, t + j * 1024, o.vo[i & 1], (uint32_t)(kk + RPL * j) * o.ld_bytes);
-    } else {
-        const int j = wave * DIRECT_IPW + i;
+    } else {                                          // W tile rows
+        const int j = wave * (W / DIRECT_ROWS / 4) + i;
         const int row0 = DIRECT_ROWS * j;
         int rowbase = row0;
         rsrc_t r = o.r0;
@@ -265,7 +265,7 @@ __device__ __forceinline__ nu4r load_one(const OpPlan& o, int i, int k0, int wav
         return __builtin_bit_cast(nu4r, __builtin_amdgcn_raw_buffer_load_b128(
             r, o.vo[i & 1], (uint32_t)(kk + RPL * j) * o.ld_bytes, 0));
     } else {
-        const int j = wave * DIRECT_IPW + i;
+        const int j = wave * (W / DIRECT_ROWS / 4) + i;
         const int row0 = DIRECT_ROWS * j;
         int rowbase = row0;
         rsrc_t r = o.r0;
@@ -368,7 +368,9 @@ struct TileLds {
 // workgroups per CU, 128 accumulators a lane and a 3-stage ring.
 template <int MODE, bool AT, bool BT, int EPI, bool OUT_F32, int TM = 256, int GA = GA_NONE>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int L, bf16* lds) {
-    static_assert(TM == 256 || (TM == 128 && MODE == MODE_KSEG && EPI == EPI_SGD), "128-row tiles: SGD epilogue");
+    static_assert(TM == 256 || (TM == 128 && ((MODE == MODE_KSEG && EPI == EPI_SGD) || MODE == MODE_ROWS)),
+                  "128-row tiles: SGD epilogue or row mode");
+    constexpr int AIPW = TM / DIRECT_ROWS / 4;       // K-contiguous A loads per wave per tile
     static_assert(GA == GA_NONE || (GA == GA_ROWS && MODE == MODE_ROWS && !AT) ||
                   (GA == GA_KA && MODE == MODE_KSEG && AT && TM == 256) ||
                   (GA == GA_KB && MODE == MODE_KSEG && BT), "gathered operand");
@@ -399,10 +401,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int L, bf16* lds)
         const int mt = p.tile_prefix[e + 1] - p.tile_prefix[e];
         int tm;
         grouped(L - p.tile_prefix[e] * NT, mt, NT, tm, n_t);
-        m0 = tm * BM;
+        m0 = tm * TM;
         row_base = p.offsets[e];
         const int seg = p.offsets[e + 1] - p.offsets[e];
-        rows_valid = min(BM, seg - m0);
+        rows_valid = min(TM, seg - m0);
     } else if (MODE == MODE_KSEG) {
         const int MT = (p.M + TM - 1) / TM;
         e = L / (MT * NT);
@@ -441,7 +443,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int L, bf16* lds)
     OpPlan pa, pb;
     // GA_ROWS: lane offset of each of this wave's A loads, the gathered row's start plus the
     // swizzled chunk (OUTB for rows past the tile: they read zeros)
-    uint32_t gvo[GA == GA_ROWS ? DIRECT_IPW : 1];
+    uint32_t gvo[GA == GA_ROWS ? AIPW : 1];
     if (AT) {   // A[k][m]
         if constexpr (GA == GA_KA) {      // k-row p is row rows_tok[p] of the source
             rsrc_t r = make_rsrc(p.A + m0, ((long)p.src_rows * p.lda - m0) * 2);
@@ -456,8 +458,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int L, bf16* lds)
         pa = plan_direct(r, r, (uint32_t)(p.lda * 2), 0);
         const int lr = lane / CHUNKS;
 #pragma unroll
-        for (int i = 0; i < DIRECT_IPW; ++i) {
-            const int row = DIRECT_ROWS * (wave * DIRECT_IPW + i) + lr;
+        for (int i = 0; i < AIPW; ++i) {
+            const int row = DIRECT_ROWS * (wave * AIPW + i) + lr;
             const uint32_t chunk = pa.vo[i & 1] - (uint32_t)lr * pa.ld_bytes;
             gvo[i] = row < rows_valid ? (uint32_t)p.rows_tok[row_base + m0 + row] * pa.ld_bytes + chunk : OUTB;
         }
@@ -502,7 +504,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int L, bf16* lds)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    constexpr int IPW_A = AT ? BK / (512 / TM) / 4 : DIRECT_IPW;
+    constexpr int IPW_A = AT ? BK / (512 / TM) / 4 : AIPW;
     constexpr int IPW_B = BT ? STRIDED_IPW : DIRECT_IPW;
     constexpr int LPW = IPW_A + IPW_B;                 // loads per wave per k-tile
     // each k-step issues PART loads in its MFMA slots; the narrowest wave layout (2 x 2)
@@ -544,7 +546,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int L, bf16* lds)
         const uint32_t st = (uint32_t)(kt % NSt) * (STAGE * 2);
         if (q < IPW_A) {
             if constexpr (GA == GA_ROWS)
-                dma16(pa.r0, lds_base + st + (uint32_t)(wave * DIRECT_IPW + q) * 1024u, gvo[q], (uint32_t)(kt * BK) * 2u);
+                dma16(pa.r0, lds_base + st + (uint32_t)(wave * AIPW + q) * 1024u, gvo[q], (uint32_t)(kt * BK) * 2u);
             else if constexpr (GA == GA_KA) dma_gathered(pa, q, lds_base + st, kt);
             else dma_one<AT, TM>(pa, q, lds_base + st, kt * BK, wave);
         } else {
@@ -1274,7 +1276,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int L, bf16* lds)
         }
     };
 
-    if constexpr (MODE == MODE_ROWS) {
+    if constexpr (MODE == MODE_ROWS && TM == 128) {
+        if (rows_valid <= 64) tile(Layout<2, 2>{});
+        else tile(Layout<2, 4>{});
+    } else if constexpr (MODE == MODE_ROWS) {
         if (rows_valid <= 64) tile(Layout<2, 2>{});
         else if (rows_valid <= 128) tile(Layout<4, 2>{});
         else tile(Layout<4, 4>{});
@@ -1411,47 +1416,77 @@ static hipError_t run(GemmParams p, int grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-static GemmParams base_rows(const ExpertGemmArgs& a) {
+// Row tiles of 256 rows (one workgroup per CU), or of 128 (two per CU, short_rows()).
+//
+// 128-row tiles cost 1.5x the operand loads per flop of 256-row ones, but two workgroups share a
+// CU, so one's prologue and epilogue run under the other's k-loop.  That pays only where a
+// tile's fixed costs weigh most: a short K (at most 1024, 32 k-tiles) over few tiles (at most
+// four rounds of 256-row tiles on the CUs).  Measured (T = 4096, d = 1024, E = 8, ffn = 4096,
+// GELU): up projection 0.133 -> 0.111 ms, down dgrad 0.129 -> 0.104 ms; with K = 2048 or more
+// tiles, or at T = 32768, they were 3-25% slower.  The SwiGLU activation-backward epilogue does
+// not fit the halved register budget, so the rule covers the MLP kinds (bias + ReLU / GELU).
+static bool short_rows(const ExpertGemmArgs& a, int K, int N) {
+    if (a.expert == MOE_EXPERT_SWIGLU || K > 1024) return false;
+    const long tiles = (long)((a.rows + BM - 1) / BM + a.E) * ((N + BN - 1) / BN);
+    return tiles <= 4L * device_cus();
+}
+
+static GemmParams base_rows(const ExpertGemmArgs& a, int tm) {
     GemmParams p = {};
     p.E = a.E;
     p.offsets = a.offsets;
-    p.tile_prefix = a.tile_prefix + 2 * (MOE_MAX_EXPERTS + 1);    // 256-row tiles
-    p.mtiles_ub = (a.rows + BM - 1) / BM + a.E;
+    p.tile_prefix = a.tile_prefix + (tm == 128 ? 1 : 2) * (MOE_MAX_EXPERTS + 1);    // 128- or 256-row tiles
+    p.mtiles_ub = (a.rows + tm - 1) / tm + a.E;
     p.b2_kstart = -1;
     p.ffn = a.ffn;
     p.xcd_group = 4;     // measured: less fabric traffic than 8, steadier clock than 1 or 2
     return p;
 }
 
-hipError_t mfma_up_fwd(const ExpertGemmArgs& a, hipStream_t s) {
+template <int TM>
+static hipError_t up_fwd_tm(const ExpertGemmArgs& a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
-    GemmParams p = base_rows(a);
+    GemmParams p = base_rows(a, TM);
     p.A = (const bf16*)a.Xp; p.lda = a.d;
     p.B = (const bf16*)a.W1; p.ldb = a.d; p.bes = (long)a.ffn * a.d;
     p.K = a.d;
     if (a.expert == MOE_EXPERT_SWIGLU) {
-        p.B2 = (const bf16*)a.W3; p.paired = 1; p.N = 2 * a.ffn;
-        p.C = a.A; p.C2 = a.H;
-        const int NT = (a.ffn + 127) / 128;
-        if (a.token_of) {       // fused dispatch: rows of X through token_of, A gate-scaled
-            p.A = (const bf16*)a.X; p.rows_tok = a.token_of; p.src_rows = a.T; p.row_scale = a.gate_of;
-            return run<MODE_ROWS, false, false, EPI_UP_SWIGLU_G, false, 256, GA_ROWS>(p, p.mtiles_ub * NT, s);
+        if constexpr (TM == 128) {
+            return hipErrorInvalidValue;     // 128-row tiles: MLP kinds only
+        } else {
+            p.B2 = (const bf16*)a.W3; p.paired = 1; p.N = 2 * a.ffn;
+            p.C = a.A; p.C2 = a.H;
+            const int NT = (a.ffn + 127) / 128;
+            if (a.token_of) {   // fused dispatch: rows of X through token_of, A gate-scaled
+                p.A = (const bf16*)a.X; p.rows_tok = a.token_of; p.src_rows = a.T; p.row_scale = a.gate_of;
+                return run<MODE_ROWS, false, false, EPI_UP_SWIGLU_G, false, TM, GA_ROWS>(p, p.mtiles_ub * NT, s);
+            }
+            return run<MODE_ROWS, false, false, EPI_UP_SWIGLU, false, TM>(p, p.mtiles_ub * NT, s);
         }
-        return run<MODE_ROWS, false, false, EPI_UP_SWIGLU, false>(p, p.mtiles_ub * NT, s);
     }
     if (a.token_of) return hipErrorInvalidValue;      // fused dispatch: SwiGLU only
     p.N = a.ffn; p.C = a.A; p.C2 = a.H; p.ldc = a.ffn;
     p.bias = (const bf16*)a.b1; p.bias_es = a.ffn;
     const int NT = (a.ffn + BN - 1) / BN;
     if (a.expert == MOE_EXPERT_RELU)
-        return run<MODE_ROWS, false, false, EPI_UP_RELU, false>(p, p.mtiles_ub * NT, s);
-    return run<MODE_ROWS, false, false, EPI_UP_GELU, false>(p, p.mtiles_ub * NT, s);
+        return run<MODE_ROWS, false, false, EPI_UP_RELU, false, TM>(p, p.mtiles_ub * NT, s);
+    return run<MODE_ROWS, false, false, EPI_UP_GELU, false, TM>(p, p.mtiles_ub * NT, s);
 }
 
+#ifdef MOE_GEMM_KT64
+hipError_t mfma_up_fwd(const ExpertGemmArgs& a, hipStream_t s) { return up_fwd_tm<256>(a, s); }
+#else
+hipError_t mfma_up_fwd(const ExpertGemmArgs& a, hipStream_t s) {
+    return short_rows(a, a.d, a.ffn) ? up_fwd_tm<128>(a, s) : up_fwd_tm<256>(a, s);
+}
+bool mfma_up_fwd_short(const ExpertGemmArgs& a) { return short_rows(a, a.d, a.ffn); }
+#endif
+
 #ifndef MOE_GEMM_KT64     // the second build holds the up projection only
-hipError_t mfma_down_fwd(const ExpertGemmArgs& a, hipStream_t s) {
+template <int TM>
+static hipError_t down_fwd_tm(const ExpertGemmArgs& a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
-    GemmParams p = base_rows(a);
+    GemmParams p = base_rows(a, TM);
     p.A = (const bf16*)a.A; p.lda = a.ffn;
     p.B = (const bf16*)a.W2; p.ldb = a.ffn; p.bes = (long)a.d * a.ffn;
     p.N = a.d; p.K = a.ffn;
@@ -1459,14 +1494,15 @@ hipError_t mfma_down_fwd(const ExpertGemmArgs& a, hipStream_t s) {
     const int NT = (a.d + BN - 1) / BN;
     if (a.b2) {
         p.bias = (const bf16*)a.b2; p.bias_es = a.d;
-        return run<MODE_ROWS, false, false, EPI_STORE_BIAS, false>(p, p.mtiles_ub * NT, s);
+        return run<MODE_ROWS, false, false, EPI_STORE_BIAS, false, TM>(p, p.mtiles_ub * NT, s);
     }
-    return run<MODE_ROWS, false, false, EPI_STORE, false>(p, p.mtiles_ub * NT, s);
+    return run<MODE_ROWS, false, false, EPI_STORE, false, TM>(p, p.mtiles_ub * NT, s);
 }
 
-hipError_t mfma_down_dgrad(const ExpertGemmArgs& a, hipStream_t s) {
+template <int TM>
+static hipError_t down_dgrad_tm(const ExpertGemmArgs& a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
-    GemmParams p = base_rows(a);
+    GemmParams p = base_rows(a, TM);
     const bool glu = a.expert == MOE_EXPERT_SWIGLU;
     const int hcols = glu ? 2 * a.ffn : a.ffn;
     p.A = (const bf16*)a.dEO; p.lda = a.d;
@@ -1475,20 +1511,31 @@ hipError_t mfma_down_dgrad(const ExpertGemmArgs& a, hipStream_t s) {
     p.C = a.dH; p.ldc = hcols;
     p.H = (const bf16*)a.H; p.ldh = hcols;
     const int grid = p.mtiles_ub * ((a.ffn + BN - 1) / BN);
-    if (a.token_of) {           // fused dispatch: rows of dY through token_of, gate applied here
-        if (!glu) return hipErrorInvalidValue;
-        p.A = (const bf16*)a.dY; p.rows_tok = a.token_of; p.src_rows = a.T; p.row_scale = a.gate_of;
-        p.dot_part = a.dgate_part; p.dot_ld = a.rows;
-        return run<MODE_ROWS, false, true, EPI_DN_SWIGLU_G, false, 256, GA_ROWS>(p, grid, s);
+    if constexpr (TM == 128) {  // 128-row tiles: MLP kinds only
+        if (glu || a.token_of) return hipErrorInvalidValue;
+        if (a.expert == MOE_EXPERT_RELU) return run<MODE_ROWS, false, true, EPI_DN_RELU, false, TM>(p, grid, s);
+        return run<MODE_ROWS, false, true, EPI_DN_GELU, false, TM>(p, grid, s);
+    } else {
+        if (a.token_of) {       // fused dispatch: rows of dY through token_of, gate applied here
+            if (!glu) return hipErrorInvalidValue;
+            p.A = (const bf16*)a.dY; p.rows_tok = a.token_of; p.src_rows = a.T; p.row_scale = a.gate_of;
+            p.dot_part = a.dgate_part; p.dot_ld = a.rows;
+            return run<MODE_ROWS, false, true, EPI_DN_SWIGLU_G, false, TM, GA_ROWS>(p, grid, s);
+        }
+        if (glu) return run<MODE_ROWS, false, true, EPI_DN_SWIGLU, false, TM>(p, grid, s);
+        if (a.expert == MOE_EXPERT_RELU) return run<MODE_ROWS, false, true, EPI_DN_RELU, false, TM>(p, grid, s);
+        return run<MODE_ROWS, false, true, EPI_DN_GELU, false, TM>(p, grid, s);
     }
-    if (glu) return run<MODE_ROWS, false, true, EPI_DN_SWIGLU, false>(p, grid, s);
-    if (a.expert == MOE_EXPERT_RELU) return run<MODE_ROWS, false, true, EPI_DN_RELU, false>(p, grid, s);
-    return run<MODE_ROWS, false, true, EPI_DN_GELU, false>(p, grid, s);
+}
+hipError_t mfma_down_fwd(const ExpertGemmArgs& a, hipStream_t s) { return down_fwd_tm<256>(a, s); }
+hipError_t mfma_down_dgrad(const ExpertGemmArgs& a, hipStream_t s) {
+    return short_rows(a, a.d, a.ffn) ? down_dgrad_tm<128>(a, s) : down_dgrad_tm<256>(a, s);
 }
 
-hipError_t mfma_up_dgrad(const ExpertGemmArgs& a, hipStream_t s) {
+template <int TM>
+static hipError_t up_dgrad_tm(const ExpertGemmArgs& a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
-    GemmParams p = base_rows(a);
+    GemmParams p = base_rows(a, TM);
     const bool glu = a.expert == MOE_EXPERT_SWIGLU;
     const int hcols = glu ? 2 * a.ffn : a.ffn;
     p.A = (const bf16*)a.dH; p.lda = hcols;
@@ -1496,8 +1543,9 @@ hipError_t mfma_up_dgrad(const ExpertGemmArgs& a, hipStream_t s) {
     if (glu) { p.B2 = (const bf16*)a.W3; p.b2_kstart = a.ffn; }
     p.N = a.d; p.K = hcols;
     p.C = a.dXp; p.ldc = a.d;
-    return run<MODE_ROWS, false, true, EPI_STORE, false>(p, p.mtiles_ub * ((a.d + BN - 1) / BN), s);
+    return run<MODE_ROWS, false, true, EPI_STORE, false, TM>(p, p.mtiles_ub * ((a.d + BN - 1) / BN), s);
 }
+hipError_t mfma_up_dgrad(const ExpertGemmArgs& a, hipStream_t s) { return up_dgrad_tm<256>(a, s); }
 
 // With the SGD step in the epilogue, the weight gradients run persistent: one workgroup per
 // CU takes its tiles from its XCD group's queue, segments with the most rows first (measured

@@ -185,6 +185,8 @@ hipError_t simple_down_wgrad(const ExpertGemmArgs& a, hipStream_t s);
 hipError_t simple_up_wgrad(const ExpertGemmArgs& a, hipStream_t s);
 // bfloat16 layer (gemm_mfma.hip): grouped MFMA tiles scheduled on the device.
 hipError_t mfma_up_fwd(const ExpertGemmArgs& a, hipStream_t s);
+// whether mfma_up_fwd takes 128-row tiles for this shape (then it runs in this build, not kt64)
+bool mfma_up_fwd_short(const ExpertGemmArgs& a);
 namespace kt64 {
 // the up projection with 64-deep k-tiles and register-staged loads (gemm_mfma_kt64.hip)
 hipError_t mfma_up_fwd(const ExpertGemmArgs& a, hipStream_t s);

@@ -372,7 +372,7 @@ int run_forward(const Ctx& x, const void* X, const moe_weights* w, void* Y, moe_
     ExpertGemmArgs ea = expert_args(x, w, r);
     if (fused(c)) set_fused(x, ea, X, r, nullptr);
     TRY(x.mark(MOE_STAGE_UP_FWD));
-    TRY(f32 ? simple_up_fwd(ea, x.s) : kt64::mfma_up_fwd(ea, x.s));
+    TRY(f32 ? simple_up_fwd(ea, x.s) : (mfma_up_fwd_short(ea) ? mfma_up_fwd(ea, x.s) : kt64::mfma_up_fwd(ea, x.s)));
     TRY(x.mark(MOE_STAGE_DOWN_FWD));
     TRY(f32 ? simple_down_fwd(ea, x.s) : mfma_down_fwd(ea, x.s));
     TRY(x.mark(MOE_STAGE_SHARED_FWD));
