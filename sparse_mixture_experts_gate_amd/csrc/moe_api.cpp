@@ -73,6 +73,10 @@ bool shape_ok(const moe_config* c) {
 }
 
 inline bool fused(const moe_config* c) { return c->fused_dispatch == 1; }
+// bf16 with k = MOE_SCATTER_FUSED_K: the scatter runs in the router dX contraction's epilogue
+inline bool scatter_in_router_dx(const moe_config* c) {
+    return c->dtype != MOE_DTYPE_F32 && c->k == MOE_SCATTER_FUSED_K;
+}
 // tiles of 256 columns of the down-projection dgrad: partial gate gradients per row
 inline int dgate_parts(const moe_config* c) { return (c->ffn + 255) / 256; }
 
@@ -127,10 +131,12 @@ Layout layout(const moe_config* c) {
     sz[B_DH] = rows * hcols(c) * s;
     sz[B_DXP] = rows * d * s;
     sz[B_DY] = T * d * s;
-    sz[B_DXR] = T * d * 4;
+    // the fp32 router part of dX: not stored when the scatter runs in the router dX
+    // contraction's epilogue (bf16, k = MOE_SCATTER_FUSED_K)
+    sz[B_DXR] = scatter_in_router_dx(c) ? 0 : T * d * 4;
     sz[B_DL] = T * E * s;
-    sz[B_DGATE] = T * c->k * 4;
-    sz[B_GATEOF] = rows * 4;
+    sz[B_DGATE] = fused(c) ? 0 : T * c->k * 4;       // fused dispatch: partials in B_DGPART
+    sz[B_GATEOF] = fused(c) ? rows * 4 : 0;          // read only by the fused-dispatch GEMMs
     sz[B_DGPART] = fused(c) ? (size_t)dgate_parts(c) * rows * 4 : 0;
     sz[B_HIST] = E * nc * 4;
     sz[B_CBASE] = E * nc * 4;
@@ -271,7 +277,7 @@ int run_routing(const moe_config* c, hipStream_t s, const RouteScratch& sc, cons
 
 int run_routing(const Ctx& x, const float* logits, const float* e_bias, moe_routing* r) {
     RouteScratch sc = {x.buf<int32_t>(B_HIST), x.buf<int32_t>(B_CBASE), x.buf<float>(B_QPART),
-                       x.buf<int32_t>(B_TPREFIX), x.buf<float>(B_GATEOF)};
+                       x.buf<int32_t>(B_TPREFIX), fused(x.c) ? x.buf<float>(B_GATEOF) : nullptr};
     return run_routing(x.c, x.s, sc, logits, e_bias, r);
 }
 
@@ -464,15 +470,16 @@ int run_backward(const Ctx& x, const void* X, const moe_weights* w, const moe_ro
                         route_scale(c)};
     TRY(x.mark(MOE_STAGE_ROUTER_BWD));
     TRY(launch_router_bwd(rb, c->dtype, x.s));
+    const bool fused_scatter = scatter_in_router_dx(c);
     RouterGemmArgs rg = {c->T, c->d, c->E, X, w->Wg, x.buf<void>(B_DL), nullptr,
-                         x.buf<float>(B_DXR), g->dWg,
+                         fused_scatter ? nullptr : x.buf<float>(B_DXR), g->dWg,
                          router_dwg_splits(c->T, c->E, c->d) > 1 ? x.buf<float>(B_DWGPART) : nullptr};
     TRY(x.mark(MOE_STAGE_ROUTER_DWG));
     TRY(f32 ? simple_router_dwg(rg, x.s) : mfma_router_dwg(rg, x.s));
     TRY(x.mark(MOE_STAGE_ROUTER_DX));
-    ScatterArgs sa = {x.buf<void>(B_DXP), r->slot_of, x.buf<float>(B_DXR), g->dX,
+    ScatterArgs sa = {x.buf<void>(B_DXP), r->slot_of, fused_scatter ? nullptr : x.buf<float>(B_DXR), g->dX,
                       shared ? x.buf<void>(B_DXS) : nullptr, c->T, c->k, vec};
-    if (!f32 && c->k == MOE_SCATTER_FUSED_K) {
+    if (fused_scatter) {
         // the scatter runs in the router dX contraction's epilogue (same sums, same order)
         TRY(mfma_router_dx_scatter(rg, sa, x.s));
         TRY(x.mark(MOE_STAGE_SCATTER));
